@@ -1,0 +1,170 @@
+/*
+ * ds_sample.h -- C ABI of the MI355X (gfx950) per-position full-vocabulary sampler.
+ *
+ * The library reduces packed logits [rows, positions, vocab] to one
+ * (token, logprob) pair per position, and reduces plain logit rows to the greedy
+ * draft triple (token, log-sum-exp, logprob).  Every step runs in HIP kernels on
+ * the caller's stream; the host side only validates arguments and launches.
+ *
+ * Sources, cited by page title and section:
+ *   [ISSUE] mstar issue "Sampler support for discrete diffusion" -- opening
+ *           request and the comment on the API shape.
+ *   [PR]    mstar PR "Add a sampler resource for discrete diffusion" -- section
+ *           "What does this PR do?" (the sample(request_ids, c_logits, u_logits,
+ *           seq_lens, iterations) contract).
+ *   [DRAFT] LightLLM PR "perf: avoid full-vocab all-gather for draft greedy
+ *           sampling" -- section "Design and invariants".
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named "device" are HIP device pointers (for example a torch
+ *     tensor's data_ptr()); pointers named "host" are ordinary host memory.
+ *   - The caller owns every buffer it passes.  Outputs are written, never
+ *     allocated.  Inputs must stay alive and unchanged until the stream reaches
+ *     the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *     Calls are asynchronous; results are valid once the stream has reached them.
+ *   - Calls return a status code (DS_OK on success).  Arguments are validated
+ *     before anything is enqueued, so a rejected call touches no output.  The
+ *     text of the last failure on the calling thread is ds_last_error().
+ *   - A sampler handle is not thread-safe and owns device scratch memory: calls
+ *     on one handle must be ordered (same stream, or externally synchronised).
+ */
+#ifndef DS_SAMPLE_H
+#define DS_SAMPLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ds_sampler ds_sampler;
+
+/* Element type of the logit tensors. */
+enum { DS_DTYPE_F32 = 0, DS_DTYPE_BF16 = 1 };
+
+/* Status codes. */
+enum {
+    DS_OK = 0,
+    DS_ERR_INVALID_ARG = 1, /* a pointer, size or value is outside its contract  */
+    DS_ERR_UNSUPPORTED = 2, /* valid request the library does not implement      */
+    DS_ERR_CAPACITY = 3,    /* sizes exceed what the handle was created for      */
+    DS_ERR_NO_MEMORY = 4,   /* device or host allocation failed at create time   */
+    DS_ERR_HIP = 5          /* a HIP runtime call failed; see ds_last_error()    */
+};
+
+/* Creation flags. */
+enum {
+    DS_FLAG_NONE = 0,
+    /* Route every cell through the plain multi-pass kernels (exact threshold by
+     * radix select over re-reads, Gumbel over every kept id) instead of the
+     * single-pass fast paths.  Results are identical; this exists so tests can
+     * compare the two paths. */
+    DS_FLAG_FORCE_FALLBACK = 1
+};
+
+/*
+ * ds_sample_create -- allocate a sampler for one vocabulary size and dtype.
+ *
+ *   out           host; receives the handle.
+ *   device        HIP device ordinal the handle's scratch lives on; every later
+ *                 call must pass pointers and a stream of that device.
+ *   vocab         V >= 1 (ids 0 .. V-1).
+ *   dtype         DS_DTYPE_F32 or DS_DTYPE_BF16.
+ *   max_rows      largest `num_rows` (C) a ds_sample call may pass (>= 1).
+ *   max_positions largest total positions P = sum(seq_lens) (>= 1); also bounds
+ *                 ds_greedy_lse's n_rows by max_rows * max_positions.
+ *   max_requests  largest `num_requests` (>= 1).
+ *   top_k         ids kept by the top-ratio filter; 0 selects ceil(V / 10) =
+ *                 (V + 9) / 10 ([ISSUE], comment on the API shape).  1 .. V.
+ *   vocab_chunks  contiguous vocabulary chunks of ceil(V / vocab_chunks) ids each
+ *                 reduced to a (max, lse, argmax) triple and merged ([DRAFT]);
+ *                 1 .. min(V, 1024).  Results do not depend on it.
+ *   flags         DS_FLAG_*.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_NO_MEMORY or DS_ERR_HIP.
+ */
+int ds_sample_create(ds_sampler **out, int device, int32_t vocab, int32_t dtype,
+                     int32_t max_rows, int64_t max_positions, int32_t max_requests,
+                     int32_t top_k, int32_t vocab_chunks, uint32_t flags);
+
+/*
+ * ds_sample -- one diffusion sampling step over every position handed in
+ * ([PR] "What does this PR do?", [ISSUE] comment on the API shape).
+ *
+ * Logits are packed as [C, P, V] row-major (vocab fastest), requests
+ * concatenated along positions in argument order: request r owns positions
+ * [off_r, off_r + seq_lens[r]) with off_r = seq_lens[0] + ... + seq_lens[r-1].
+ * For cell (row, p) of request r at offset t = p - off_r:
+ *   h[v]     = c[v] when guidance_scale[r] == 0 (u is not read), otherwise
+ *              fmaf(s, c[v] - u[v], c[v]) in fp32; a c of -inf stays -inf.
+ *   logprob  = log-probability, over the full vocabulary, before temperature and
+ *              filtering, of the guided distribution lc + s*(lc - lu) on
+ *              log-softmaxed c and u, renormalised; equal to h[token] - LSE(h).
+ *   temperature[r] == 0: token = smallest id with the largest h.
+ *   temperature[r]  > 0: keep the ids whose h is >= the top_k-th largest h (ties
+ *              kept); token = argmax over kept ids of h/tau + G, smallest id on
+ *              exact ties, with Gumbel noise G = -log(-log U) from Philox4x32-10:
+ *              key (seed low, seed high), counter (v >> 2, t,
+ *              (row & 0xFFFF) | (iterations[r] << 16), (uint32)request_ids[r]),
+ *              word v & 3, U = ((word >> 9) * 2 + 1) * 2^-24.
+ *
+ *   request_ids    host [R]; the low 32 bits key the noise.
+ *   c_logits       device [C, P, V] of the handle's dtype; 4-byte aligned (f32)
+ *                  or 2-byte aligned (bf16).  Values finite or -inf.
+ *   u_logits       device, same layout; may be NULL iff every guidance scale is
+ *                  0.  Rows of requests with guidance 0 are never read (they may
+ *                  hold anything).  Elsewhere finite, or -inf where c is -inf.
+ *   seq_lens       host [R], each >= 0; P = sum <= max_positions.
+ *   iterations     host [R]; diffusion step index, keys the noise (16 bits used).
+ *   guidance_scale host [R]; finite.
+ *   temperature    host [R]; >= 0 and finite; 0 means greedy.
+ *   num_requests   R, 1 .. max_requests.
+ *   num_rows       C, 1 .. max_rows.
+ *   seed           64-bit noise key.
+ *   tokens_out     device int32 [C, P].
+ *   logprobs_out   device float [C, P].
+ *   threshold_out  device float [C, P] or NULL; the top_k-th largest h of each
+ *                  sampled cell, NaN for greedy cells.
+ *   stream         hipStream_t.
+ */
+int ds_sample(ds_sampler *s, const int64_t *request_ids, const void *c_logits,
+              const void *u_logits, const int32_t *seq_lens, const int32_t *iterations,
+              const float *guidance_scale, const float *temperature, int32_t num_requests,
+              int32_t num_rows, uint64_t seed, int32_t *tokens_out, float *logprobs_out,
+              float *threshold_out, void *stream);
+
+/*
+ * ds_greedy_lse -- draft greedy reduction of plain logit rows ([DRAFT]).
+ *
+ *   logits       device [n_rows, V] of the handle's dtype (alignment as above),
+ *                values finite or -inf, no row entirely -inf.
+ *   n_rows       0 .. max_rows * max_positions (0 is a no-op).
+ *   token_out    device int32 [n_rows]: smallest id attaining the row maximum.
+ *   lse_out      device float [n_rows]: log-sum-exp over the full row.
+ *   logprob_out  device float [n_rows]: logits[token] - lse, the log of the
+ *                exact selected-token probability.
+ *   triples_out  device float [vocab_chunks][n_rows][3] or NULL: per chunk
+ *                (max, lse, id) with the int32 id stored bit-for-bit in the third
+ *                float word (reinterpret, never convert); an empty chunk is
+ *                (-inf, -inf, INT32_MAX).
+ *   stream       hipStream_t.
+ */
+int ds_greedy_lse(ds_sampler *s, const void *logits, int64_t n_rows, int32_t *token_out,
+                  float *lse_out, float *logprob_out, float *triples_out, void *stream);
+
+/* Release a handle and its device scratch.  NULL is a no-op.  The caller must
+ * make sure no call on the handle is still pending on a stream. */
+void ds_sample_destroy(ds_sampler *s);
+
+/* Text of the last failure on the calling thread ("" if none).  The pointer
+ * stays valid until the next call on the same thread. */
+const char *ds_last_error(void);
+
+/* Library version, as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int ds_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_SAMPLE_H */

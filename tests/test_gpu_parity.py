@@ -1,0 +1,238 @@
+"""GPU parity: the HIP sampler (through the C ABI) against the CPU oracle.
+
+Every case prints what it runs before launching, so a failure names its case.
+Bars are stated in tests/gpu_helpers.py.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import (check_greedy, check_sample, log, run_greedy, run_sample, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    torch.cuda.init()
+
+
+# ------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("tau", [0.0, 0.9])
+def test_tiny_step_all_cells(tau):
+    w = synth.tiny(tau)
+    got = run_sample(w)
+    check_sample(w, got, oracle.sample_workload(w))
+
+
+def test_omnivoice_step_all_cells():
+    w = synth.omnivoice()
+    ref = oracle.sample_workload(w)
+    got = run_sample(w)
+    check_sample(w, got, ref)
+    # asking for the threshold does not change the draw
+    got2 = run_sample(w, threshold=False)
+    assert np.array_equal(got[0], got2[0]) and np.array_equal(got[1], got2[1])
+
+
+def test_mixed_guidance_batch_all_cells():
+    w = synth.mixed()
+    assert np.any(w.guidance == 0) and w.u is not None
+    ref = oracle.sample_workload(w)
+    rep = check_sample(w, run_sample(w), ref)
+    assert rep.greedy > 0 and rep.sampled > 0
+
+
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_draft_greedy_full_size(chunks):
+    x = synth.draft().logits
+    ref = oracle.greedy_lse(x, vocab_chunks=chunks)
+    got = run_greedy(x, chunks)
+    check_greedy(x, got, ref, f"draft chunks={chunks}")
+    w = synth.draft()
+    # planted ties resolve to the smallest id
+    for r in w.tie_rows:
+        row = oracle.bf16_to_f32(x[r])
+        assert got[0][r] == int(np.flatnonzero(row == row.max())[0])
+
+
+def test_stress_small_positions_dense_chunked_and_fallback():
+    w = synth.stress(positions=24)
+    ref = oracle.sample_workload(w)
+    got4 = run_sample(w)
+    check_sample(w, got4, ref)
+    got1 = run_sample(w, vocab_chunks=1)
+    check_sample(w, got1, ref)
+    gotf = run_sample(w, force_fallback=True)
+    check_sample(w, gotf, ref)
+    assert np.array_equal(got1[0], got4[0]) and np.array_equal(gotf[0], got4[0])
+
+
+def test_stress_full_size_sampled_cells_and_chunk_equality():
+    import torch
+
+    w = synth.stress()
+    c = to_dev(w.c)
+    u = to_dev(w.u)
+    got4 = run_sample(w, c_dev=c, u_dev=u, threshold=False)
+    got1 = run_sample(w, c_dev=c, u_dev=u, threshold=False, vocab_chunks=1)
+    del c, u
+    torch.cuda.empty_cache()
+    # the four-chunk result equals the dense single-pass result in every cell
+    assert np.array_equal(got4[0], got1[0])
+    assert np.max(np.abs(got4[1] - got1[1])) <= 1e-5
+    cells = np.linspace(0, w.cells - 1, 40).astype(np.int64)
+    ref = oracle.sample_workload(w, cells=cells)
+    check_sample(w, got4, ref, check_threshold=False)
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 2, 3, 63, 64, 65, 127, 129, 1000, 2046])
+def test_small_vocab_sizes(V, dtype):
+    seq = [3, 0, 5, 2]
+    for k in sorted({1, max(1, V // 3), V}):
+        w = synth.diffusion(f"V{V}_k{k}", seed=V + k, vocab=V, rows=3, seq_lens=seq, dtype=dtype,
+                            sigma=2.0, guidance=[2.0, 1.0, 0.0, -0.5],
+                            temperature=[0.9, 0.3, 1.5, 0.0], top_k=k)
+        check_sample(w, run_sample(w), oracle.sample_workload(w))
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 3000), ("bf16", 4096 + 7), ("f32", 5000)])
+def test_row_kernel_mid_vocab(dtype, V):
+    w = synth.diffusion(f"row_{dtype}_{V}", seed=V, vocab=V, rows=2, seq_lens=[5, 4], dtype=dtype,
+                        sigma=3.0, guidance=[2.0, 0.0], temperature=[1.0, 0.0])
+    ref = oracle.sample_workload(w)
+    for chunks in (1, 3, 8):
+        check_sample(w, run_sample(w, vocab_chunks=chunks), ref)
+    check_sample(w, run_sample(w, force_fallback=True), ref)
+
+
+def test_masked_ids_stay_masked():
+    V = 1025
+    w = synth.diffusion("masked", seed=5, vocab=V, rows=4, seq_lens=[30, 20], sigma=3.0,
+                        guidance=[2.0, 0.0], temperature=[0.9, 1.2], masked_ids=[0, 17, 1024])
+    ref = oracle.sample_workload(w)
+    got = run_sample(w)
+    check_sample(w, got, ref)
+    assert not np.isin(got[0], [0, 17, 1024]).any()
+    gotf = run_sample(w, force_fallback=True)
+    check_sample(w, gotf, ref)
+
+
+def test_heavy_ties_and_extreme_top_k():
+    V = 1025
+    for k, tau in ((1, 1.0), (103, 0.9), (1025, 2.0), (500, 50.0), (103, 1e-3)):
+        w = synth.diffusion(f"ties_k{k}", seed=k, vocab=V, rows=2, seq_lens=[40], sigma=2.0,
+                            guidance=0.0, temperature=tau, top_k=k)
+        # snap logits to a coarse grid so thresholds and maxima tie
+        f = oracle.bf16_to_f32(w.c)
+        w.c = synth.bf16_from_f32(np.round(f * 2) / 2)
+        ref = oracle.sample_workload(w)
+        check_sample(w, run_sample(w), ref)
+        check_sample(w, run_sample(w, force_fallback=True), ref)
+
+
+def test_many_requests_span_several_launches():
+    rng = np.random.default_rng(3)
+    R = 150
+    seq = rng.integers(0, 6, R)
+    w = synth.diffusion("many", seed=9, vocab=1025, rows=2, seq_lens=seq, sigma=3.0,
+                        guidance=rng.choice([0.0, 2.0], R), temperature=rng.choice([0.0, 0.9], R),
+                        iterations=rng.integers(0, 1000, R))
+    check_sample(w, run_sample(w), oracle.sample_workload(w))
+
+
+def test_guidance_zero_everywhere_needs_no_u():
+    w = synth.diffusion("no_u", seed=4, vocab=1025, rows=2, seq_lens=[10, 7], guidance=0.0,
+                        temperature=[0.9, 0.0])
+    assert w.u is None
+    check_sample(w, run_sample(w), oracle.sample_workload(w))
+
+
+def test_unaligned_views_and_side_stream():
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    w = synth.diffusion("unaligned", seed=12, vocab=1025, rows=2, seq_lens=[9, 6], sigma=3.0,
+                        guidance=2.0, temperature=0.9)
+    n = w.c.size
+    cbuf = torch.zeros(n + 1, dtype=torch.int16, device="cuda")
+    ubuf = torch.zeros(n + 1, dtype=torch.int16, device="cuda")
+    cbuf[1:] = torch.from_numpy(w.c.reshape(-1).view(np.int16)).cuda()
+    ubuf[1:] = torch.from_numpy(w.u.reshape(-1).view(np.int16)).cuda()
+    c = cbuf[1:].view(torch.bfloat16).view(w.c.shape)
+    u = ubuf[1:].view(torch.bfloat16).view(w.u.shape)
+    ref = oracle.sample_workload(w)
+    check_sample(w, run_sample(w, c_dev=c, u_dev=u), ref)
+    check_sample(w, run_sample(w, c_dev=c, u_dev=u, force_fallback=True), ref)
+    side = torch.cuda.Stream()
+    with ds.Sampler(w.vocab, "bf16", max_rows=2, max_positions=w.positions) as smp:
+        with torch.cuda.stream(side):
+            tok, lp = smp.sample(w.request_ids, c, u, w.seq_lens, w.iterations, w.guidance,
+                                 w.temperature, seed=w.seed)
+        side.synchronize()
+    assert np.array_equal(tok.reshape(-1).cpu().numpy(), ref.tokens)
+
+
+def test_repeat_calls_are_bitwise_identical():
+    w = synth.omnivoice(n_requests=3)
+    a = run_sample(w)
+    b = run_sample(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("V,chunks", [(1, 1), (9, 4), (1025, 7), (1025, 1024), (5000, 3)])
+def test_greedy_lse_shapes_and_chunks(V, chunks):
+    rng = np.random.default_rng(V)
+    for dtype in ("bf16", "f32"):
+        x = (rng.integers(-8, 9, (37, V)) * 0.5).astype(np.float32)  # many ties
+        if dtype == "bf16":
+            x = synth.bf16_from_f32(x)
+        ref = oracle.greedy_lse(x, vocab_chunks=chunks)
+        check_greedy(x, run_greedy(x, chunks), ref, f"V={V} chunks={chunks} {dtype}")
+
+
+def test_invalid_calls_are_rejected_before_launch():
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    w = synth.tiny(0.9)
+    c = to_dev(w.c)
+    u = to_dev(w.u)
+    with ds.Sampler(w.vocab, "f32", max_rows=2, max_positions=16, max_requests=1) as smp:
+        tok = torch.full((2, 16), -7, dtype=torch.int32, device="cuda")
+        lp = torch.zeros((2, 16), dtype=torch.float32, device="cuda")
+        cases = [
+            dict(u_logits=None),
+            dict(temperature=[-1.0]),
+            dict(temperature=[float("nan")]),
+            dict(guidance_scale=[float("inf")]),
+            dict(seq_lens=[17]),
+            dict(seq_lens=[-1]),
+            dict(num_rows=3),
+        ]
+        for bad in cases:
+            args = dict(request_ids=w.request_ids, c_logits=c, u_logits=u, seq_lens=w.seq_lens,
+                        iterations=w.iterations, guidance_scale=w.guidance,
+                        temperature=w.temperature, num_rows=2, seed=1, tokens_out=tok,
+                        logprobs_out=lp)
+            args.update(bad)
+            log(f"[gpu] invalid call {bad}")
+            with pytest.raises(ds.DSError):
+                ds.ds_sample(smp._h, **args)
+        torch.cuda.synchronize()
+        assert int((tok == -7).sum()) == tok.numel()  # nothing was written

@@ -1,0 +1,108 @@
+"""MI355X-native per-position full-vocabulary sampler.
+
+The compute lives in ``libdssample.so`` (hand-written HIP for gfx950, C ABI in
+``include/ds_sample.h``).  This package is a thin binding: the ``ds_*`` functions
+mirror the C entry points one to one, and ``Sampler`` wraps a handle and allocates
+output tensors with torch.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+from ._binding import (  # noqa: F401
+    DS_DTYPE_BF16,
+    DS_DTYPE_F32,
+    DS_ERR_CAPACITY,
+    DS_ERR_HIP,
+    DS_ERR_INVALID_ARG,
+    DS_ERR_NO_MEMORY,
+    DS_ERR_UNSUPPORTED,
+    DS_FLAG_FORCE_FALLBACK,
+    DS_FLAG_NONE,
+    DS_OK,
+    DSError,
+    EXPORTED,
+    LIB_PATH,
+    ds_greedy_lse,
+    ds_last_error,
+    ds_sample,
+    ds_sample_create,
+    ds_sample_destroy,
+    ds_version,
+    lib,
+)
+
+
+class Sampler:
+    """A sampler handle for one vocabulary size and logit dtype.
+
+    ``sample`` follows the diffusion sampler contract
+    ``sample(request_ids, c_logits, u_logits, seq_lens, iterations) -> (tokens,
+    logprobs)`` with per-request guidance scale and temperature;
+    ``greedy_lse`` is the draft path's (token, lse, logprob) reduction.
+    """
+
+    def __init__(self, vocab: int, dtype: str = "bf16", *, max_rows: int = 8,
+                 max_positions: int = 4096, max_requests: int = 64, top_k: int = 0,
+                 vocab_chunks: int = 1, device: int = 0, force_fallback: bool = False):
+        if dtype not in ("bf16", "f32"):
+            raise ValueError("dtype must be 'bf16' or 'f32'")
+        self.vocab = vocab
+        self.dtype = dtype
+        self.device = device
+        self.vocab_chunks = vocab_chunks
+        flags = DS_FLAG_FORCE_FALLBACK if force_fallback else DS_FLAG_NONE
+        self._h = ds_sample_create(device, vocab, DS_DTYPE_BF16 if dtype == "bf16" else DS_DTYPE_F32,
+                                   max_rows, max_positions, max_requests, top_k, vocab_chunks, flags)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            ds_sample_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def sample(self, request_ids: Sequence[int], c_logits, u_logits, seq_lens: Sequence[int],
+               iterations: Sequence[int], guidance_scale: Sequence[float],
+               temperature: Sequence[float], seed: int = 0, threshold: bool = False,
+               out=None, stream=None):
+        """Returns (tokens int32 [C, P], logprobs float32 [C, P]) and, with
+        threshold=True, the per-cell top-ratio threshold as a third tensor."""
+        import torch
+
+        C_, P = int(c_logits.shape[0]), int(c_logits.shape[1])
+        dev = c_logits.device
+        if out is None:
+            tokens = torch.empty((C_, P), dtype=torch.int32, device=dev)
+            logprobs = torch.empty((C_, P), dtype=torch.float32, device=dev)
+            thr = torch.empty((C_, P), dtype=torch.float32, device=dev) if threshold else None
+        else:
+            tokens, logprobs, thr = out
+        ds_sample(self._h, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
+                  temperature, C_, seed, tokens, logprobs, thr, stream)
+        return (tokens, logprobs, thr) if threshold else (tokens, logprobs)
+
+    def greedy_lse(self, logits, triples: bool = False, out=None, stream=None):
+        """logits [n_rows, V] -> (token int32, lse float32, logprob float32)
+        [, triples float32 [vocab_chunks, n_rows, 3] with the id bit-cast]."""
+        import torch
+
+        n = int(logits.shape[0])
+        dev = logits.device
+        if out is None:
+            tok = torch.empty(n, dtype=torch.int32, device=dev)
+            lse = torch.empty(n, dtype=torch.float32, device=dev)
+            lp = torch.empty(n, dtype=torch.float32, device=dev)
+            tri = torch.empty((self.vocab_chunks, n, 3), dtype=torch.float32, device=dev) if triples else None
+        else:
+            tok, lse, lp, tri = out
+        ds_greedy_lse(self._h, logits, n, tok, lse, lp, tri, stream)
+        return (tok, lse, lp, tri) if triples else (tok, lse, lp)

@@ -1,0 +1,148 @@
+"""ctypes binding of libdssample.so: argument marshalling only.
+
+Functions carry the C entry points' names (ds_sample_create, ds_sample,
+ds_greedy_lse, ds_sample_destroy, ds_last_error, ds_version).  Device buffers are
+torch tensors on a HIP device (torch supplies memory and streams); per-request
+arrays are host sequences.  Every computation happens in the HIP library; when the
+library is missing the calls raise instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdssample.so")
+
+DS_DTYPE_F32, DS_DTYPE_BF16 = 0, 1
+DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY, DS_ERR_HIP = range(6)
+DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK = 0, 1
+
+EXPORTED = ("ds_sample_create", "ds_sample", "ds_greedy_lse", "ds_sample_destroy", "ds_last_error",
+            "ds_version")
+
+_lib = None
+
+
+class DSError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m vocab_wise_logit_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, I64, U32, U64 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_uint64
+        L.ds_sample_create.restype = C.c_int
+        L.ds_sample_create.argtypes = [C.POINTER(P), C.c_int, I32, I32, I32, I64, I32, I32, I32, U32]
+        L.ds_sample.restype = C.c_int
+        L.ds_sample.argtypes = [P, P, P, P, P, P, P, P, I32, I32, U64, P, P, P, P]
+        L.ds_greedy_lse.restype = C.c_int
+        L.ds_greedy_lse.argtypes = [P, P, I64, P, P, P, P, P]
+        L.ds_sample_destroy.restype = None
+        L.ds_sample_destroy.argtypes = [P]
+        L.ds_last_error.restype = C.c_char_p
+        L.ds_last_error.argtypes = []
+        L.ds_version.restype = C.c_int
+        L.ds_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != DS_OK:
+        raise DSError(rc, lib().ds_last_error().decode())
+
+
+def _dev_ptr(t, what: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor on a HIP device")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must live on a HIP device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must have dtype {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _host(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def ds_version() -> int:
+    return lib().ds_version()
+
+
+def ds_last_error() -> str:
+    return lib().ds_last_error().decode()
+
+
+def ds_sample_create(device: int, vocab: int, dtype: int, max_rows: int, max_positions: int,
+                     max_requests: int, top_k: int = 0, vocab_chunks: int = 1, flags: int = 0) -> int:
+    h = C.c_void_p()
+    _check(lib().ds_sample_create(C.byref(h), device, vocab, dtype, max_rows, max_positions,
+                                  max_requests, top_k, vocab_chunks, flags))
+    return h.value
+
+
+def ds_sample_destroy(handle: int) -> None:
+    lib().ds_sample_destroy(handle)
+
+
+def ds_sample(handle: int, request_ids: Sequence[int], c_logits, u_logits, seq_lens: Sequence[int],
+              iterations: Sequence[int], guidance_scale: Sequence[float],
+              temperature: Sequence[float], num_rows: int, seed: int, tokens_out, logprobs_out,
+              threshold_out=None, stream=None) -> None:
+    import torch
+
+    rid = _host(request_ids, np.int64)
+    sl = _host(seq_lens, np.int32)
+    it = _host(iterations, np.int32)
+    gs = _host(guidance_scale, np.float32)
+    tp = _host(temperature, np.float32)
+    n = rid.size
+    if not (sl.size == it.size == gs.size == tp.size == n):
+        raise ValueError("per-request arrays must all have num_requests entries")
+    cp = _dev_ptr(c_logits, "c_logits")
+    up = _dev_ptr(u_logits, "u_logits")
+    _check(lib().ds_sample(handle, rid.ctypes.data, cp, up, sl.ctypes.data, it.ctypes.data,
+                           gs.ctypes.data, tp.ctypes.data, n, num_rows, seed & (2**64 - 1),
+                           _dev_ptr(tokens_out, "tokens_out", torch.int32),
+                           _dev_ptr(logprobs_out, "logprobs_out", torch.float32),
+                           _dev_ptr(threshold_out, "threshold_out", torch.float32),
+                           _stream_ptr(stream)))
+
+
+def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_out,
+                  triples_out=None, stream=None) -> None:
+    import torch
+
+    _check(lib().ds_greedy_lse(handle, _dev_ptr(logits, "logits"), n_rows,
+                               _dev_ptr(token_out, "token_out", torch.int32),
+                               _dev_ptr(lse_out, "lse_out", torch.float32),
+                               _dev_ptr(logprob_out, "logprob_out", torch.float32),
+                               _dev_ptr(triples_out, "triples_out", torch.float32),
+                               _stream_ptr(stream)))

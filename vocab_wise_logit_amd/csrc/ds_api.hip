@@ -1,0 +1,271 @@
+// ds_api.hip -- host side of the C ABI declared in include/ds_sample.h.
+//
+// Validates every argument before anything is enqueued, splits a call into
+// launches of at most 64 requests (their per-request parameters travel by value in
+// the kernel argument segment, so no host-to-device copy precedes a launch), and
+// picks the kernel: one wavefront per cell when the row fits in registers, one
+// workgroup per cell otherwise.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "ds_kernels.h"
+#include "ds_sample.h"
+
+struct ds_sampler {
+    int device;
+    int32_t vocab;
+    int32_t dtype;
+    int32_t max_rows;
+    int64_t max_positions;
+    int32_t max_requests;
+    int32_t top_k;
+    int32_t vocab_chunks;
+    uint32_t flags;
+    float z0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Standard normal quantile by bisection on erfc (host, once per handle).
+double normal_quantile(double p) {
+    double lo = -10.0, hi = 10.0;
+    for (int i = 0; i < 200; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        const double cdf = 0.5 * std::erfc(-mid / std::sqrt(2.0));
+        if (cdf < p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool use_small_kernel(const ds_sampler* s) {
+    if (s->flags & DS_FLAG_FORCE_FALLBACK) return false;
+    const bool bf16 = s->dtype == DS_DTYPE_BF16;
+    const int ns = ds::small_slots_needed(bf16, s->vocab);
+    return ns <= (bf16 ? ds::kSmallMaxSlotsBf16 : ds::kSmallMaxSlotsF32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ds_last_error(void) { return g_err.c_str(); }
+
+int ds_version(void) { return 100; }
+
+int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype, int32_t max_rows,
+                     int64_t max_positions, int32_t max_requests, int32_t top_k,
+                     int32_t vocab_chunks, uint32_t flags) {
+    g_err.clear();
+    if (!out) return fail(DS_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (vocab < 1) return fail(DS_ERR_INVALID_ARG, "vocab must be >= 1 (got %d)", vocab);
+    if (dtype != DS_DTYPE_F32 && dtype != DS_DTYPE_BF16)
+        return fail(DS_ERR_INVALID_ARG, "dtype must be DS_DTYPE_F32 or DS_DTYPE_BF16 (got %d)", dtype);
+    if (max_rows < 1) return fail(DS_ERR_INVALID_ARG, "max_rows must be >= 1");
+    if (max_positions < 1) return fail(DS_ERR_INVALID_ARG, "max_positions must be >= 1");
+    if (max_requests < 1) return fail(DS_ERR_INVALID_ARG, "max_requests must be >= 1");
+    if ((int64_t)max_rows * max_positions > (int64_t)INT32_MAX)
+        return fail(DS_ERR_INVALID_ARG, "max_rows * max_positions exceeds 2^31 - 1 cells");
+    if (top_k < 0 || top_k > vocab) return fail(DS_ERR_INVALID_ARG, "top_k must be in [0, vocab]");
+    const int32_t max_chunks = vocab < 1024 ? vocab : 1024;
+    if (vocab_chunks < 1 || vocab_chunks > max_chunks)
+        return fail(DS_ERR_INVALID_ARG, "vocab_chunks must be in [1, %d]", max_chunks);
+    if (flags & ~(uint32_t)DS_FLAG_FORCE_FALLBACK) return fail(DS_ERR_INVALID_ARG, "unknown flags");
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= ndev) return fail(DS_ERR_INVALID_ARG, "device %d out of range", device);
+
+    ds_sampler* s = new (std::nothrow) ds_sampler();
+    if (!s) return fail(DS_ERR_NO_MEMORY, "host allocation failed");
+    s->device = device;
+    s->vocab = vocab;
+    s->dtype = dtype;
+    s->max_rows = max_rows;
+    s->max_positions = max_positions;
+    s->max_requests = max_requests;
+    s->top_k = top_k ? top_k : (vocab + 9) / 10;
+    s->vocab_chunks = vocab_chunks;
+    s->flags = flags;
+    // first pivot of the threshold search aims at a count a little above top_k
+    double q0 = 1.25 * (double)s->top_k / vocab + 2.0 / std::sqrt((double)vocab);
+    if (q0 > 0.5) q0 = 0.5;
+    s->z0 = (float)normal_quantile(1.0 - q0);
+    *out = s;
+    return DS_OK;
+}
+
+void ds_sample_destroy(ds_sampler* s) { delete s; }
+
+int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
+              const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
+              const float* temperature, int32_t num_requests, int32_t num_rows, uint64_t seed,
+              int32_t* tokens_out, float* logprobs_out, float* threshold_out, void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    if (!request_ids || !seq_lens || !iterations || !guidance_scale || !temperature)
+        return fail(DS_ERR_INVALID_ARG, "a per-request host array is NULL");
+    if (!c_logits || !tokens_out || !logprobs_out)
+        return fail(DS_ERR_INVALID_ARG, "c_logits, tokens_out and logprobs_out must be non-NULL");
+    if (num_requests < 1 || num_requests > s->max_requests)
+        return fail(DS_ERR_CAPACITY, "num_requests %d outside [1, %d]", num_requests, s->max_requests);
+    if (num_rows < 1 || num_rows > s->max_rows)
+        return fail(DS_ERR_CAPACITY, "num_rows %d outside [1, %d]", num_rows, s->max_rows);
+    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(c_logits, es)) return fail(DS_ERR_INVALID_ARG, "c_logits is not %d-byte aligned", (int)es);
+    if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4) || (threshold_out && !aligned(threshold_out, 4)))
+        return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+    int64_t P = 0;
+    bool need_u = false;
+    for (int32_t r = 0; r < num_requests; ++r) {
+        if (seq_lens[r] < 0) return fail(DS_ERR_INVALID_ARG, "seq_lens[%d] = %d < 0", r, seq_lens[r]);
+        if (!std::isfinite(guidance_scale[r]))
+            return fail(DS_ERR_INVALID_ARG, "guidance_scale[%d] is not finite", r);
+        if (!(temperature[r] >= 0.0f) || !std::isfinite(temperature[r]))
+            return fail(DS_ERR_INVALID_ARG, "temperature[%d] must be finite and >= 0", r);
+        need_u |= guidance_scale[r] != 0.0f;
+        P += seq_lens[r];
+    }
+    if (P > s->max_positions)
+        return fail(DS_ERR_CAPACITY, "sum(seq_lens) = %lld exceeds max_positions %lld", (long long)P,
+                    (long long)s->max_positions);
+    if (need_u && !u_logits)
+        return fail(DS_ERR_INVALID_ARG, "u_logits is NULL but a request has guidance_scale != 0");
+    if (need_u) {
+        if (!aligned(u_logits, es)) return fail(DS_ERR_INVALID_ARG, "u_logits is not %d-byte aligned", (int)es);
+        if ((((uintptr_t)u_logits - (uintptr_t)c_logits) & 15u) != 0)
+            return fail(DS_ERR_UNSUPPORTED, "u_logits and c_logits must have the same address modulo 16 bytes");
+    }
+    if (P == 0) return DS_OK;
+
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf16 = s->dtype == DS_DTYPE_BF16;
+    const bool small = use_small_kernel(s);
+
+    ds::SampleArgs a;
+    a.c = c_logits;
+    a.u = need_u ? u_logits : nullptr;
+    a.V = s->vocab;
+    a.rows = num_rows;
+    a.top_k = s->top_k;
+    a.vocab_chunks = s->vocab_chunks;
+    a.k0 = (uint32_t)seed;
+    a.k1 = (uint32_t)(seed >> 32);
+    a.z0 = s->z0;
+    a.force_fallback = (s->flags & DS_FLAG_FORCE_FALLBACK) ? 1 : 0;
+    a.tokens = tokens_out;
+    a.logprobs = logprobs_out;
+    a.thresholds = threshold_out;
+    a.work = nullptr;
+
+    // one launch per group of up to 64 non-empty requests (contiguous positions)
+    int32_t r = 0;
+    int64_t pos = 0;
+    while (r < num_requests) {
+        ds::ReqTable rq;
+        std::memset(&rq, 0, sizeof rq);
+        rq.P = (int32_t)P;
+        while (r < num_requests && seq_lens[r] == 0) ++r;
+        if (r >= num_requests) break;
+        rq.pos0 = (int32_t)pos;
+        int32_t n = 0, rel = 0;
+        while (r < num_requests && n < ds::kMaxReqPerLaunch) {
+            if (seq_lens[r] > 0) {
+                rq.offs[n] = rel;
+                rq.scale[n] = guidance_scale[r];
+                rq.tau[n] = temperature[r];
+                rq.inv_tau[n] = temperature[r] > 0.0f ? 1.0f / temperature[r] : 0.0f;
+                rq.row_iter_hi[n] = (uint32_t)iterations[r] << 16;
+                rq.rid[n] = (uint32_t)request_ids[r];
+                rel += seq_lens[r];
+                ++n;
+            }
+            ++r;
+        }
+        rq.n = n;
+        rq.offs[n] = rel;
+        rq.npos = rel;
+        const hipError_t e = small ? ds::launch_sample_small(bf16, a, rq, st)
+                                   : ds::launch_sample_row(bf16, a, rq, st);
+        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+        pos += rel;
+    }
+    return DS_OK;
+}
+
+int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* token_out, float* lse_out,
+                  float* logprob_out, float* triples_out, void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    if (n_rows < 0) return fail(DS_ERR_INVALID_ARG, "n_rows must be >= 0");
+    if (n_rows > (int64_t)s->max_rows * s->max_positions)
+        return fail(DS_ERR_CAPACITY, "n_rows %lld exceeds max_rows * max_positions", (long long)n_rows);
+    if (n_rows == 0) return DS_OK;
+    if (!logits || !token_out || !lse_out || !logprob_out)
+        return fail(DS_ERR_INVALID_ARG, "logits, token_out, lse_out and logprob_out must be non-NULL");
+    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(logits, es)) return fail(DS_ERR_INVALID_ARG, "logits is not %d-byte aligned", (int)es);
+    if (!aligned(token_out, 4) || !aligned(lse_out, 4) || !aligned(logprob_out, 4) ||
+        (triples_out && !aligned(triples_out, 4)))
+        return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    ds::GreedyArgs a;
+    a.x = logits;
+    a.n_rows = n_rows;
+    a.V = s->vocab;
+    a.vocab_chunks = s->vocab_chunks;
+    a.token = token_out;
+    a.lse = lse_out;
+    a.logprob = logprob_out;
+    a.triples = triples_out;
+    const hipError_t e = ds::launch_greedy_lse(s->dtype == DS_DTYPE_BF16, a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "greedy kernel launch");
+    return DS_OK;
+}
+
+}  // extern "C"

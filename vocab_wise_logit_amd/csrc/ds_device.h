@@ -1,0 +1,191 @@
+// ds_device.h -- device building blocks shared by the sampler kernels (gfx950).
+//
+// Sources, by page title and section:
+//   [ISSUE] mstar issue "Sampler support for discrete diffusion", comment on the API
+//           shape: CFG combine, top-ratio filter to ceil(0.1 V) ids, Gumbel noise.
+//   [DRAFT] LightLLM PR "perf: avoid full-vocab all-gather for draft greedy
+//           sampling", "Design and invariants": max / log-sum-exp / argmax triples,
+//           smallest id on ties.
+//   [PHILOX] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+//           1, 2, 3", SC'11: Philox4x32 round function and Weyl key schedule.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Largest Gumbel value the noise map can produce is -log(-log(1 - 2^-24)) =
+// 16.6355...; the bound used to prune ids that cannot win adds a margin for the
+// fp32 rounding of G and of h / tau.
+constexpr float kGumbelBound = 16.75f;
+// Smallest value, -log(-log(2^-24)) = -2.8116..., with margin.
+constexpr float kGumbelFloor = -2.82f;
+
+// ------------------------------------------------------------ element decode
+
+// bf16 is the upper half of a binary32, so widening is a shift (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// [ISSUE] CFG combine in fp32 with one rounding of s*(c-u)+c.  The max with -inf
+// maps the NaN of (-inf) - (-inf) at masked ids back to -inf (IEEE maxNum returns
+// the non-NaN operand); every other input passes through unchanged.
+__device__ __forceinline__ float guided(float c, float u, float s) {
+    float h = __builtin_fmaf(s, c - u, c);
+    return __builtin_fmaxf(h, kNegInf);
+}
+
+// Order-preserving map binary32 -> uint32 (negative values: all bits flipped,
+// others: sign bit set).  Callers never feed -0 where it could differ from +0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t b = __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// ------------------------------------------------------------------- noise
+
+// [PHILOX] Philox4x32 with ten rounds.  Each round multiplies words 0 and 2 by
+// the two Philox constants, swaps the halves and xors in the round key; the key
+// advances by the Weyl increments.  The key words are wave-uniform, so the
+// schedule runs on the scalar unit.
+struct Words4 {
+    uint32_t w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                                uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t pa = (uint64_t)0xD2511F53u * x0;
+        const uint64_t pb = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t y0 = (uint32_t)(pb >> 32) ^ x1 ^ k0;
+        const uint32_t y2 = (uint32_t)(pa >> 32) ^ x3 ^ k1;
+        x1 = (uint32_t)pb;
+        x3 = (uint32_t)pa;
+        x0 = y0;
+        x2 = y2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return Words4{x0, x1, x2, x3};
+}
+
+// Per-cell noise stream: the counter words that do not depend on the id.
+struct NoiseKey {
+    uint32_t k0, k1;    // seed halves
+    uint32_t t;         // position inside the request
+    uint32_t row_iter;  // (row & 0xFFFF) | (iteration << 16)
+    uint32_t rid;       // low 32 bits of the request id
+};
+
+__device__ __forceinline__ uint32_t noise_word(const NoiseKey& nk, uint32_t v) {
+    const Words4 w = philox4x32_10(v >> 2, nk.t, nk.row_iter, nk.rid, nk.k0, nk.k1);
+    const uint32_t sel = v & 3u;
+    uint32_t x = w.w0;
+    x = sel == 1u ? w.w1 : x;
+    x = sel == 2u ? w.w2 : x;
+    x = sel == 3u ? w.w3 : x;
+    return x;
+}
+
+// G = -log(-log U), U = ((x >> 9) * 2 + 1) * 2^-24 (exact in fp32).  -log U is
+// taken as -log1p(U - 1), U - 1 = -(1 - U) being exact, so that U near 1 keeps
+// full relative accuracy.
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+    const float U = (float)((x >> 9) * 2u + 1u) * 0x1p-24f;
+    const float w = -log1pf(U - 1.0f);
+    return -logf(w);
+}
+
+// ---------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = __builtin_fminf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Wave argmax of (z, id): larger z wins, equal z keeps the smaller id.
+__device__ __forceinline__ void wave_argmax(float& z, int& id) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float oz = __shfl_xor(z, o);
+        const int oi = __shfl_xor(id, o);
+        const bool take = (oz > z) || (oz == z && oi < id);
+        z = take ? oz : z;
+        id = take ? oi : id;
+    }
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+// Number of set bits of m in lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// ------------------------------------------------------ per-launch requests
+
+// Per-request parameters of the requests covered by one launch, passed by value
+// in the kernel argument segment ([PR]: per-request guidance and temperature,
+// broadcast to every position of the request).
+constexpr int kMaxReqPerLaunch = 64;
+
+struct ReqTable {
+    int32_t n;        // requests in this launch
+    int32_t pos0;     // first packed position covered
+    int32_t npos;     // positions covered
+    int32_t P;        // total packed positions of the call
+    int32_t offs[kMaxReqPerLaunch + 1];  // request starts, relative to pos0
+    float scale[kMaxReqPerLaunch];
+    float tau[kMaxReqPerLaunch];
+    float inv_tau[kMaxReqPerLaunch];
+    uint32_t row_iter_hi[kMaxReqPerLaunch];  // iteration << 16
+    uint32_t rid[kMaxReqPerLaunch];
+};
+
+// The request owning launch-relative position pl: the last r with offs[r] <= pl.
+__device__ __forceinline__ int find_request(const ReqTable& rq, int pl) {
+    int lo = 0, hi = rq.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rq.offs[mid] <= pl)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace ds

@@ -1,0 +1,51 @@
+// ds_kernels.h -- launch interface between the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ds_device.h"
+
+namespace ds {
+
+// Arguments common to one sampler launch (one group of <= 64 requests).
+struct SampleArgs {
+    const void* c;          // [C, P, V] logits (f32 or bf16)
+    const void* u;          // same layout, or nullptr when no request in the call reads it
+    int32_t V;
+    int32_t rows;           // C
+    int32_t top_k;
+    int32_t vocab_chunks;   // row kernel only
+    uint32_t k0, k1;        // seed halves
+    float z0;               // normal quantile used for the first threshold pivot
+    int32_t force_fallback; // row kernel: skip the single-pass paths
+    int32_t* tokens;        // [C, P]
+    float* logprobs;        // [C, P]
+    float* thresholds;      // [C, P] or nullptr
+    float* work;            // row kernel scratch (unused by the small kernel)
+};
+
+// Largest row the wave-per-cell kernel keeps in registers, in dwords per lane.
+constexpr int kSmallMaxSlotsBf16 = 16;  // V <= 2046
+constexpr int kSmallMaxSlotsF32 = 32;   // V <= 2048
+int small_slots_needed(bool bf16, int V);
+
+hipError_t launch_sample_small(bool bf16, const SampleArgs& a, const ReqTable& rq,
+                               hipStream_t st);
+hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq,
+                             hipStream_t st);
+
+struct GreedyArgs {
+    const void* x;      // [n_rows, V]
+    int64_t n_rows;
+    int32_t V;
+    int32_t vocab_chunks;
+    int32_t* token;
+    float* lse;
+    float* logprob;
+    float* triples;     // [chunks][n_rows][3] or nullptr
+};
+
+hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st);
+
+}  // namespace ds
