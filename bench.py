@@ -1,0 +1,280 @@
+"""Benchmark of the per-position full-vocabulary sampler on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload omnivoice] [--no-suite]
+
+One step is one ``ds_sample`` call over one synthetic batch already resident in
+HBM: CFG combine, temperature, exact top-ratio threshold, Gumbel-max and the
+full-vocabulary logprob for every (row, position) cell.  The headline workload is
+the OmniVoice-shaped masked-diffusion step (8 requests x 8 codebook rows, ragged
+lengths 80-120, V=1025 bf16).  Input buffers rotate through copies totalling at
+least 1 GiB so that neither the L2 nor the 256 MB Infinity Cache serves a repeat.
+
+Prints ONE JSON line: positions/s for the headline step, the roofline of its
+kernel (algorithmic bytes over the kernel's average duration, timed live with HIP
+events on the launch stream), the CPU oracle timed on a bounded sample, and the
+same figures for the other workloads under "per_config".
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sampled positions/sec + achieved HBM GB/s (% of MI355X peak) per config"
+ROTATE_BYTES = 1 << 30
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "vocab_wise_logit_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by a copy-kernel calibration), if they were taken on the
+    current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def to_dev(arr: np.ndarray):
+    """Copy a numpy array (float32, or bf16 bit patterns as uint16) to the GPU."""
+    import torch
+
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def kernel_name(w, kind: str) -> str:
+    if kind == "draft":
+        return "k_greedy_lse"
+    slots = ((w.vocab + 2) // 2 if w.dtype == "bf16" else w.vocab + 63) // 64
+    small = slots <= (16 if w.dtype == "bf16" else 32)
+    return "k_sample_small" if small else "k_sample_row"
+
+
+def make_workload(name: str):
+    import synth
+
+    if name == "tiny":
+        return synth.tiny(0.9)
+    return synth.WORKLOADS[name]()
+
+
+class Runner:
+    """Device copies of one workload and a sampler handle; `step(i)` issues one
+    call on rotating buffers."""
+
+    def __init__(self, w, kind: str):
+        import torch
+
+        import vocab_wise_logit_amd as ds
+
+        self.w, self.kind = w, kind
+        if kind == "draft":
+            x = to_dev(w.logits)
+            per_set = x.numel() * x.element_size()
+            self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
+            self.x = [x] + [x.clone() for _ in range(self.n_sets - 1)]
+            n = w.n_rows
+            self.smp = ds.Sampler(w.vocab, w.dtype, max_rows=1, max_positions=n,
+                                  vocab_chunks=w.vocab_chunks)
+            self.out = (torch.empty(n, dtype=torch.int32, device="cuda"),
+                        torch.empty(n, dtype=torch.float32, device="cuda"),
+                        torch.empty(n, dtype=torch.float32, device="cuda"), None)
+            self.cells = n
+        else:
+            c = to_dev(w.c)
+            u = to_dev(w.u) if w.u is not None else None
+            per_set = c.numel() * c.element_size() * (2 if u is not None else 1)
+            self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
+            self.c = [c] + [c.clone() for _ in range(self.n_sets - 1)]
+            self.u = [u] + [u.clone() for _ in range(self.n_sets - 1)] if u is not None else None
+            self.smp = ds.Sampler(w.vocab, w.dtype, max_rows=w.rows, max_positions=w.positions,
+                                  max_requests=len(w.seq_lens), top_k=w.top_k,
+                                  vocab_chunks=w.vocab_chunks)
+            shape = (w.rows, w.positions)
+            self.out = (torch.empty(shape, dtype=torch.int32, device="cuda"),
+                        torch.empty(shape, dtype=torch.float32, device="cuda"), None)
+            self.cells = w.cells
+
+    def step(self, i: int) -> None:
+        s = i % self.n_sets
+        w = self.w
+        if self.kind == "draft":
+            self.smp.greedy_lse(self.x[s], out=self.out)
+        else:
+            self.smp.sample(w.request_ids, self.c[s], self.u[s] if self.u else None, w.seq_lens,
+                            w.iterations, w.guidance, w.temperature, seed=w.seed, out=self.out)
+
+    def close(self):
+        self.smp.close()
+
+
+def time_runner(r: Runner, steps: int, warmup: int):
+    """(ms per step over the whole timed region, mean per-launch ms from events
+    recorded around every launch on the same stream)."""
+    import torch
+
+    for i in range(warmup):
+        r.step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        r.step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # per-launch durations (same stream), second pass over the same buffers
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        r.step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    return ms_step, float(np.mean(per)), float(np.median(per)), float(np.percentile(per, 10)), float(
+        np.percentile(per, 90))
+
+
+def describe(w, kind: str) -> dict:
+    if kind == "draft":
+        return {"workload": "draft_greedy", "rows": w.n_rows, "vocab": w.vocab,
+                "input_dtype": w.dtype, "vocab_chunks": w.vocab_chunks}
+    return {"workload": {"omnivoice": "omnivoice_step", "mixed": "mixed_guidance_batch",
+                         "stress": "large_vocab_chunked", "tiny": "tiny_step"}.get(w.name, w.name),
+            "requests": int(len(w.seq_lens)), "rows": w.rows, "positions": w.positions,
+            "cells": w.cells, "vocab": w.vocab, "input_dtype": w.dtype, "top_k": w.top_k,
+            "vocab_chunks": w.vocab_chunks}
+
+
+def bench_one(name: str, steps: int, warmup: int) -> dict:
+    import torch
+
+    kind = "draft" if name == "draft" else "sample"
+    w = make_workload(name)
+    r = Runner(w, kind)
+    ms_step, ms_kernel, med, p10, p90 = time_runner(r, steps, warmup)
+    r.close()
+    del r
+    torch.cuda.empty_cache()
+    alg = w.algorithmic_bytes()
+    cells = w.n_rows if kind == "draft" else w.cells
+    achieved = alg / (ms_kernel * 1e-3) / 1e9
+    return {"config": describe(w, kind), "kernel": kernel_name(w, kind), "positions_per_s": cells / (ms_step * 1e-3),
+            "ms_per_step": ms_step, "kernel_ms_mean": ms_kernel, "kernel_ms_median": med,
+            "kernel_ms_p10": p10, "kernel_ms_p90": p90, "algorithmic_bytes": alg,
+            "achieved_GBs": achieved, "frac_of_peak": achieved / HBM_PEAK_GBS, "workload_obj": w}
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands (single-threaded C) on a bounded sample of cells."""
+    import oracle
+
+    cells_all = np.arange(w.cells, dtype=np.int64)
+    # estimate cost on a small slice, then size the sample to the time budget
+    probe = cells_all[: min(256, w.cells)]
+    t = time.perf_counter()
+    oracle.sample_workload(w, cells=probe)
+    per_cell = (time.perf_counter() - t) / probe.size
+    n = int(max(probe.size, min(w.cells, budget_s / max(per_cell, 1e-9))))
+    sample = cells_all[:n]
+    t = time.perf_counter()
+    oracle.sample_workload(w, cells=sample)
+    dt = time.perf_counter() - t
+    return {"value": n / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {w.cells} cells of the same workload "
+                      f"({'whole batch' if n == w.cells else 'bounded'}), {dt:.2f} s, "
+                      f"single-threaded C oracle"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="omnivoice")
+    ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this sampler has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 2
+
+    head = bench_one(args.workload, args.steps, args.warmup)
+    w = head.pop("workload_obj")
+    traffic = stored_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(head["achieved_GBs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(head["frac_of_peak"], 4),
+                "traffic": traffic,
+                "kernel": head["kernel"],
+                "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
+                "kernel_ms_mean": head["kernel_ms_mean"], "kernel_ms_median": head["kernel_ms_median"]}
+    per_config = {}
+    if not args.no_suite:
+        for name in ("tiny", "omnivoice", "mixed", "draft", "stress"):
+            if name == args.workload:
+                res = head
+            else:
+                res = bench_one(name, max(10, args.steps // 2), max(3, args.warmup // 2))
+                res.pop("workload_obj", None)
+            per_config[res["config"]["workload"]] = {
+                k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    line = {
+        "metric": METRIC,
+        "value": head["positions_per_s"],
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
