@@ -26,6 +26,21 @@ constexpr float kGumbelBound = 16.75f;
 // Smallest value, -log(-log(2^-24)) = -2.8116..., with margin.
 constexpr float kGumbelFloor = -2.82f;
 
+// ------------------------------------------------------ global-memory views
+
+// Kernel arguments arrive as generic pointers; casting them to the global
+// address space lets the compiler emit global_load instead of flat_load.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+
+// 16-byte load unit of the streaming kernels.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ gptr<T> as_global(const void* p) {
+    return (gptr<T>)p;
+}
+
 // ------------------------------------------------------------ element decode
 
 // bf16 is the upper half of a binary32, so widening is a shift (exact).
@@ -106,45 +121,71 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
 }
 
 // ---------------------------------------------------------- wave reductions
+//
+// All-lane reductions use DPP inside each row of 16 lanes (xor 1, xor 2, half
+// mirror, mirror) and then combine the four row results read into scalar
+// registers, so the result is wave-uniform and no LDS round trip is involved.
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o));
-    return x;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = __builtin_fminf(x, __shfl_xor(x, o));
-    return x;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
-__device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Wave argmax of (z, id): larger z wins, equal z keeps the smaller id.
-__device__ __forceinline__ void wave_argmax(float& z, int& id) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float oz = __shfl_xor(z, o);
-        const int oi = __shfl_xor(id, o);
-        const bool take = (oz > z) || (oz == z && oi < id);
-        z = take ? oz : z;
-        id = take ? oi : id;
-    }
+__device__ __forceinline__ float wave_max(float x) {
+    x = __builtin_fmaxf(x, dpp_f<kDppXor1>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppXor2>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppMirror>(x));
+    return __builtin_fmaxf(__builtin_fmaxf(readlane_f(x, 0), readlane_f(x, 16)),
+                           __builtin_fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+}
+__device__ __forceinline__ float wave_min(float x) {
+    x = __builtin_fminf(x, dpp_f<kDppXor1>(x));
+    x = __builtin_fminf(x, dpp_f<kDppXor2>(x));
+    x = __builtin_fminf(x, dpp_f<kDppHalfMirror>(x));
+    x = __builtin_fminf(x, dpp_f<kDppMirror>(x));
+    return __builtin_fminf(__builtin_fminf(readlane_f(x, 0), readlane_f(x, 16)),
+                           __builtin_fminf(readlane_f(x, 32), readlane_f(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    x += dpp_f<kDppMirror>(x);
+    return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+    x = min(x, dpp_i<kDppXor1>(x));
+    x = min(x, dpp_i<kDppXor2>(x));
+    x = min(x, dpp_i<kDppHalfMirror>(x));
+    x = min(x, dpp_i<kDppMirror>(x));
+    return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Wave argmax of (z, id): larger z wins, equal z keeps the smaller id.  Returns
+// the winning lane's (z, id) in every lane, and the winning lane index.
+__device__ __forceinline__ int wave_argmax(float& z, int& id) {
+    const float zm = wave_max(z);
+    const int im = wave_min_i(z == zm ? id : 0x7FFFFFFF);
+    const uint64_t m = __ballot(z == zm && id == im);
+    z = zm;
+    id = im;
+    return (int)__builtin_ctzll(m);
 }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }

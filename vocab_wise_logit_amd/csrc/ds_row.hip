@@ -92,16 +92,8 @@ __device__ __forceinline__ int block_min_i(int x, Shared& sh) {
 
 // Block argmax of (z, id, h): larger z, then smaller id.
 __device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Shared& sh) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float oz = __shfl_xor(z, o);
-        const int oi = __shfl_xor(id, o);
-        const float oh = __shfl_xor(hv, o);
-        const bool take = (oz > z) || (oz == z && oi < id);
-        z = take ? oz : z;
-        id = take ? oi : id;
-        hv = take ? oh : hv;
-    }
+    const int wl = wave_argmax(z, id);
+    hv = readlane_f(hv, wl);
     const int w = threadIdx.x >> 6;
     __syncthreads();
     if (lane_id() == 0) {
@@ -130,13 +122,11 @@ struct Piece {
 };
 
 template <bool BF16>
-__device__ __forceinline__ void load_piece(const uint4* c16, const uint4* u16, int64_t q, float s,
-                                           bool use_u, Piece<BF16>& P) {
-    const uint4 cw = c16[q];
+__device__ __forceinline__ void decode_piece(const u32x4 cw, const u32x4 uw, float s, bool use_u,
+                                             Piece<BF16>& P) {
     if (BF16) {
         const uint32_t cc[4] = {cw.x, cw.y, cw.z, cw.w};
         if (use_u) {
-            const uint4 uw = u16[q];
             const uint32_t uu[4] = {uw.x, uw.y, uw.z, uw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -154,7 +144,6 @@ __device__ __forceinline__ void load_piece(const uint4* c16, const uint4* u16, i
         const float cf[4] = {__uint_as_float(cw.x), __uint_as_float(cw.y), __uint_as_float(cw.z),
                              __uint_as_float(cw.w)};
         if (use_u) {
-            const uint4 uw = u16[q];
             const float uf[4] = {__uint_as_float(uw.x), __uint_as_float(uw.y), __uint_as_float(uw.z),
                                  __uint_as_float(uw.w)};
 #pragma unroll
@@ -166,10 +155,18 @@ __device__ __forceinline__ void load_piece(const uint4* c16, const uint4* u16, i
     }
 }
 
+template <bool BF16>
+__device__ __forceinline__ void load_piece(gptr<u32x4> c16, gptr<u32x4> u16, int64_t q, float s,
+                                           bool use_u, Piece<BF16>& P) {
+    const u32x4 cw = c16[q];
+    const u32x4 uw = use_u ? u16[q] : cw;
+    decode_piece<BF16>(cw, uw, s, use_u, P);
+}
+
 // Geometry of one row inside the 16-byte-aligned view of the tensors.
 struct RowGeom {
-    const uint4* c16;
-    const uint4* u16;
+    gptr<u32x4> c16;
+    gptr<u32x4> u16;
     int64_t gbase;  // element index of id 0 in the aligned view
     int V;
     int L;          // chunk length ceil(V / nch)
@@ -301,7 +298,7 @@ __device__ __forceinline__ int wave_append(bool pred, int* counter) {
     int base = 0;
     const int leader = (int)__builtin_ctzll(m);
     if (lane_id() == leader) base = atomicAdd(counter, popc(m));
-    base = __shfl(base, leader);
+    base = __builtin_amdgcn_readlane(base, leader);
     return pred ? base + lanes_below(m) : -1;
 }
 
@@ -325,19 +322,33 @@ __device__ RowResult stream_row(const RowGeom& G, float s, bool use_u, bool keep
         int bg = -1;  // group (within chunk) holding this thread's max
         const int64_t nq = cr.q1 - cr.q0 + 1;
         const int its = (int)((nq + (int64_t)NT * U - 1) / ((int64_t)NT * U));
-        for (int it = 0; it < its; ++it) {
+        // one group: U raw 16-byte pieces of c (and u); two groups are in flight
+        // at a time (ping-pong) so the loads of the next group overlap the math
+        // on the current one
+        struct Raw {
+            u32x4 c[U], u[U];
+        };
+        auto load = [&](Raw& R, int it) {
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                const int64_t q = cr.q0 + (int64_t)it * NT * U + (int64_t)uu * NT + threadIdx.x;
+                const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
+                R.c[uu] = u32x4{ninf, ninf, ninf, ninf};
+                R.u[uu] = R.c[uu];
+                if (q <= cr.q1) {
+                    R.c[uu] = G.c16[q];
+                    if (use_u) R.u[uu] = G.u16[q];
+                }
+            }
+        };
+        auto process = [&](const Raw& R, int it) {
             Piece<BF16> P[U];
             float gm = kNegInf;
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const int64_t q = cr.q0 + (int64_t)it * NT * U + (int64_t)uu * NT + threadIdx.x;
-                if (q <= cr.q1) {
-                    load_piece<BF16>(G.c16, G.u16, q, s, use_u, P[uu]);
-                    mask_piece<BF16>(P[uu], q, G, cr.lo, cr.hi);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < EPP; ++i) P[uu].h[i] = kNegInf;
-                }
+                decode_piece<BF16>(R.c[uu], R.u[uu], s, use_u, P[uu]);
+                mask_piece<BF16>(P[uu], q, G, cr.lo, cr.hi);
 #pragma unroll
                 for (int i = 0; i < EPP; ++i) gm = __builtin_fmaxf(gm, P[uu].h[i]);
             }
@@ -354,6 +365,16 @@ __device__ RowResult stream_row(const RowGeom& G, float s, bool use_u, bool keep
 #pragma unroll
                 for (int i = 0; i < EPP; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(P[uu].h[i], kLog2e, -mL));
             if (keep_groups) sh.gmax[j * G.gpc + gid] = gm;
+        };
+        Raw A, B;
+        if (its > 0) load(A, 0);
+        for (int it = 0; it < its; it += 2) {
+            if (it + 1 < its) load(B, it + 1);
+            process(A, it);
+            if (it + 1 < its) {
+                if (it + 2 < its) load(A, it + 2);
+                process(B, it + 1);
+            }
         }
         // undo the rounding of m * log2(e) for this thread's partial sum
         if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(NT) void k_greedy_lse(GreedyArgs a) {
     constexpr int ES = BF16 ? 2 : 4;
     const uintptr_t xb = (uintptr_t)a.x;
     RowGeom G;
-    G.c16 = (const uint4*)(xb & ~(uintptr_t)15);
+    G.c16 = as_global<u32x4>((const char*)a.x - (xb & 15));
     G.u16 = G.c16;
     G.gbase = (int64_t)((xb & 15) / ES) + row * a.V;
     G.V = a.V;
@@ -441,8 +462,8 @@ __global__ __launch_bounds__(NT) void k_sample_row(SampleArgs a, ReqTable rq) {
 
     const uintptr_t cb = (uintptr_t)a.c;
     RowGeom G;
-    G.c16 = (const uint4*)(cb & ~(uintptr_t)15);
-    G.u16 = use_u ? (const uint4*)((uintptr_t)a.u & ~(uintptr_t)15) : G.c16;
+    G.c16 = as_global<u32x4>((const char*)a.c - (cb & 15));
+    G.u16 = use_u ? as_global<u32x4>((const char*)a.u - (cb & 15)) : G.c16;
     G.gbase = (int64_t)((cb & 15) / ES) + cell * a.V;
     G.V = a.V;
     G.nch = a.vocab_chunks;

@@ -27,72 +27,58 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kListCap = 512;
 constexpr int kListRegs = kListCap / kWave;
 
-// Wave argmax of (z, id) that also carries the winner's h.
-__device__ __forceinline__ void wave_argmax3(float& z, int& id, float& hv) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float oz = __shfl_xor(z, o);
-        const int oi = __shfl_xor(id, o);
-        const float oh = __shfl_xor(hv, o);
-        const bool take = (oz > z) || (oz == z && oi < id);
-        z = take ? oz : z;
-        id = take ? oi : id;
-        hv = take ? oh : hv;
-    }
-}
+struct Entry {
+    float h;
+    int e;
+};
 
 template <bool BF16, int NS>
 struct Row {
     static constexpr int NE = BF16 ? 2 * NS : NS;
     float h[NE];
-    int par;  // bf16: 1 if the row starts in the high half of a dword
+    int ebase;  // id of register element 0 in this lane (bf16: 2 * lane - parity)
 
     // Row-relative id of register element i of this lane.
-    __device__ __forceinline__ int id_of(int i, int lane) const {
-        if (BF16) return 2 * ((i >> 1) * kWave + lane) + (i & 1) - par;
-        return i * kWave + lane;
+    __device__ __forceinline__ int id_of(int i) const {
+        if (BF16) return ebase + 2 * kWave * (i >> 1) + (i & 1);
+        return ebase + kWave * i;
     }
 
-    // Number of ids in h that are >= x (x > -inf), counted with ballots.
+    // Number of ids whose h is >= x (x > -inf), counted with ballots.
     __device__ __forceinline__ int count_ge(float x) const {
         int n = 0;
 #pragma unroll
         for (int i = 0; i < NE; ++i) n += popc(ballot(h[i] >= x));
         return n;
     }
-};
 
-// Count ids >= x and write every such (h, id) to the wave's LDS list (entries
-// beyond the capacity are dropped; the caller checks the returned count).
-template <bool BF16, int NS>
-__device__ __forceinline__ int count_and_compact(const Row<BF16, NS>& R, float x, int lane,
-                                                 float* lh, int* le) {
-    int base = 0;
+    // Count the ids whose h is >= x and write them, as (h, id) in register-slot
+    // order, to `list`; entries past kListCap are dropped (the caller checks the
+    // returned count before using the list).
+    __device__ __forceinline__ int count_compact(float x, Entry* list) const {
+        int base = 0;
 #pragma unroll
-    for (int i = 0; i < Row<BF16, NS>::NE; ++i) {
-        const bool pred = R.h[i] >= x;
-        const uint64_t m = ballot(pred);
-        if (m) {
-            const int o = base + lanes_below(m);
-            if (pred && o < kListCap) {
-                lh[o] = R.h[i];
-                le[o] = R.id_of(i, lane);
+        for (int i = 0; i < NE; ++i) {
+            const bool pred = h[i] >= x;
+            const uint64_t m = ballot(pred);
+            if (m) {
+                const int o = base + lanes_below(m);
+                if (pred && o < kListCap) list[o] = Entry{h[i], id_of(i)};
+                base += popc(m);
             }
-            base += popc(m);
         }
+        __builtin_amdgcn_wave_barrier();
+        return base;
     }
-    __builtin_amdgcn_wave_barrier();
-    return base;
-}
+};
 
 // Exact k-th largest over all valid ids, by key-space bisection on the full
 // registers (bounded by 32 rounds).  Used only when the pivot search fails.
 template <bool BF16, int NS>
 __device__ float kth_by_bisection(const Row<BF16, NS>& R, int k, int V, float M) {
-    uint32_t lo = order_key(kNegInf);  // count(lo) = V >= k
-    uint32_t hi = order_key(M) + 1u;   // count = 0 < k
     if (R.count_ge(M) >= k) return M;
-    hi = order_key(M);
+    uint32_t lo = order_key(kNegInf);  // count(lo) = V >= k
+    uint32_t hi = order_key(M);        // count(hi) < k
     while (hi - lo > 1u) {
         const uint32_t mid = lo + ((hi - lo) >> 1);
         const int c = (mid == order_key(kNegInf)) ? V : R.count_ge(key_value(mid));
@@ -104,14 +90,128 @@ __device__ float kth_by_bisection(const Row<BF16, NS>& R, int k, int V, float M)
     return key_value(lo);
 }
 
+// Smallest finite h of the row (rare path).  The empty volatile asm pins the
+// computation inside the branch that needs it; otherwise the compiler hoists this
+// loop-invariant reduction into the common path.
 template <bool BF16, int NS>
-__global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleArgs a, ReqTable rq) {
+__device__ __forceinline__ float min_finite(const Row<BF16, NS>& R) {
+    float mn = __builtin_huge_valf();
+    asm volatile("" : "+v"(mn));
+#pragma unroll
+    for (int i = 0; i < Row<BF16, NS>::NE; ++i) mn = R.h[i] > kNegInf ? __builtin_fminf(mn, R.h[i]) : mn;
+    return wave_min(mn);
+}
+
+// Exact k-th largest of a wave's LDS list, given that the list holds every id
+// whose h is >= lo and n >= k of them (lo < M).  Interpolation on the count
+// narrows [lo, hi); distinct values are then taken from the top until the count
+// reaches k.
+__device__ __forceinline__ float list_kth(const Entry* list, int n, int k, float lo, float M,
+                                                    int lane) {
+    float xl[kListRegs];
+    const int nl = (n + kWave - 1) / kWave;
+#pragma unroll
+    for (int i = 0; i < kListRegs; ++i) {
+        const int o = i * kWave + lane;
+        xl[i] = kNegInf;
+        if (i < nl && o < n) xl[i] = list[o].h;
+    }
+    auto cnt = [&](float x) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kListRegs; ++i)
+            if (i < nl) c += popc(ballot(xl[i] >= x));
+        return c;
+    };
+    float hi = M;
+    int c_hi = cnt(M);
+    if (c_hi >= k) return M;
+    int clo = n;
+    for (int it = 0; it < 48; ++it) {
+        const int nw = clo - c_hi;
+        if (nw <= 4 || k - c_hi <= 1) break;
+        float p = lo + (hi - lo) * ((float)(clo - k) + 0.5f) * __builtin_amdgcn_rcpf((float)nw);
+        if (!(p > lo && p < hi)) p = 0.5f * lo + 0.5f * hi;
+        if (!(p > lo && p < hi)) break;
+        const int c = cnt(p);
+        if (c >= k) {
+            lo = p;
+            clo = c;
+        } else {
+            hi = p;
+            c_hi = c;
+        }
+    }
+    for (int it = 0; it <= kListCap; ++it) {
+        float m2 = kNegInf;
+#pragma unroll
+        for (int i = 0; i < kListRegs; ++i)
+            if (i < nl) m2 = xl[i] < hi ? __builtin_fmaxf(m2, xl[i]) : m2;
+        const float xm = wave_max(m2);
+        const int c = cnt(xm);
+        if (c >= k) return xm;
+        hi = xm;
+    }
+    return lo;  // not reached: the count at the smallest list value is n >= k
+}
+
+// Gumbel race over the list entries with h >= cthr: each lane keeps its best
+// (z, id, h) with z = h / tau + G, larger z first, smaller id on ties.
+__device__ __forceinline__ void gumbel_list(Entry* list, int n, float cthr, bool filter, float inv_tau,
+                                            const NoiseKey& nk, int lane, float& bz, int& be, float& bh) {
+    // keep only the entries that can win, in order
+    int base = filter ? 0 : n;
+    for (int b0 = 0; filter && b0 < n; b0 += kWave) {
+        const int o = b0 + lane;
+        Entry en{kNegInf, 0};
+        if (o < n) en = list[o];
+        const bool pred = o < n && en.h >= cthr;
+        const uint64_t m = ballot(pred);
+        __builtin_amdgcn_wave_barrier();
+        if (pred) list[base + lanes_below(m)] = en;
+        base += popc(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (int b0 = 0; b0 < base; b0 += kWave) {
+        const int o = b0 + lane;
+        if (o < base) {
+            const Entry en = list[o];
+            const float z = __builtin_fmaf(en.h, inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)en.e)));
+            if (z > bz || (z == bz && en.e < be)) {
+                bz = z;
+                be = en.e;
+                bh = en.h;
+            }
+        }
+    }
+}
+
+// Load one row's dwords: slots below `nfull` are in range for every lane, the
+// rest only where j * 64 + lane < ndw (missing dwords read as `fill`).
+template <int NS>
+__device__ __forceinline__ void load_slots(gptr<uint32_t> base, int lane, int ndw, uint32_t fill,
+                                           uint32_t (&w)[NS]) {
+    const int nfull = ndw >> 6;
+    const gptr<uint32_t> p = base + lane;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        if (j < nfull) {
+            w[j] = p[j * kWave];
+        } else {
+            w[j] = fill;
+            if (j * kWave + lane < ndw) w[j] = p[j * kWave];
+        }
+    }
+}
+
+template <bool BF16, int NS>
+__device__ __forceinline__ void sample_small_body(const SampleArgs& a, const ReqTable& rq) {
     using R_t = Row<BF16, NS>;
     constexpr int NE = R_t::NE;
-    __shared__ float s_h[kWavesPerBlock][kListCap];
-    __shared__ int s_e[kWavesPerBlock][kListCap];
+    __shared__ Entry s_list[kWavesPerBlock][kListCap];
 
-    const int wv = threadIdx.x >> 6;
+    // every per-cell quantity below is wave-uniform (scalar registers)
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wv;
     if (wid >= (int64_t)a.rows * rq.npos) return;  // whole wave leaves together
@@ -122,34 +222,25 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleA
     const int V = a.V;
     const float s = rq.scale[r];
     const float tau = rq.tau[r];
-    float* lh = s_h[wv];
-    int* le = s_e[wv];
+    Entry* list = s_list[wv];
 
     // ---------------------------------------------------------------- load
     R_t R;
     if (BF16) {
         const uintptr_t cb = (uintptr_t)a.c;
-        const uint32_t* c32 = (const uint32_t*)(cb & ~(uintptr_t)3);
+        // dword-aligned view of c (u has the same address modulo 16)
+        const gptr<uint32_t> c32 = as_global<uint32_t>((const char*)a.c - (cb & 3));
         const int64_t g = (int64_t)((cb & 3) >> 1) + cell * V;
-        R.par = (int)(g & 1);
+        const int par = (int)(g & 1);
         const int64_t d0 = g >> 1;
-        const int ndw = (R.par + V + 1) >> 1;
+        const int ndw = (par + V + 1) >> 1;
+        R.ebase = 2 * lane - par;
         uint32_t cw[NS];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int d = j * kWave + lane;
-            cw[j] = 0xFF80FF80u;  // two bf16 -inf
-            if (d < ndw) cw[j] = c32[d0 + d];
-        }
+        load_slots<NS>(c32 + d0, lane, ndw, 0xFF80FF80u, cw);
         if (s != 0.0f) {
-            const uint32_t* u32 = (const uint32_t*)((uintptr_t)a.u & ~(uintptr_t)3);
+            const gptr<uint32_t> u32 = as_global<uint32_t>((const char*)a.u - (cb & 3));
             uint32_t uw[NS];
-#pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                const int d = j * kWave + lane;
-                uw[j] = 0xFF80FF80u;
-                if (d < ndw) uw[j] = u32[d0 + d];
-            }
+            load_slots<NS>(u32 + d0, lane, ndw, 0xFF80FF80u, uw);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 R.h[2 * j] = guided(bf16_lo(cw[j]), bf16_lo(uw[j]), s);
@@ -163,35 +254,27 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleA
             }
         }
         // the two half-dwords that belong to the neighbouring rows
-        if (R.par && lane == 0) R.h[0] = kNegInf;
-        if ((R.par + V) & 1) {
+        if (par && lane == 0) R.h[0] = kNegInf;
+        if ((par + V) & 1) {
             const int dl = ndw - 1;
 #pragma unroll
             for (int j = 0; j < NS; ++j)
                 if (j == (dl >> 6) && lane == (dl & 63)) R.h[2 * j + 1] = kNegInf;
         }
     } else {
-        R.par = 0;
-        const float* c = (const float*)a.c + cell * V;
-        float cv[NS];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int e = j * kWave + lane;
-            cv[j] = kNegInf;
-            if (e < V) cv[j] = c[e];
-        }
+        R.ebase = lane;
+        const gptr<uint32_t> c = as_global<uint32_t>(a.c) + cell * V;
+        uint32_t cw[NS];
+        load_slots<NS>(c, lane, V, 0xFF800000u, cw);
         if (s != 0.0f) {
-            const float* u = (const float*)a.u + cell * V;
+            const gptr<uint32_t> u = as_global<uint32_t>(a.u) + cell * V;
+            uint32_t uw[NS];
+            load_slots<NS>(u, lane, V, 0xFF800000u, uw);
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                const int e = j * kWave + lane;
-                float uv = kNegInf;
-                if (e < V) uv = u[e];
-                R.h[j] = guided(cv[j], uv, s);
-            }
+            for (int j = 0; j < NS; ++j) R.h[j] = guided(__uint_as_float(cw[j]), __uint_as_float(uw[j]), s);
         } else {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) R.h[j] = cv[j];
+            for (int j = 0; j < NS; ++j) R.h[j] = __uint_as_float(cw[j]);
         }
     }
 
@@ -210,9 +293,9 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleA
             const uint64_t m0 = ballot(R.h[2 * j] == M);
             const uint64_t m1 = ballot(R.h[2 * j + 1] == M);
             if (m0 | m1) {
-                const int a0 = m0 ? 2 * (j * kWave + (int)__builtin_ctzll(m0)) - R.par : 0x7FFFFFFF;
-                const int a1 = m1 ? 2 * (j * kWave + (int)__builtin_ctzll(m1)) + 1 - R.par : 0x7FFFFFFF;
-                am = a0 < a1 ? a0 : a1;
+                const int a0 = m0 ? 2 * (j * kWave + (int)__builtin_ctzll(m0)) : 0x7FFFFFFF;
+                const int a1 = m1 ? 2 * (j * kWave + (int)__builtin_ctzll(m1)) + 1 : 0x7FFFFFFF;
+                am = (a0 < a1 ? a0 : a1) - (R.ebase & 1);  // ebase & 1 == parity
                 break;
             }
         } else {
@@ -223,6 +306,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleA
             }
         }
     }
+    am = __builtin_amdgcn_readfirstlane(am);
 
     const float mL = M * kLog2e;
     float acc = 0.0f;
@@ -242,139 +326,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleA
         return;
     }
 
-    // ------------------------------------------------ top-k threshold (exact)
+    // ------------------------------------------------------------ sampling
     const int k = a.top_k;
-    // first pivot: mean + z0 * sd of (h - M) over the first slots, clamped
-    float sum = 0.0f, sq = 0.0f;
-    constexpr int NSTAT = NE < 4 ? NE : 4;
-#pragma unroll
-    for (int i = 0; i < NSTAT; ++i) {
-        const float d = __builtin_fmaxf(R.h[i] - M, -64.0f);
-        sum += d;
-        sq = __builtin_fmaf(d, d, sq);
-    }
-    const float nstat = (float)(NSTAT * kWave);
-    const float mean = wave_sum(sum) / nstat;
-    const float var = __builtin_fmaxf(wave_sum(sq) / nstat - mean * mean, 0.0f);
-    const float sd = __builtin_sqrtf(var) + 1e-3f;
-
-    float t = kNegInf;
-    bool have_t = false;     // t is exact
-    bool list_ok = false;    // the LDS list holds every id >= lo
-    float lo = M + mean + a.z0 * sd;
-    if (!(lo < M)) lo = M - sd;
-    float hi = M;
-    int c_hi = -1;
-    int c_lo = 0;
-    for (int tries = 0; tries < 8; ++tries) {
-        c_lo = count_and_compact(R, lo, lane, lh, le);
-        if (c_lo >= k && c_lo <= kListCap) {
-            list_ok = true;
-            break;
-        }
-        if (c_lo < k) {
-            hi = lo;
-            c_hi = c_lo;
-            if (tries < 3) {
-                lo = lo - (2.0f + 2.0f * tries) * sd;
-            } else {
-                // smallest finite h of the row
-                float mn = __builtin_huge_valf();
-#pragma unroll
-                for (int i = 0; i < NE; ++i) mn = R.h[i] > kNegInf ? __builtin_fminf(mn, R.h[i]) : mn;
-                lo = wave_min(mn);
-                if (R.count_ge(lo) < k) {  // fewer than k finite ids: t = -inf
-                    t = kNegInf;
-                    have_t = true;
-                    break;
-                }
-            }
-        } else {
-            // too many ids for the list: move the pivot up towards hi
-            const float target = 0.5f * (float)kListCap;
-            const float chi = (float)(c_hi < 0 ? 1 : c_hi);
-            float p = lo + (hi - lo) * (((float)c_lo - target) / ((float)c_lo - chi));
-            if (!(p > lo && p < hi)) p = 0.5f * lo + 0.5f * hi;
-            if (!(p > lo && p < hi)) {
-                // lo and hi are adjacent floats: every id in [lo, hi) equals lo
-                t = lo;
-                have_t = true;
-                break;
-            }
-            const int cp = R.count_ge(p);
-            if (cp >= k) {
-                lo = p;
-            } else {
-                hi = p;
-                c_hi = cp;
-            }
-        }
-    }
-
-    // list registers (all ids >= lo), refined on a few registers per lane
-    float xl[kListRegs];
-    int el[kListRegs];
-    const int nl = list_ok ? (c_lo + kWave - 1) / kWave : 0;
-    if (list_ok) {
-#pragma unroll
-        for (int i = 0; i < kListRegs; ++i) {
-            const int o = i * kWave + lane;
-            xl[i] = kNegInf;
-            el[i] = 0x7FFFFFFF;
-            if (i < nl && o < c_lo) {
-                xl[i] = lh[o];
-                el[i] = le[o];
-            }
-        }
-        auto cnt_l = [&](float x) {
-            int n = 0;
-#pragma unroll
-            for (int i = 0; i < kListRegs; ++i)
-                if (i < nl) n += popc(ballot(xl[i] >= x));
-            return n;
-        };
-        hi = M;
-        c_hi = cnt_l(M);
-        int clo = c_lo;
-        if (c_hi >= k) {
-            t = M;
-        } else {
-            for (int it = 0; it < 48; ++it) {
-                const int nw = clo - c_hi;
-                if (nw <= 4 || k - c_hi <= 1) break;
-                float p = lo + (hi - lo) * (((float)(clo - k) + 0.5f) / (float)nw);
-                if (!(p > lo && p < hi)) p = 0.5f * lo + 0.5f * hi;
-                if (!(p > lo && p < hi)) break;
-                const int c = cnt_l(p);
-                if (c >= k) {
-                    lo = p;
-                    clo = c;
-                } else {
-                    hi = p;
-                    c_hi = c;
-                }
-            }
-            // take distinct values from the top of [lo, hi) until the count reaches k
-            for (int it = 0; it <= kListCap; ++it) {
-                float m2 = kNegInf;
-#pragma unroll
-                for (int i = 0; i < kListRegs; ++i)
-                    if (i < nl) m2 = xl[i] < hi ? __builtin_fmaxf(m2, xl[i]) : m2;
-                const float xm = wave_max(m2);
-                const int c = cnt_l(xm);
-                if (c >= k) {
-                    t = xm;
-                    break;
-                }
-                hi = xm;
-                c_hi = c;
-            }
-        }
-        have_t = true;
-    }
-    if (!have_t) t = kth_by_bisection(R, k, V, M);
-
-    // ------------------------------------------------------------ Gumbel-max
     NoiseKey nk;
     nk.k0 = a.k0;
     nk.k1 = a.k1;
@@ -382,77 +335,156 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small(SampleA
     nk.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
     nk.rid = rq.rid[r];
     const float inv_tau = rq.inv_tau[r];
-    // ids below cthr cannot beat the argmax (see the header comment)
+    // No id with h below `prune` can beat the argmax: its h/tau plus the largest
+    // possible noise stays below M/tau plus the smallest possible noise.
     const float prune = M - tau * (kGumbelBound - kGumbelFloor);
-    const float cthr = __builtin_fmaxf(t, prune);
+    const bool want_t = a.thresholds != nullptr;
 
+    float t = kNegInf;
+    float cthr = prune;  // draw noise for list entries with h >= cthr
+    int n_list = -1;     // entries in the LDS list (all ids >= the list floor), or -1
+    // Fast path: the ids that can still win.  If at most top_k of them reach
+    // `prune`, they all lie inside the top-ratio set (fewer than top_k ids are
+    // larger than any of them), so the filter is satisfied without locating its
+    // exact threshold; otherwise the threshold is above `prune` and is found
+    // among them.
+    if (!want_t) {
+        const int nb = R.count_compact(prune, list);
+        if (nb <= kListCap) {
+            n_list = nb;
+            if (nb > k) {
+                t = list_kth(list, nb, k, prune, M, lane);
+                cthr = __builtin_fmaxf(t, prune);
+            }
+        }
+    }
+    if (n_list < 0) {
+        // Exact threshold over the whole row: pivot from the row's spread, count
+        // and compact the ids above the pivot, refine on the compacted list.
+        bool have_t = false;
+        float sum = 0.0f, sq = 0.0f;
+        constexpr int NSTAT = NE < 4 ? NE : 4;
+#pragma unroll
+        for (int i = 0; i < NSTAT; ++i) {
+            const float d = __builtin_fmaxf(R.h[i] - M, -64.0f);
+            sum += d;
+            sq = __builtin_fmaf(d, d, sq);
+        }
+        constexpr float inv_n = 1.0f / (float)(NSTAT * kWave);
+        const float mean = wave_sum(sum) * inv_n;
+        const float var = __builtin_fmaxf(wave_sum(sq) * inv_n - mean * mean, 0.0f);
+        const float sd = __builtin_amdgcn_sqrtf(var) + 1e-3f;
+        float lo = M + mean + a.z0 * sd;
+        if (!(lo < M)) lo = M - sd;
+        float hi = M;
+        int c_hi = -1;
+        for (int tries = 0; tries < 8; ++tries) {
+            const int c_lo = R.count_compact(lo, list);
+            if (c_lo >= k && c_lo <= kListCap) {
+                t = list_kth(list, c_lo, k, lo, M, lane);
+                n_list = c_lo;
+                have_t = true;
+                break;
+            }
+            if (c_lo < k) {
+                hi = lo;
+                c_hi = c_lo;
+                if (tries < 3) {
+                    lo = lo - (2.0f + 2.0f * tries) * sd;
+                } else {
+                    lo = min_finite(R);
+                    if (R.count_ge(lo) < k) {  // fewer than k finite ids: t = -inf
+                        t = kNegInf;
+                        have_t = true;
+                        break;
+                    }
+                }
+            } else {
+                // too many ids for the list: move the pivot up towards hi
+                const float target = 0.5f * (float)kListCap;
+                const float chi = (float)(c_hi < 0 ? 1 : c_hi);
+                float p = lo + (hi - lo) * ((float)c_lo - target) * __builtin_amdgcn_rcpf((float)c_lo - chi);
+                if (!(p > lo && p < hi)) p = 0.5f * lo + 0.5f * hi;
+                if (!(p > lo && p < hi)) {
+                    // lo and hi are adjacent floats: every id in [lo, hi) equals lo
+                    t = lo;
+                    have_t = true;
+                    break;
+                }
+                const int cp = R.count_ge(p);
+                if (cp >= k) {
+                    lo = p;
+                } else {
+                    hi = p;
+                    c_hi = cp;
+                }
+            }
+        }
+        if (!have_t) t = kth_by_bisection(R, k, V, M);
+        cthr = __builtin_fmaxf(t, prune);
+    }
+
+    // ------------------------------------------------------------ Gumbel-max
     float bz = kNegInf, bh = kNegInf;
     int be = 0x7FFFFFFF;
-    if (list_ok && cthr >= lo) {
-        // recompact the survivors from the list registers
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < kListRegs; ++i) {
-            if (i < nl) {
-                const bool pred = xl[i] >= cthr;
-                const uint64_t m = ballot(pred);
-                if (m) {
-                    const int o = base + lanes_below(m);
-                    if (pred) {
-                        lh[o] = xl[i];
-                        le[o] = el[i];
-                    }
-                    base += popc(m);
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        for (int b0 = 0; b0 < base; b0 += kWave) {
-            const int o = b0 + lane;
-            if (o < base) {
-                const float hv = lh[o];
-                const int ev = le[o];
-                const float z = __builtin_fmaf(hv, inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)ev)));
-                if (z > bz || (z == bz && ev < be)) {
-                    bz = z;
-                    be = ev;
-                    bh = hv;
-                }
-            }
-        }
+    if (n_list >= 0) {
+        gumbel_list(list, n_list, cthr, cthr > prune, inv_tau, nk, lane, bz, be, bh);
     } else {
-        // every valid id with h >= cthr, straight from the row registers
-#pragma unroll
+        // every valid id with h >= cthr, straight from the row registers (rare:
+        // fewer than top_k finite ids, massive ties, or a failed pivot search);
+        // the slot loop stays rolled so the noise code is emitted once
+#pragma unroll 1
         for (int i = 0; i < NE; ++i) {
-            const int ev = R.id_of(i, lane);
-            const bool pred = R.h[i] >= cthr && ev >= 0 && ev < V;
+            float hv = R.h[0];
+#pragma unroll
+            for (int j = 1; j < NE; ++j) hv = (i == j) ? R.h[j] : hv;
+            const int ev = BF16 ? R.ebase + 2 * kWave * (i >> 1) + (i & 1) : R.ebase + kWave * i;
+            const bool pred = hv >= cthr && ev >= 0 && ev < V;
             if (ballot(pred)) {
                 if (pred) {
-                    const float z =
-                        __builtin_fmaf(R.h[i], inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)ev)));
+                    const float z = __builtin_fmaf(hv, inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)ev)));
                     if (z > bz || (z == bz && ev < be)) {
                         bz = z;
                         be = ev;
-                        bh = R.h[i];
+                        bh = hv;
                     }
                 }
             }
         }
     }
-    wave_argmax3(bz, be, bh);
+    const int wl = wave_argmax(bz, be);
+    bh = readlane_f(bh, wl);
     if (lane == 0) {
         a.tokens[cell] = be;
         a.logprobs[cell] = bh - lse;
-        if (a.thresholds) a.thresholds[cell] = t + 0.0f;
+        if (want_t) a.thresholds[cell] = t + 0.0f;
     }
+}
+
+// Rows of up to 9 register slots (bf16) or 16 (f32) are held to 7 waves per SIMD
+// or more (at most 73 VGPRs) without spilling, so a 6.5k-cell step fits in one
+// round of the GPU's 1024 SIMDs; wider rows take what the compiler needs.
+template <bool BF16, int NS>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) __attribute__((amdgpu_waves_per_eu(7, 8)))
+void k_sample_small(SampleArgs a, ReqTable rq) {
+    sample_small_body<BF16, NS>(a, rq);
+}
+template <bool BF16, int NS>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small_wide(SampleArgs a, ReqTable rq) {
+    sample_small_body<BF16, NS>(a, rq);
 }
 
 template <bool BF16, int NS>
 hipError_t launch_ns(const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
     const int64_t cells = (int64_t)a.rows * rq.npos;
     const int64_t blocks = (cells + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((k_sample_small<BF16, NS>), dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
-                       st, a, rq);
+    constexpr bool kOcc = BF16 ? NS <= 9 : NS <= 16;
+    if constexpr (kOcc)
+        hipLaunchKernelGGL((k_sample_small<BF16, NS>), dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
+                           st, a, rq);
+    else
+        hipLaunchKernelGGL((k_sample_small_wide<BF16, NS>), dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave),
+                           0, st, a, rq);
     return hipGetLastError();
 }
 
