@@ -70,10 +70,10 @@ def to_dev(arr: np.ndarray):
 
 def kernel_name(w, kind: str) -> str:
     if kind == "draft":
-        return "k_greedy_lse"
+        return "k_greedy_parts+k_greedy_merge"
     slots = ((w.vocab + 2) // 2 if w.dtype == "bf16" else w.vocab + 63) // 64
     if slots > (16 if w.dtype == "bf16" else 32):
-        return "k_sample_row"
+        return "k_sample_parts+k_sample_merge"
     return "k_sample_small" if slots <= (9 if w.dtype == "bf16" else 16) else "k_sample_small_wide"
 
 

@@ -19,6 +19,8 @@
 
 struct ds_sampler {
     int device;
+    // streaming-kernel workspace: one partial record per (row, vocabulary part)
+    ds::PartRec* ws_part;
     int32_t vocab;
     int32_t dtype;
     int32_t max_rows;
@@ -118,6 +120,9 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
     if (device < 0 || device >= ndev) return fail(DS_ERR_INVALID_ARG, "device %d out of range", device);
 
     ds_sampler* s = new (std::nothrow) ds_sampler();
+    if (s) {
+        s->ws_part = nullptr;
+    }
     if (!s) return fail(DS_ERR_NO_MEMORY, "host allocation failed");
     s->device = device;
     s->vocab = vocab;
@@ -132,11 +137,28 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
     double q0 = 1.25 * (double)s->top_k / vocab + 2.0 / std::sqrt((double)vocab);
     if (q0 > 0.5) q0 = 0.5;
     s->z0 = (float)normal_quantile(1.0 - q0);
+    {
+        DeviceGuard dg(device);
+        if (dg.err != hipSuccess) {
+            delete s;
+            return hip_fail(dg.err, "hipSetDevice");
+        }
+        const hipError_t e1 = hipMalloc(&s->ws_part, sizeof(ds::PartRec) * ds::kWorkParts);
+        if (e1 != hipSuccess) {
+            delete s;
+            return fail(DS_ERR_NO_MEMORY, "device workspace allocation failed");
+        }
+    }
     *out = s;
     return DS_OK;
 }
 
-void ds_sample_destroy(ds_sampler* s) { delete s; }
+void ds_sample_destroy(ds_sampler* s) {
+    if (!s) return;
+    DeviceGuard dg(s->device);
+    (void)hipFree(s->ws_part);
+    delete s;
+}
 
 int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
               const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
@@ -199,7 +221,7 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
     a.tokens = tokens_out;
     a.logprobs = logprobs_out;
     a.thresholds = threshold_out;
-    a.work = nullptr;
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
 
     // one launch per group of up to 64 non-empty requests (contiguous positions)
     int32_t r = 0;
@@ -228,9 +250,22 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         rq.n = n;
         rq.offs[n] = rel;
         rq.npos = rel;
-        const hipError_t e = small ? ds::launch_sample_small(bf16, a, rq, st)
-                                   : ds::launch_sample_row(bf16, a, rq, st);
-        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+        if (small) {
+            const hipError_t e = ds::launch_sample_small(bf16, a, rq, st);
+            if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+        } else {
+            // the streaming kernel: cells in batches that fit the workspace
+            const int64_t cells = (int64_t)num_rows * rel;
+            a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
+            a.w.nparts = a.w.ppc * s->vocab_chunks;
+            const int64_t slots = ds::kWorkParts / a.w.nparts;
+            for (int64_t c0 = 0; c0 < cells; c0 += slots) {
+                a.w.cell_base = c0;
+                a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
+                const hipError_t e = ds::launch_sample_row(bf16, a, rq, st);
+                if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+            }
+        }
         pos += rel;
     }
     return DS_OK;
@@ -263,8 +298,17 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
     a.lse = lse_out;
     a.logprob = logprob_out;
     a.triples = triples_out;
-    const hipError_t e = ds::launch_greedy_lse(s->dtype == DS_DTYPE_BF16, a, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "greedy kernel launch");
+    const bool bf16 = s->dtype == DS_DTYPE_BF16;
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, n_rows);
+    a.w.nparts = a.w.ppc * s->vocab_chunks;
+    const int64_t slots = ds::kWorkParts / a.w.nparts;
+    for (int64_t c0 = 0; c0 < n_rows; c0 += slots) {
+        a.w.cell_base = c0;
+        a.w.ncells = (int32_t)(n_rows - c0 < slots ? n_rows - c0 : slots);
+        const hipError_t e = ds::launch_greedy_lse(bf16, a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "greedy kernel launch");
+    }
     return DS_OK;
 }
 

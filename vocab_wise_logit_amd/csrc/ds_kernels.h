@@ -8,6 +8,35 @@
 
 namespace ds {
 
+// Device workspace of the streaming kernels.  A row is cut into `nparts`
+// (vocabulary chunk, part) pieces, each reduced by its own workgroup to a
+// partial record; a second kernel merges each row.
+struct PartRec {
+    float m;      // max of h over the part
+    float s;      // sum of exp(h - m) over the part
+    int id;       // smallest id attaining m (INT32_MAX when the part is empty)
+    int nq;       // ids the part's Gumbel race scored, or -1 when it ran none
+    float bz;     // best perturbed score h/tau + G among them
+    int be;       // its id (smallest on equal scores)
+    float bh;     // its h
+    int pad;
+};
+struct Cand {
+    float h;
+    int e;
+};
+constexpr int kRowThreads = 512;
+constexpr int kRowU = 4;            // 16-byte pieces per thread per group
+constexpr int kWorkParts = 16384;   // parts the workspace holds per launch
+
+struct RowWork {
+    PartRec* part;     // [slots * nparts]
+    int32_t nparts;    // vocab_chunks * parts_per_chunk
+    int32_t ppc;       // parts per chunk
+    int64_t cell_base; // first launch-relative cell handled by this launch
+    int32_t ncells;    // cells in this launch (<= slots)
+};
+
 // Arguments common to one sampler launch (one group of <= 64 requests).
 struct SampleArgs {
     const void* c;          // [C, P, V] logits (f32 or bf16)
@@ -22,7 +51,7 @@ struct SampleArgs {
     int32_t* tokens;        // [C, P]
     float* logprobs;        // [C, P]
     float* thresholds;      // [C, P] or nullptr
-    float* work;            // row kernel scratch (unused by the small kernel)
+    RowWork w;              // streaming kernel workspace (unused by the small kernel)
 };
 
 // Largest row the wave-per-cell kernel keeps in registers, in dwords per lane.
@@ -44,7 +73,11 @@ struct GreedyArgs {
     float* lse;
     float* logprob;
     float* triples;     // [chunks][n_rows][3] or nullptr
+    RowWork w;
 };
+
+// Parts per chunk for a launch of `cells` rows (see ds_row.hip).
+int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells);
 
 hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st);
 

@@ -1,123 +1,150 @@
-// ds_row.hip -- one 1024-thread workgroup per row for large vocabularies.
+// ds_row.hip -- streaming kernels for large vocabularies.
 //
-// The row is streamed once from HBM in 16-byte pieces.  Each thread keeps an
-// online (max, sum of exp) pair ([DRAFT] "Design and invariants": per-shard max,
-// log-sum-exp and argmax), and the vocabulary is cut into `vocab_chunks`
-// contiguous chunks, each reduced to a (max, lse, argmax) triple that is merged
-// with the smallest-id tie rule -- the page's tensor-parallel shards, here as
-// chunks of one row inside one workgroup.
+// A row is cut into contiguous vocabulary chunks ([DRAFT] "Design and
+// invariants": each tensor-parallel shard reduces its part of the vocabulary to
+// (max, log-sum-exp, argmax); here the shards are chunks of one row on one GPU),
+// and each chunk into `ppc` parts.  One 512-thread workgroup streams one part
+// once from HBM in 16-byte pieces, four pieces per thread per group, keeping an
+// online max and exp-sum per thread, and writes a partial record to the
+// workspace.  A second, small kernel merges each row's partial records in
+// order: larger max wins, equal maxima keep the smaller id, sums add in
+// probability space.  The kernel boundary is the only synchronisation; no
+// workgroup ever waits for another.
 //
-// Sampling ([ISSUE] comment on the API shape: top-ratio filter plus Gumbel) needs
-// the few ids that can still win the Gumbel race.  While streaming, each thread
-// records the maximum of every group of 4 pieces it loaded in LDS.  After the
-// pass the argmax's own noise G_a fixes a bound b = (M/tau + G_a - Gmax) * tau
-// below which no id can win; only groups whose maximum reaches b are re-read
-// (typically a few hundred of the row's ids), their ids with h >= b become
-// candidates, and:
-//   - if at most top_k ids reach b, all of them are inside the top-ratio set;
-//   - otherwise the exact top_k-th largest h is among the candidates and is
-//     selected there (radix select on the LDS list).
-// When the lists overflow, when the caller asks for the threshold and it lies
-// below b, or when the fallback is forced, the exact multi-pass path runs: a
-// radix select of the threshold over re-reads of the row and a Gumbel pass over
-// every kept id.  Both paths return the same token.
+// Sampling ([ISSUE] comment on the API shape: top-ratio filter plus Gumbel).
+// While it streams, each wave keeps a bound below which no id can win the
+// Gumbel race: first from its running maximum (an id more than
+// tau * (Gmax - Gmin) below some other id always loses to it), then from the
+// best perturbed score it has drawn so far.  Ids at or above the bound are
+// queued in LDS and scored 64 at a time, one per lane, so the noise costs one
+// Philox block per queued id and nothing for the rest.  The part records its
+// best (score, id, h) and how many ids it queued.  Every id that can win the
+// row's race was queued by its part, so if the parts queued at most top_k ids in
+// all, every id that can win lies inside the top-ratio set and the best of the
+// part winners is the row's winner.  Otherwise (a flat row), when the fallback
+// is forced, or for the threshold output, the merge runs the exact multi-pass
+// path over the row: a radix select of the threshold and a Gumbel pass over
+// every kept id.
 #include <stdint.h>
 
 #include "ds_device.h"
 #include "ds_kernels.h"
 
+#include <type_traits>
+
 namespace ds {
 namespace {
 
-constexpr int NT = 1024;
+constexpr int NT = kRowThreads;
 constexpr int NWAVES = NT / kWave;
-constexpr int U = 4;          // pieces per group
-constexpr int GCAP = 8192;    // group maxima kept in LDS
-constexpr int GLCAP = 2048;   // groups re-read
-constexpr int CCAP = 2048;    // candidate (h, id) pairs
+constexpr int U = kRowU;
 
-enum Mode { kModeGreedy = 0, kModeSample = 1 };
-
-struct Shared {
-    float gmax[GCAP];
-    int glist[GLCAP];
-    float ch[CCAP];
-    int ce[CCAP];
-    uint32_t hist[256];
-    float red_f[NWAVES];
-    float red_f2[NWAVES];
-    int red_i[NWAVES];
-    int cnt_g;
-    int cnt_c;
-    int flag;
+// Cross-wave reduction slots.
+struct Red {
+    float f[NWAVES];
+    float f2[NWAVES];
+    int i[NWAVES];
     uint32_t bcast_u;
-    float bcast_f;
 };
 
-__device__ __forceinline__ float block_max(float x, Shared& sh) {
+// A sampled part's Gumbel race queues, per wave: pieces holding an id at or
+// above the bound (their decoded h and first id), and ids at or above the bound.
+// Each is drained once it holds 64 entries, and one step adds at most 64, so 128
+// entries never overflow.
+template <bool BF16, bool SAMPLE>
+struct PartLDS {
+    static constexpr int EPP = BF16 ? 8 : 4;
+    static constexpr int kQ = SAMPLE ? 2 * kWave : 1;
+    float ph[NWAVES][kQ][EPP];
+    int pv[NWAVES][kQ];
+    Cand q[NWAVES][kQ];
+    uint32_t bkey;  // order key of the block's race bound (only grows)
+    Red r;
+};
+
+// The merge's radix-select histogram.
+struct MergeLDS {
+    uint32_t hist[256];
+    Red r;
+};
+
+__device__ __forceinline__ float block_max(float x, Red& r) {
     x = wave_max(x);
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if (lane_id() == 0) sh.red_f[w] = x;
+    if (lane_id() == 0) r.f[w] = x;
     __syncthreads();
-    float r = sh.red_f[0];
+    float y = r.f[0];
 #pragma unroll
-    for (int i = 1; i < NWAVES; ++i) r = __builtin_fmaxf(r, sh.red_f[i]);
-    return r;
+    for (int i = 1; i < NWAVES; ++i) y = __builtin_fmaxf(y, r.f[i]);
+    return y;
 }
 
-__device__ __forceinline__ float block_sum(float x, Shared& sh) {
+__device__ __forceinline__ float block_sum(float x, Red& r) {
     x = wave_sum(x);
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if (lane_id() == 0) sh.red_f[w] = x;
+    if (lane_id() == 0) r.f[w] = x;
     __syncthreads();
-    float r = 0.0f;
+    float y = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NWAVES; ++i) r += sh.red_f[i];
-    return r;
+    for (int i = 0; i < NWAVES; ++i) y += r.f[i];
+    return y;
 }
 
-__device__ __forceinline__ int block_min_i(int x, Shared& sh) {
+__device__ __forceinline__ int block_min_i(int x, Red& r) {
     x = wave_min_i(x);
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if (lane_id() == 0) sh.red_i[w] = x;
+    if (lane_id() == 0) r.i[w] = x;
     __syncthreads();
-    int r = sh.red_i[0];
+    int y = r.i[0];
 #pragma unroll
-    for (int i = 1; i < NWAVES; ++i) r = min(r, sh.red_i[i]);
-    return r;
+    for (int i = 1; i < NWAVES; ++i) y = min(y, r.i[i]);
+    return y;
+}
+
+// Sum of a wave-uniform count over the block.
+__device__ __forceinline__ int block_sum_uniform(int x, Red& r) {
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane_id() == 0) r.i[w] = x;
+    __syncthreads();
+    int y = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) y += r.i[i];
+    return y;
 }
 
 // Block argmax of (z, id, h): larger z, then smaller id.
-__device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Shared& sh) {
+__device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Red& r) {
     const int wl = wave_argmax(z, id);
     hv = readlane_f(hv, wl);
     const int w = threadIdx.x >> 6;
     __syncthreads();
     if (lane_id() == 0) {
-        sh.red_f[w] = z;
-        sh.red_i[w] = id;
-        sh.red_f2[w] = hv;
+        r.f[w] = z;
+        r.i[w] = id;
+        r.f2[w] = hv;
     }
     __syncthreads();
-    z = sh.red_f[0];
-    id = sh.red_i[0];
-    hv = sh.red_f2[0];
+    z = r.f[0];
+    id = r.i[0];
+    hv = r.f2[0];
 #pragma unroll
     for (int i = 1; i < NWAVES; ++i) {
-        const bool take = (sh.red_f[i] > z) || (sh.red_f[i] == z && sh.red_i[i] < id);
-        z = take ? sh.red_f[i] : z;
-        id = take ? sh.red_i[i] : id;
-        hv = take ? sh.red_f2[i] : hv;
+        const bool take = (r.f[i] > z) || (r.f[i] == z && r.i[i] < id);
+        z = take ? r.f[i] : z;
+        id = take ? r.i[i] : id;
+        hv = take ? r.f2[i] : hv;
     }
 }
 
-// Elements of one 16-byte piece, widened and guided.
+// ------------------------------------------------------------- row geometry
+
 template <bool BF16>
 struct Piece {
-    static constexpr int EPP = BF16 ? 8 : 4;
+    static constexpr int EPP = BF16 ? 8 : 4;  // ids per 16-byte piece
     float h[EPP];
 };
 
@@ -155,15 +182,7 @@ __device__ __forceinline__ void decode_piece(const u32x4 cw, const u32x4 uw, flo
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void load_piece(gptr<u32x4> c16, gptr<u32x4> u16, int64_t q, float s,
-                                           bool use_u, Piece<BF16>& P) {
-    const u32x4 cw = c16[q];
-    const u32x4 uw = use_u ? u16[q] : cw;
-    decode_piece<BF16>(cw, uw, s, use_u, P);
-}
-
-// Geometry of one row inside the 16-byte-aligned view of the tensors.
+// One row inside the 16-byte-aligned views of c and u.
 struct RowGeom {
     gptr<u32x4> c16;
     gptr<u32x4> u16;
@@ -171,42 +190,47 @@ struct RowGeom {
     int V;
     int L;          // chunk length ceil(V / nch)
     int nch;
-    int gpc;        // group ids reserved per chunk
+    int ppc;        // parts per chunk
 };
 
+// Pieces [q0, q1] (q1 < q0 when empty) holding part `q` of chunk `j`, whose ids are
+// [lo, hi).
 template <bool BF16>
-struct ChunkRange {
-    int lo, hi;          // row ids [lo, hi)
-    int64_t q0, q1;      // first / last piece index (q1 < q0 when empty)
-    __device__ ChunkRange(const RowGeom& G, int j) {
+struct PartRange {
+    int lo, hi;
+    int64_t q0, q1;
+    __device__ PartRange(const RowGeom& G, int j, int q) {
         constexpr int EPP = Piece<BF16>::EPP;
         lo = min(G.V, j * G.L);
         hi = min(G.V, lo + G.L);
+        q0 = 0;
+        q1 = -1;
         if (hi > lo) {
-            q0 = (G.gbase + lo) / EPP;
-            q1 = (G.gbase + hi - 1) / EPP;
-        } else {
-            q0 = 0;
-            q1 = -1;
+            const int64_t c0 = (G.gbase + lo) / EPP;
+            const int64_t c1 = (G.gbase + hi - 1) / EPP;
+            const int64_t per = (c1 - c0 + G.ppc) / G.ppc;
+            q0 = c0 + (int64_t)q * per;
+            q1 = min(c1, q0 + per - 1);
         }
     }
 };
 
-// Mask the ids of a piece that fall outside [lo, hi) (row-relative).
 template <bool BF16>
-__device__ __forceinline__ void mask_piece(Piece<BF16>& P, int64_t q, const RowGeom& G, int lo, int hi) {
+__device__ __forceinline__ void load_piece(const RowGeom& G, int64_t q, float s, bool use_u, int lo, int hi,
+                                           Piece<BF16>& P) {
     constexpr int EPP = Piece<BF16>::EPP;
+    const u32x4 cw = G.c16[q];
+    const u32x4 uw = use_u ? G.u16[q] : cw;
+    decode_piece<BF16>(cw, uw, s, use_u, P);
     const int64_t v0 = q * EPP - G.gbase;
     if (v0 < lo || v0 + EPP > hi) {
 #pragma unroll
-        for (int i = 0; i < EPP; ++i) {
-            const int64_t v = v0 + i;
-            if (v < lo || v >= hi) P.h[i] = kNegInf;
-        }
+        for (int i = 0; i < EPP; ++i)
+            if (v0 + i < lo || v0 + i >= hi) P.h[i] = kNegInf;
     }
 }
 
-// Visit every id of the row (all chunks): f(v, h).  Used by the exact paths.
+// Visit every id of the row: f(v, h).  Used by the exact multi-pass path.
 template <bool BF16, typename F>
 __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_u, F&& f) {
     constexpr int EPP = Piece<BF16>::EPP;
@@ -214,8 +238,7 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
     const int64_t q1 = (G.gbase + G.V - 1) / EPP;
     for (int64_t q = q0 + threadIdx.x; q <= q1; q += NT) {
         Piece<BF16> P;
-        load_piece<BF16>(G.c16, G.u16, q, s, use_u, P);
-        mask_piece<BF16>(P, q, G, 0, G.V);
+        load_piece<BF16>(G, q, s, use_u, 0, G.V, P);
         const int64_t v0 = q * EPP - G.gbase;
 #pragma unroll
         for (int i = 0; i < EPP; ++i)
@@ -223,9 +246,29 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
     }
 }
 
+// Pick the 8-bit digit holding the kk-th largest key from the histogram.
+__device__ __forceinline__ void pick_digit(MergeLDS& sh, int& kk, uint32_t& prefix, uint32_t& pmask, int shift) {
+    if (threadIdx.x == 0) {
+        int above = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+            const int c = (int)sh.hist[d];
+            if (above + c >= kk) break;
+            above += c;
+        }
+        sh.r.bcast_u = (uint32_t)d | ((uint32_t)above << 8);
+    }
+    __syncthreads();
+    const uint32_t d = sh.r.bcast_u & 255u;
+    kk -= (int)(sh.r.bcast_u >> 8);
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+}
+
 // Exact top_k-th largest h of the row: four 8-bit radix passes over re-reads.
 template <bool BF16>
-__device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, Shared& sh) {
+__device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, MergeLDS& sh) {
     uint32_t prefix = 0, pmask = 0;
     int kk = k;
     for (int pass = 0; pass < 4; ++pass) {
@@ -237,407 +280,493 @@ __device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, 
             if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
         });
         __syncthreads();
-        if (threadIdx.x == 0) {
-            int above = 0;
-            int d = 255;
-            for (; d > 0; --d) {
-                const int c = (int)sh.hist[d];
-                if (above + c >= kk) break;
-                above += c;
-            }
-            sh.bcast_u = (uint32_t)d | ((uint32_t)above << 8);
-        }
-        __syncthreads();
-        const uint32_t d = sh.bcast_u & 255u;
-        kk -= (int)(sh.bcast_u >> 8);
-        prefix |= d << shift;
-        pmask |= 255u << shift;
-        __syncthreads();
+        pick_digit(sh, kk, prefix, pmask, shift);
     }
     return key_value(prefix);
 }
 
-// Exact top_k-th largest among the first n candidates in LDS (n >= k).
-__device__ float radix_select_list(int n, int k, Shared& sh) {
-    uint32_t prefix = 0, pmask = 0;
-    int kk = k;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += NT) {
-            const uint32_t key = order_key(sh.ch[i] + 0.0f);
-            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int above = 0;
-            int d = 255;
-            for (; d > 0; --d) {
-                const int c = (int)sh.hist[d];
-                if (above + c >= kk) break;
-                above += c;
-            }
-            sh.bcast_u = (uint32_t)d | ((uint32_t)above << 8);
-        }
-        __syncthreads();
-        const uint32_t d = sh.bcast_u & 255u;
-        kk -= (int)(sh.bcast_u >> 8);
-        prefix |= d << shift;
-        pmask |= 255u << shift;
-        __syncthreads();
-    }
-    return key_value(prefix);
-}
+// ----------------------------------------------------------- one part
 
-// Wave-aggregated append of this lane's item to an LDS counter; returns the slot
-// (or -1 when the lane has nothing).
-__device__ __forceinline__ int wave_append(bool pred, int* counter) {
-    const uint64_t m = ballot(pred);
-    if (!m) return -1;
-    int base = 0;
-    const int leader = (int)__builtin_ctzll(m);
-    if (lane_id() == leader) base = atomicAdd(counter, popc(m));
-    base = __builtin_amdgcn_readlane(base, leader);
-    return pred ? base + lanes_below(m) : -1;
-}
-
-struct RowResult {
-    float M;       // row max of h
-    float lse;     // log-sum-exp of h
-    int id;        // smallest argmax
+// Per-cell parameters of one sampled (or greedy) row.
+struct CellParams {
+    int64_t cell;   // index into the [C, P] outputs
+    float s, tau, inv_tau;
+    NoiseKey nk;
 };
 
-// The single streaming pass: per-chunk triples merged into the row result.
-// Optionally writes each group's maximum to sh.gmax and each chunk's triple.
-template <bool BF16>
-__device__ RowResult stream_row(const RowGeom& G, float s, bool use_u, bool keep_groups,
-                                float* triples, int64_t n_rows, int64_t row_index, Shared& sh) {
+struct PartOut {
+    float m, s;
+    int id;
+    // Gumbel race of a sampled part: best (score, id, h) among the queued ids and
+    // how many ids were queued
+    float bz, bh;
+    int be, nq;
+};
+
+// Stream one part: online max / exp-sum per thread, block-reduced to (m, s,
+// smallest argmax).  A thread notes the id of its maximum while the group that
+// raised it is still in registers, so no re-read is needed at the end.  With
+// `race`, each wave also runs the Gumbel race over the ids that can still win
+// (queued in LDS, scored 64 at a time).  At most 64 VGPRs: four workgroups per CU
+// keep enough loads in flight.
+template <bool BF16, bool SAMPLE>
+__device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, const CellParams& cp, bool use_u,
+                               bool race, PartLDS<BF16, SAMPLE>& sh) {
     constexpr int EPP = Piece<BF16>::EPP;
-    float Mrow = kNegInf, Srow = 0.0f;
-    int idrow = 0x7FFFFFFF;
-    for (int j = 0; j < G.nch; ++j) {
-        const ChunkRange<BF16> cr(G, j);
-        float m = kNegInf, acc = 0.0f;
-        int bg = -1;  // group (within chunk) holding this thread's max
-        const int64_t nq = cr.q1 - cr.q0 + 1;
-        const int its = (int)((nq + (int64_t)NT * U - 1) / ((int64_t)NT * U));
-        // one group: U raw 16-byte pieces of c (and u); two groups are in flight
-        // at a time (ping-pong) so the loads of the next group overlap the math
-        // on the current one
-        struct Raw {
-            u32x4 c[U], u[U];
-        };
-        auto load = [&](Raw& R, int it) {
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const int64_t q = cr.q0 + (int64_t)it * NT * U + (int64_t)uu * NT + threadIdx.x;
-                const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
-                R.c[uu] = u32x4{ninf, ninf, ninf, ninf};
-                R.u[uu] = R.c[uu];
-                if (q <= cr.q1) {
-                    R.c[uu] = G.c16[q];
-                    if (use_u) R.u[uu] = G.u16[q];
+    const float s = cp.s;
+    float m = kNegInf, acc = 0.0f;
+    int mid = 0x7FFFFFFF;  // smallest id of this thread attaining m
+    const int64_t nq = pr.q1 - pr.q0 + 1;
+    const int its = nq > 0 ? (int)((nq + (int64_t)NT * U - 1) / ((int64_t)NT * U)) : 0;
+    // piece j of this part is c16[q0 + j]; thread t takes j = it*NT*U + uu*NT + t
+    const gptr<u32x4> pc = G.c16 + pr.q0;
+    const gptr<u32x4> pu = G.u16 + pr.q0;
+    const int nqi = (int)nq;
+    const int vbase = (int)(pr.q0 * EPP - G.gbase);  // row id of element 0 of piece 0
+    const int lane = lane_id();
+
+    // Gumbel race state: wave-uniform bound, queue lengths and queued count; the
+    // lane's best (score, id, h)
+    const int wv = threadIdx.x >> 6;
+    float Bw = kNegInf;
+    int pn = 0, qn = 0, qtot = 0;
+    float bz = kNegInf, bh = kNegInf;
+    int be = 0x7FFFFFFF;
+    if (SAMPLE && race) {
+        if (threadIdx.x == 0) sh.bkey = order_key(kNegInf);
+        __syncthreads();
+    }
+    // score 64 queued ids, one per lane, and raise the bound
+    auto flush_ids = [&]() {
+        qn -= kWave;
+        const Cand c = sh.q[wv][qn + lane];
+        const float z = __builtin_fmaf(c.h, cp.inv_tau, gumbel_from_word(noise_word(cp.nk, (uint32_t)c.e)));
+        if (z > bz || (z == bz && c.e < be)) {
+            bz = z;
+            be = c.e;
+            bh = c.h;
+        }
+        const float nb = win_bound(wave_max(bz), cp.tau);
+        if (nb > Bw) {
+            Bw = nb;
+            if (lane == 0) atomicMax(&sh.bkey, order_key(nb));
+        }
+    };
+    // move the ids at or above the bound of 64 queued pieces to the id queue
+    auto expand = [&](float Bq) {
+        pn -= kWave;
+        const int pi = pn + lane;
+        const int v0 = sh.pv[wv][pi];
+#pragma unroll 1
+        for (int i = 0; i < EPP; ++i) {
+            const float h = sh.ph[wv][pi][i];
+            const bool pred = h >= Bq;
+            const uint64_t mk = ballot(pred);
+            if (mk) {
+                if (pred) sh.q[wv][qn + lanes_below(mk)] = Cand{h, v0 + i};
+                qn += popc(mk);
+                qtot += popc(mk);
+                if (qn >= kWave) {
+                    __builtin_amdgcn_wave_barrier();
+                    flush_ids();
+                    __builtin_amdgcn_wave_barrier();
+                    Bq = __builtin_fmaxf(Bq, Bw);
                 }
             }
-        };
-        auto process = [&](const Raw& R, int it) {
-            Piece<BF16> P[U];
-            float gm = kNegInf;
+        }
+    };
+
+    // ids [lo, hi) cover every element of pieces 1 .. nq-2; only the first and the
+    // last iteration can hold a partial or missing piece
+    auto group = [&](int it, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        u32x4 rc[U], ru[U];
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const int64_t q = cr.q0 + (int64_t)it * NT * U + (int64_t)uu * NT + threadIdx.x;
-                decode_piece<BF16>(R.c[uu], R.u[uu], s, use_u, P[uu]);
-                mask_piece<BF16>(P[uu], q, G, cr.lo, cr.hi);
-#pragma unroll
-                for (int i = 0; i < EPP; ++i) gm = __builtin_fmaxf(gm, P[uu].h[i]);
-            }
-            const int gid = it * NT + (int)threadIdx.x;
-            if (gm > m) {
-                acc *= __builtin_amdgcn_exp2f((m - gm) * kLog2e);
-                m = gm;
-                bg = gid;
-            }
-            // a thread that has seen only -inf keeps acc = 0 (exp2(-inf) = 0)
-            const float mL = (m > kNegInf) ? m * kLog2e : 0.0f;
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-                for (int i = 0; i < EPP; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(P[uu].h[i], kLog2e, -mL));
-            if (keep_groups) sh.gmax[j * G.gpc + gid] = gm;
-        };
-        Raw A, B;
-        if (its > 0) load(A, 0);
-        for (int it = 0; it < its; it += 2) {
-            if (it + 1 < its) load(B, it + 1);
-            process(A, it);
-            if (it + 1 < its) {
-                if (it + 2 < its) load(A, it + 2);
-                process(B, it + 1);
+        for (int uu = 0; uu < U; ++uu) {
+            const int j = it * NT * U + uu * NT + (int)threadIdx.x;
+            if (!EDGE) {
+                rc[uu] = pc[j];
+                if (use_u) ru[uu] = pu[j];
+            } else {
+                const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
+                rc[uu] = u32x4{ninf, ninf, ninf, ninf};
+                ru[uu] = rc[uu];
+                if (j < nqi) {
+                    rc[uu] = pc[j];
+                    if (use_u) ru[uu] = pu[j];
+                }
             }
         }
-        // undo the rounding of m * log2(e) for this thread's partial sum
-        if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
-        const float Mj = block_max(m, sh);
-        const float part = (m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - Mj) * kLog2e) : 0.0f;
-        const float Sj = block_sum(part, sh);
-        // smallest id attaining Mj: only threads whose max equals Mj look again
+        Piece<BF16> P[U];
+        float pm[U];
+        float gm = kNegInf;
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            const int j = it * NT * U + uu * NT + (int)threadIdx.x;
+            decode_piece<BF16>(rc[uu], ru[uu], s, use_u, P[uu]);
+            if (EDGE) {
+                const int v0 = vbase + j * EPP;
+                if (v0 < pr.lo || v0 + EPP > pr.hi) {
+#pragma unroll
+                    for (int i = 0; i < EPP; ++i)
+                        if (v0 + i < pr.lo || v0 + i >= pr.hi) P[uu].h[i] = kNegInf;
+                }
+            }
+            pm[uu] = P[uu].h[0];
+#pragma unroll
+            for (int i = 1; i < EPP; ++i) pm[uu] = __builtin_fmaxf(pm[uu], P[uu].h[i]);
+            gm = __builtin_fmaxf(gm, pm[uu]);
+        }
+        if (gm > m) {
+            // first piece, then first id, holding the new maximum (ids grow with
+            // the piece index inside a group and with the element inside a piece)
+            int id = 0x7FFFFFFF;
+#pragma unroll
+            for (int uu = U - 1; uu >= 0; --uu) {
+                if (pm[uu] == gm) {
+                    int e = EPP - 1;
+#pragma unroll
+                    for (int i = EPP - 1; i >= 0; --i)
+                        if (P[uu].h[i] == gm) e = i;
+                    id = vbase + (it * NT * U + uu * NT + (int)threadIdx.x) * EPP + e;
+                }
+            }
+            acc *= __builtin_amdgcn_exp2f((m - gm) * kLog2e);
+            m = gm;
+            mid = id;
+        }
+        // queue bound: no id below it can win (a bound of -inf means the wave has
+        // seen no finite h yet, and then nothing is queued)
+        float Bq = __builtin_inff();
+        if (SAMPLE && race) {
+            if (EDGE && it == 0) {
+                // after the first group, every lane scores its own maximum so far
+                // (one Philox batch per wave, as for a single id) and the block
+                // shares the bound of the best score; these ids stay in the race
+                // but are not counted, the counted queue still sees every id above
+                // the bound
+                if (m > kNegInf) {
+                    const float z = __builtin_fmaf(m, cp.inv_tau, gumbel_from_word(noise_word(cp.nk, (uint32_t)mid)));
+                    if (z > bz || (z == bz && mid < be)) {
+                        bz = z;
+                        be = mid;
+                        bh = m;
+                    }
+                }
+                const float nb = win_bound(wave_max(bz), cp.tau);
+                if (lane == 0) atomicMax(&sh.bkey, order_key(nb));
+                __syncthreads();
+                Bw = key_value(sh.bkey);
+            } else {
+                Bw = __builtin_fmaxf(Bw, key_value(__hip_atomic_load(&sh.bkey, __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_WORKGROUP)));
+            }
+            if (Bw > kNegInf) Bq = Bw;
+        }
+        // a thread that has seen only -inf keeps acc = 0 (exp2(-inf) = 0)
+        const float mL = (m > kNegInf) ? m * kLog2e : 0.0f;
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+#pragma unroll
+            for (int i = 0; i < EPP; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(P[uu].h[i], kLog2e, -mL));
+            if (SAMPLE && race) {
+                const bool pred = pm[uu] >= Bq;
+                const uint64_t mk = ballot(pred);
+                if (mk) {
+                    if (pred) {
+                        const int at = pn + lanes_below(mk);
+#pragma unroll
+                        for (int i = 0; i < EPP; ++i) sh.ph[wv][at][i] = P[uu].h[i];
+                        sh.pv[wv][at] = vbase + (it * NT * U + uu * NT + (int)threadIdx.x) * EPP;
+                    }
+                    pn += popc(mk);
+                    if (pn >= kWave) {
+                        __builtin_amdgcn_wave_barrier();
+                        expand(Bq);
+                        __builtin_amdgcn_wave_barrier();
+                        Bq = __builtin_fmaxf(Bq, Bw);
+                    }
+                }
+            }
+        }
+    };
+    for (int it = 0; it < its; ++it) {
+        if (it == 0 || it == its - 1)
+            group(it, std::true_type{});
+        else
+            group(it, std::false_type{});
+    }
+    // undo the rounding of m * log2(e) for this thread's partial sum
+    if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
+    PartOut o;
+    o.m = block_max(m, sh.r);
+    o.s = block_sum((m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - o.m) * kLog2e) : 0.0f, sh.r);
+    o.id = block_min_i((o.m > kNegInf && m == o.m) ? mid : 0x7FFFFFFF, sh.r);
+    o.bz = kNegInf;
+    o.bh = kNegInf;
+    o.be = 0x7FFFFFFF;
+    o.nq = 0;
+    if (SAMPLE && race) {
+        // drain the queues: the last pieces (fewer than 64), then the last ids
+        __builtin_amdgcn_wave_barrier();
+        if (pn > 0) {
+            const int take = pn;
+            pn = kWave;  // expand() takes entries [pn - 64, pn): pad to a full step
+            if (lane >= take) sh.pv[wv][lane] = 0;
+            if (lane >= take)
+#pragma unroll
+                for (int i = 0; i < EPP; ++i) sh.ph[wv][lane][i] = kNegInf;
+            __builtin_amdgcn_wave_barrier();
+            expand(Bw);
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (lane < qn) {
+            const Cand c = sh.q[wv][lane];
+            const float z = __builtin_fmaf(c.h, cp.inv_tau, gumbel_from_word(noise_word(cp.nk, (uint32_t)c.e)));
+            if (z > bz || (z == bz && c.e < be)) {
+                bz = z;
+                be = c.e;
+                bh = c.h;
+            }
+        }
+        block_argmax3(bz, be, bh, sh.r);
+        o.bz = bz;
+        o.be = be;
+        o.bh = bh;
+        o.nq = block_sum_uniform(qtot, sh.r);
+    }
+    return o;
+}
+
+// --------------------------------------------------------------- kernels
+
+template <bool BF16>
+__device__ __forceinline__ RowGeom row_geom(const void* cptr, const void* uptr, bool use_u, int64_t cell, int V,
+                                             int nch, int ppc) {
+    constexpr int ES = BF16 ? 2 : 4;
+    const uintptr_t cb = (uintptr_t)cptr;
+    RowGeom G;
+    G.c16 = as_global<u32x4>((const char*)cptr - (cb & 15));
+    G.u16 = use_u ? as_global<u32x4>((const char*)uptr - (cb & 15)) : G.c16;
+    G.gbase = (int64_t)((cb & 15) / ES) + cell * V;
+    G.V = V;
+    G.nch = nch;
+    G.L = (V + nch - 1) / nch;
+    G.ppc = ppc;
+    return G;
+}
+
+// Kernel 1 body: stream part `part` of the row and write its partial record.
+template <bool BF16, bool SAMPLE>
+__device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bool force_fallback,
+                          const RowWork& w, const CellParams& cp, int64_t slot, int part) {
+    __shared__ PartLDS<BF16, SAMPLE> sh;
+    const int j = part / w.ppc;
+    const int q = part - j * w.ppc;
+    const bool use_u = SAMPLE && cp.s != 0.0f;
+    const bool race = SAMPLE && cp.tau != 0.0f && !force_fallback;
+    const RowGeom G = row_geom<BF16>(cptr, uptr, use_u, cp.cell, V, nch, w.ppc);
+    const PartRange<BF16> pr(G, j, q);
+    const PartOut po = stream_part<BF16, SAMPLE>(G, pr, cp, use_u, race, sh);
+    if (threadIdx.x == 0) {
+        PartRec* rec = w.part + slot * w.nparts + part;
+        rec->m = po.m;
+        rec->s = po.s;
+        rec->id = po.id;
+        rec->nq = race ? po.nq : -1;
+        rec->bz = po.bz;
+        rec->be = po.be;
+        rec->bh = po.bh;
+    }
+}
+
+// Kernel 2 body: merge the row's partial records ([DRAFT]: larger max wins,
+// equal maxima keep the smaller id, sums add in probability space), then finish
+// the greedy or sampled decision.
+template <bool BF16, bool SAMPLE>
+__device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, int top_k, bool force_fallback,
+                           const RowWork& w, const CellParams& cp, int64_t slot, int* tokens, float* logprobs,
+                           float* lse_out, float* thresholds, float* triples, int64_t n_rows) {
+    __shared__ MergeLDS sh;
+    const bool use_u = SAMPLE && cp.s != 0.0f;
+    const bool sampled = SAMPLE && cp.tau != 0.0f;
+    const PartRec* recs = w.part + slot * w.nparts;
+    float M = kNegInf, S = 0.0f;
+    int id = 0x7FFFFFFF;
+    // race winners of the parts
+    float bz = kNegInf, bh = kNegInf;
+    int be = 0x7FFFFFFF;
+    int64_t queued = 0;
+    bool raced = sampled && !force_fallback;
+    for (int jj = 0; jj < nch; ++jj) {
+        float mj = kNegInf, sj = 0.0f;
         int idj = 0x7FFFFFFF;
-        if (Mj > kNegInf && m == Mj && bg >= 0) {
-            const int it = bg / NT;
-#pragma unroll
-            for (int uu = 0; uu < U && idj == 0x7FFFFFFF; ++uu) {
-                const int64_t q = cr.q0 + (int64_t)it * NT * U + (int64_t)uu * NT + threadIdx.x;
-                if (q > cr.q1) break;
-                Piece<BF16> P1;
-                load_piece<BF16>(G.c16, G.u16, q, s, use_u, P1);
-                mask_piece<BF16>(P1, q, G, cr.lo, cr.hi);
-                const int64_t v0 = q * EPP - G.gbase;
-#pragma unroll
-                for (int i = EPP - 1; i >= 0; --i)
-                    if (P1.h[i] == Mj) idj = (int)(v0 + i);
+        for (int qq = 0; qq < w.ppc; ++qq) {
+            const PartRec r = recs[jj * w.ppc + qq];
+            if (sampled) {
+                raced &= r.nq >= 0;
+                queued += r.nq;
+                if (r.bz > bz || (r.bz == bz && r.be < be)) {
+                    bz = r.bz;
+                    be = r.be;
+                    bh = r.bh;
+                }
             }
+            if (!(r.m > kNegInf)) continue;
+            const float mn = __builtin_fmaxf(mj, r.m);
+            sj = ((mj > kNegInf) ? sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e) : 0.0f) +
+                 r.s * __builtin_amdgcn_exp2f((r.m - mn) * kLog2e);
+            if (r.m > mj || (r.m == mj && r.id < idj)) idj = r.id;
+            mj = mn;
         }
-        idj = block_min_i(idj, sh);
         if (triples && threadIdx.x == 0) {
-            float* o = triples + ((int64_t)j * n_rows + row_index) * 3;
-            o[0] = Mj;
-            o[1] = (Mj > kNegInf) ? Mj + __builtin_logf(Sj) : kNegInf;
+            float* o = triples + ((int64_t)jj * n_rows + cp.cell) * 3;
+            o[0] = mj;
+            o[1] = (mj > kNegInf) ? mj + __builtin_logf(sj) : kNegInf;
             o[2] = __int_as_float(idj);
         }
-        // merge the chunk triple into the row ([DRAFT]: larger max wins, equal
-        // maxima keep the smaller id, sums add in probability space)
-        if (Mj > kNegInf) {
-            const float Mn = __builtin_fmaxf(Mrow, Mj);
-            Srow = ((Mrow > kNegInf) ? Srow * __builtin_amdgcn_exp2f((Mrow - Mn) * kLog2e) : 0.0f) +
-                   Sj * __builtin_amdgcn_exp2f((Mj - Mn) * kLog2e);
-            if (Mj > Mrow || (Mj == Mrow && idj < idrow)) idrow = idj;
-            Mrow = Mn;
-        }
+        if (!(mj > kNegInf)) continue;
+        const float mn = __builtin_fmaxf(M, mj);
+        S = ((M > kNegInf) ? S * __builtin_amdgcn_exp2f((M - mn) * kLog2e) : 0.0f) +
+            sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e);
+        if (mj > M || (mj == M && idj < id)) id = idj;
+        M = mn;
     }
-    RowResult r;
-    r.M = Mrow;
-    r.lse = Mrow + __builtin_logf(Srow);
-    r.id = idrow;
-    return r;
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(NT) void k_greedy_lse(GreedyArgs a) {
-    __shared__ Shared sh;
-    const int64_t row = blockIdx.x;
-    if (row >= a.n_rows) return;
-    constexpr int ES = BF16 ? 2 : 4;
-    const uintptr_t xb = (uintptr_t)a.x;
-    RowGeom G;
-    G.c16 = as_global<u32x4>((const char*)a.x - (xb & 15));
-    G.u16 = G.c16;
-    G.gbase = (int64_t)((xb & 15) / ES) + row * a.V;
-    G.V = a.V;
-    G.nch = a.vocab_chunks;
-    G.L = (a.V + a.vocab_chunks - 1) / a.vocab_chunks;
-    G.gpc = 0;
-    const RowResult r = stream_row<BF16>(G, 0.0f, false, false, a.triples, a.n_rows, row, sh);
-    if (threadIdx.x == 0) {
-        a.token[row] = r.id;
-        a.lse[row] = r.lse;
-        a.logprob[row] = r.M - r.lse;
-    }
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(NT) void k_sample_row(SampleArgs a, ReqTable rq) {
-    __shared__ Shared sh;
-    constexpr int EPP = Piece<BF16>::EPP;
-    constexpr int ES = BF16 ? 2 : 4;
-    const int64_t wid = blockIdx.x;
-    if (wid >= (int64_t)a.rows * rq.npos) return;
-    const int row = (int)(wid / rq.npos);
-    const int pl = (int)(wid - (int64_t)row * rq.npos);
-    const int r = find_request(rq, pl);
-    const int64_t cell = (int64_t)row * rq.P + rq.pos0 + pl;
-    const float s = rq.scale[r];
-    const float tau = rq.tau[r];
-    const bool use_u = s != 0.0f;
-
-    const uintptr_t cb = (uintptr_t)a.c;
-    RowGeom G;
-    G.c16 = as_global<u32x4>((const char*)a.c - (cb & 15));
-    G.u16 = use_u ? as_global<u32x4>((const char*)a.u - (cb & 15)) : G.c16;
-    G.gbase = (int64_t)((cb & 15) / ES) + cell * a.V;
-    G.V = a.V;
-    G.nch = a.vocab_chunks;
-    G.L = (a.V + a.vocab_chunks - 1) / a.vocab_chunks;
-    {
-        const int64_t qmax = (int64_t)G.L / EPP + 2;
-        G.gpc = (int)(((qmax + (int64_t)NT * U - 1) / ((int64_t)NT * U)) * NT);
-    }
-    const bool sampled = tau != 0.0f;
-    const bool groups_fit = (int64_t)G.gpc * G.nch <= GCAP;
-    const bool fast = sampled && groups_fit && !a.force_fallback;
-    if (fast)
-        for (int i = threadIdx.x; i < GCAP; i += NT) sh.gmax[i] = kNegInf;
-    __syncthreads();
-
-    const RowResult rr = stream_row<BF16>(G, s, use_u, fast, nullptr, 0, 0, sh);
+    const float lse = M + __builtin_logf(S);
     if (!sampled) {
         if (threadIdx.x == 0) {
-            a.tokens[cell] = rr.id;
-            a.logprobs[cell] = rr.M - rr.lse;
-            if (a.thresholds) a.thresholds[cell] = __builtin_nanf("");
+            tokens[cp.cell] = id;
+            if (lse_out) lse_out[cp.cell] = lse;
+            logprobs[cp.cell] = M - lse;
+            if (thresholds) thresholds[cp.cell] = __builtin_nanf("");
         }
         return;
     }
 
-    NoiseKey nk;
-    nk.k0 = a.k0;
-    nk.k1 = a.k1;
-    nk.t = (uint32_t)(pl - rq.offs[r]);
-    nk.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
-    nk.rid = rq.rid[r];
-    const float inv_tau = rq.inv_tau[r];
-    const int k = a.top_k;
-    // the argmax's own draw bounds every id that could still win
-    const float za = __builtin_fmaf(rr.M, inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)rr.id)));
-    const float b = (za - kGumbelBound) * tau;
-
+    // ---- Gumbel-max over the top-ratio set.  Every id that can win was queued by
+    // its part; when at most top_k ids were queued they all lie inside the set.
+    const int k = top_k;
+    const bool done = raced && queued <= (int64_t)k;
     float t = kNegInf;
-    bool have_t = false;
-    bool done = false;
-    float bz = kNegInf, bh = kNegInf;
-    int be = 0x7FFFFFFF;
-
-    if (fast) {
-        if (threadIdx.x == 0) {
-            sh.cnt_g = 0;
-            sh.cnt_c = 0;
-        }
-        __syncthreads();
-        const int ng = G.gpc * G.nch;
-        for (int g0 = 0; g0 < ng; g0 += NT) {
-            const int g = g0 + (int)threadIdx.x;
-            const bool pred = g < ng && sh.gmax[g] >= b;
-            const int slot = wave_append(pred, &sh.cnt_g);
-            if (slot >= 0 && slot < GLCAP) sh.glist[slot] = g;
-        }
-        __syncthreads();
-        const int nglist = sh.cnt_g;
-        if (nglist <= GLCAP) {
-            for (int i0 = 0; i0 < nglist; i0 += NT) {
-                const int i = i0 + (int)threadIdx.x;
-                Piece<BF16> P[U];
-                int64_t qs[U];
-                bool any = false;
-                if (i < nglist) {
-                    const int g = sh.glist[i];
-                    const int j = g / G.gpc;
-                    const int rem = g - j * G.gpc;
-                    const int it = rem / NT;
-                    const int tt = rem - it * NT;
-                    const ChunkRange<BF16> cr(G, j);
-#pragma unroll
-                    for (int uu = 0; uu < U; ++uu) {
-                        qs[uu] = cr.q0 + (int64_t)it * NT * U + (int64_t)uu * NT + tt;
-                        if (qs[uu] <= cr.q1) {
-                            load_piece<BF16>(G.c16, G.u16, qs[uu], s, use_u, P[uu]);
-                            mask_piece<BF16>(P[uu], qs[uu], G, cr.lo, cr.hi);
-                            any = true;
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < EPP; ++e) P[uu].h[e] = kNegInf;
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int uu = 0; uu < U; ++uu) {
-                        qs[uu] = 0;
-#pragma unroll
-                        for (int e = 0; e < EPP; ++e) P[uu].h[e] = kNegInf;
-                    }
-                }
-                (void)any;
-#pragma unroll
-                for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-                    for (int e = 0; e < EPP; ++e) {
-                        const bool pred = P[uu].h[e] >= b;
-                        const int slot = wave_append(pred, &sh.cnt_c);
-                        if (slot >= 0 && slot < CCAP) {
-                            sh.ch[slot] = P[uu].h[e];
-                            sh.ce[slot] = (int)(qs[uu] * EPP + e - G.gbase);
-                        }
-                    }
-            }
-            __syncthreads();
-            const int nb = sh.cnt_c;
-            if (nb <= CCAP) {
-                // every id with h >= b is in the list
-                float cthr = b;
-                if (nb >= k) {
-                    t = radix_select_list(nb, k, sh);
-                    have_t = true;
-                    cthr = __builtin_fmaxf(t, b);
-                }
-                for (int i = threadIdx.x; i < nb; i += NT) {
-                    const float hv = sh.ch[i];
-                    const int ev = sh.ce[i];
-                    if (hv >= cthr) {
-                        const float z = __builtin_fmaf(hv, inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)ev)));
-                        if (z > bz || (z == bz && ev < be)) {
-                            bz = z;
-                            be = ev;
-                            bh = hv;
-                        }
-                    }
-                }
-                done = true;
-            }
-        }
-    }
-    // uniform: `done` depends only on LDS counters read after a barrier
-    if (!done || (a.thresholds && !have_t)) {
-        t = radix_select_row<BF16>(G, s, use_u, k, sh);
-        have_t = true;
-    }
+    const RowGeom G = row_geom<BF16>(cptr, uptr, use_u, cp.cell, V, nch, w.ppc);
+    if (!done || thresholds) t = radix_select_row<BF16>(G, cp.s, use_u, k, sh);
     if (!done) {
-        const float cthr = __builtin_fmaxf(t, b);
+        // exact pass over the kept ids that can beat the argmax
+        const float cthr = __builtin_fmaxf(t, max_bound(M, cp.inv_tau, cp.tau));
         bz = kNegInf;
         be = 0x7FFFFFFF;
-        for_each_id<BF16>(G, s, use_u, [&](int v, float hv) {
+        bh = kNegInf;
+        for_each_id<BF16>(G, cp.s, use_u, [&](int v, float hv) {
             if (!(hv >= cthr)) return;
-            const float z = __builtin_fmaf(hv, inv_tau, gumbel_from_word(noise_word(nk, (uint32_t)v)));
+            const float z = __builtin_fmaf(hv, cp.inv_tau, gumbel_from_word(noise_word(cp.nk, (uint32_t)v)));
             if (z > bz || (z == bz && v < be)) {
                 bz = z;
                 be = v;
                 bh = hv;
             }
         });
+        block_argmax3(bz, be, bh, sh.r);
     }
-    block_argmax3(bz, be, bh, sh);
     if (threadIdx.x == 0) {
-        a.tokens[cell] = be;
-        a.logprobs[cell] = bh - rr.lse;
-        if (a.thresholds) a.thresholds[cell] = t + 0.0f;
+        tokens[cp.cell] = be;
+        logprobs[cp.cell] = bh - lse;
+        if (thresholds) thresholds[cp.cell] = t + 0.0f;
     }
+}
+
+__device__ __forceinline__ CellParams sample_cell(const SampleArgs& a, const ReqTable& rq, int64_t slot) {
+    const int64_t lin = a.w.cell_base + slot;  // launch-relative cell
+    const int row = (int)(lin / rq.npos);
+    const int pl = (int)(lin - (int64_t)row * rq.npos);
+    const int r = find_request(rq, pl);
+    CellParams cp;
+    cp.cell = (int64_t)row * rq.P + rq.pos0 + pl;
+    cp.s = rq.scale[r];
+    cp.tau = rq.tau[r];
+    cp.inv_tau = rq.inv_tau[r];
+    cp.nk.k0 = a.k0;
+    cp.nk.k1 = a.k1;
+    cp.nk.t = (uint32_t)(pl - rq.offs[r]);
+    cp.nk.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
+    cp.nk.rid = rq.rid[r];
+    return cp;
+}
+
+__device__ __forceinline__ CellParams greedy_cell(const GreedyArgs& a, int64_t slot) {
+    CellParams cp;
+    cp.cell = a.w.cell_base + slot;
+    cp.s = 0.0f;
+    cp.tau = 0.0f;
+    cp.inv_tau = 0.0f;
+    cp.nk = NoiseKey{0, 0, 0, 0, 0};
+    return cp;
+}
+
+// Block b is part (b % nparts) of row slot (b / nparts), so neighbouring
+// workgroups stream neighbouring memory.  At most 64 VGPRs: four workgroups per CU.
+template <bool BF16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_sample_parts(SampleArgs a, ReqTable rq) {
+    const int64_t slot = blockIdx.x / a.w.nparts;
+    const int part = (int)(blockIdx.x - slot * a.w.nparts);
+    part_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot), slot,
+                          part);
+}
+template <bool BF16>
+__global__ __launch_bounds__(NT) void k_sample_merge(SampleArgs a, ReqTable rq) {
+    const int64_t slot = blockIdx.x;
+    merge_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
+                           sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr, a.thresholds, nullptr, 0);
+}
+template <bool BF16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_greedy_parts(GreedyArgs a) {
+    const int64_t slot = blockIdx.x / a.w.nparts;
+    const int part = (int)(blockIdx.x - slot * a.w.nparts);
+    part_body<BF16, false>(a.x, nullptr, a.V, a.vocab_chunks, false, a.w, greedy_cell(a, slot), slot, part);
+}
+template <bool BF16>
+__global__ __launch_bounds__(NT) void k_greedy_merge(GreedyArgs a) {
+    const int64_t slot = blockIdx.x;
+    merge_body<BF16, false>(a.x, nullptr, a.V, a.vocab_chunks, 1, false, a.w, greedy_cell(a, slot), slot, a.token,
+                            a.logprob, a.lse, nullptr, a.triples, a.n_rows);
 }
 
 }  // namespace
 
+int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells) {
+    const int epp = bf16 ? 8 : 4;
+    const int64_t L = ((int64_t)V + chunks - 1) / chunks;
+    const int64_t pieces = L / epp + 2;
+    // enough workgroups to cover the GPU several times over, parts of >= 1024 pieces
+    const int64_t target = 1024;
+    int64_t p = (target + cells * chunks - 1) / (cells * chunks);
+    const int64_t p_cap = pieces / 1024 > 1 ? pieces / 1024 : 1;
+    if (p > p_cap) p = p_cap;
+    if (p * chunks > kWorkParts) p = kWorkParts / chunks > 0 ? kWorkParts / chunks : 1;
+    return (int)(p < 1 ? 1 : p);
+}
+
 hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
-    const int64_t cells = (int64_t)a.rows * rq.npos;
-    if (bf16)
-        hipLaunchKernelGGL(k_sample_row<true>, dim3((unsigned)cells), dim3(NT), 0, st, a, rq);
-    else
-        hipLaunchKernelGGL(k_sample_row<false>, dim3((unsigned)cells), dim3(NT), 0, st, a, rq);
+    const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
+    if (bf16) {
+        hipLaunchKernelGGL(k_sample_parts<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
+        hipLaunchKernelGGL(k_sample_merge<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, rq);
+    } else {
+        hipLaunchKernelGGL(k_sample_parts<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
+        hipLaunchKernelGGL(k_sample_merge<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, rq);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st) {
-    if (a.n_rows == 0) return hipSuccess;
-    if (bf16)
-        hipLaunchKernelGGL(k_greedy_lse<true>, dim3((unsigned)a.n_rows), dim3(NT), 0, st, a);
-    else
-        hipLaunchKernelGGL(k_greedy_lse<false>, dim3((unsigned)a.n_rows), dim3(NT), 0, st, a);
+    const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
+    if (parts == 0) return hipSuccess;
+    if (bf16) {
+        hipLaunchKernelGGL(k_greedy_parts<true>, dim3((unsigned)parts), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL(k_greedy_merge<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(k_greedy_parts<false>, dim3((unsigned)parts), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL(k_greedy_merge<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -337,7 +337,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     const float inv_tau = rq.inv_tau[r];
     // No id with h below `prune` can beat the argmax: its h/tau plus the largest
     // possible noise stays below M/tau plus the smallest possible noise.
-    const float prune = M - tau * (kGumbelBound - kGumbelFloor);
+    const float prune = max_bound(M, inv_tau, tau);
     const bool want_t = a.thresholds != nullptr;
 
     float t = kNegInf;
