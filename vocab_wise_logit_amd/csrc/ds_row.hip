@@ -39,11 +39,21 @@ constexpr int NT = kRowThreads;
 constexpr int NWAVES = NT / kWave;
 constexpr int U = kRowU;
 
+// One wave's share of a part: (max, exp-sum, argmax) and its race winner.
+struct WaveRec {
+    float m, s;
+    int id;
+    float bz, bh;
+    int be, nq;
+    int pad;
+};
+
 // Cross-wave reduction slots.
 struct Red {
     float f[NWAVES];
     float f2[NWAVES];
     int i[NWAVES];
+    WaveRec w[NWAVES];
     uint32_t bcast_u;
 };
 
@@ -62,59 +72,13 @@ struct PartLDS {
     Red r;
 };
 
-// The merge's radix-select histogram.
+// The merge's staged part records and radix-select histogram.
 struct MergeLDS {
+    PartRec rec[NT];
     uint32_t hist[256];
     Red r;
 };
 
-__device__ __forceinline__ float block_max(float x, Red& r) {
-    x = wave_max(x);
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane_id() == 0) r.f[w] = x;
-    __syncthreads();
-    float y = r.f[0];
-#pragma unroll
-    for (int i = 1; i < NWAVES; ++i) y = __builtin_fmaxf(y, r.f[i]);
-    return y;
-}
-
-__device__ __forceinline__ float block_sum(float x, Red& r) {
-    x = wave_sum(x);
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane_id() == 0) r.f[w] = x;
-    __syncthreads();
-    float y = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NWAVES; ++i) y += r.f[i];
-    return y;
-}
-
-__device__ __forceinline__ int block_min_i(int x, Red& r) {
-    x = wave_min_i(x);
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane_id() == 0) r.i[w] = x;
-    __syncthreads();
-    int y = r.i[0];
-#pragma unroll
-    for (int i = 1; i < NWAVES; ++i) y = min(y, r.i[i]);
-    return y;
-}
-
-// Sum of a wave-uniform count over the block.
-__device__ __forceinline__ int block_sum_uniform(int x, Red& r) {
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane_id() == 0) r.i[w] = x;
-    __syncthreads();
-    int y = 0;
-#pragma unroll
-    for (int i = 0; i < NWAVES; ++i) y += r.i[i];
-    return y;
-}
 
 // Block argmax of (z, id, h): larger z, then smaller id.
 __device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Red& r) {
@@ -442,7 +406,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
             if (EDGE && it == 0) {
                 // after the first group, every lane scores its own maximum so far
                 // (one Philox batch per wave, as for a single id) and the block
-                // shares the bound of the best score; these ids stay in the race
+                // adopts the bound of the best score; these ids stay in the race
                 // but are not counted, the counted queue still sees every id above
                 // the bound
                 if (m > kNegInf) {
@@ -498,14 +462,6 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
     }
     // undo the rounding of m * log2(e) for this thread's partial sum
     if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
-    PartOut o;
-    o.m = block_max(m, sh.r);
-    o.s = block_sum((m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - o.m) * kLog2e) : 0.0f, sh.r);
-    o.id = block_min_i((o.m > kNegInf && m == o.m) ? mid : 0x7FFFFFFF, sh.r);
-    o.bz = kNegInf;
-    o.bh = kNegInf;
-    o.be = 0x7FFFFFFF;
-    o.nq = 0;
     if (SAMPLE && race) {
         // drain the queues: the last pieces (fewer than 64), then the last ids
         __builtin_amdgcn_wave_barrier();
@@ -529,11 +485,44 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
                 bh = c.h;
             }
         }
-        block_argmax3(bz, be, bh, sh.r);
-        o.bz = bz;
-        o.be = be;
-        o.bh = bh;
-        o.nq = block_sum_uniform(qtot, sh.r);
+    }
+    // wave shares, then one exchange through LDS; thread 0 combines them
+    const float wm = wave_max(m);
+    const float ws = wave_sum((m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - wm) * kLog2e) : 0.0f);
+    const int wid = wave_min_i((wm > kNegInf && m == wm) ? mid : 0x7FFFFFFF);
+    if (SAMPLE && race) {
+        const int wl = wave_argmax(bz, be);
+        bh = readlane_f(bh, wl);
+    }
+    if (lane == 0) sh.r.w[wv] = WaveRec{wm, ws, wid, bz, bh, be, qtot, 0};
+    __syncthreads();
+    PartOut o;
+    o.m = kNegInf;
+    o.s = 0.0f;
+    o.id = 0x7FFFFFFF;
+    o.bz = kNegInf;
+    o.bh = kNegInf;
+    o.be = 0x7FFFFFFF;
+    o.nq = 0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) o.m = __builtin_fmaxf(o.m, sh.r.w[i].m);
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) {
+            const WaveRec r = sh.r.w[i];
+            if (r.m > kNegInf) {
+                o.s += r.s * __builtin_amdgcn_exp2f((r.m - o.m) * kLog2e);
+                if (r.m == o.m) o.id = min(o.id, r.id);
+            }
+            if (SAMPLE && race) {
+                if (r.bz > o.bz || (r.bz == o.bz && r.be < o.be)) {
+                    o.bz = r.bz;
+                    o.be = r.be;
+                    o.bh = r.bh;
+                }
+                o.nq += r.nq;
+            }
+        }
     }
     return o;
 }
@@ -598,11 +587,17 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
     int be = 0x7FFFFFFF;
     int64_t queued = 0;
     bool raced = sampled && !force_fallback;
-    for (int jj = 0; jj < nch; ++jj) {
-        float mj = kNegInf, sj = 0.0f;
-        int idj = 0x7FFFFFFF;
-        for (int qq = 0; qq < w.ppc; ++qq) {
-            const PartRec r = recs[jj * w.ppc + qq];
+    // records in chunk-major order, staged through LDS NT at a time
+    float mj = kNegInf, sj = 0.0f;
+    int idj = 0x7FFFFFFF;
+    for (int t0 = 0; t0 < w.nparts; t0 += NT) {
+        const int n = min(NT, w.nparts - t0);
+        __syncthreads();
+        if ((int)threadIdx.x < n) sh.rec[threadIdx.x] = recs[t0 + threadIdx.x];
+        __syncthreads();
+        for (int i = 0; i < n; ++i) {
+            const int p = t0 + i;
+            const PartRec r = sh.rec[i];
             if (sampled) {
                 raced &= r.nq >= 0;
                 queued += r.nq;
@@ -612,25 +607,33 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
                     bh = r.bh;
                 }
             }
-            if (!(r.m > kNegInf)) continue;
-            const float mn = __builtin_fmaxf(mj, r.m);
-            sj = ((mj > kNegInf) ? sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e) : 0.0f) +
-                 r.s * __builtin_amdgcn_exp2f((r.m - mn) * kLog2e);
-            if (r.m > mj || (r.m == mj && r.id < idj)) idj = r.id;
-            mj = mn;
+            if (r.m > kNegInf) {
+                const float mn = __builtin_fmaxf(mj, r.m);
+                sj = ((mj > kNegInf) ? sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e) : 0.0f) +
+                     r.s * __builtin_amdgcn_exp2f((r.m - mn) * kLog2e);
+                if (r.m > mj || (r.m == mj && r.id < idj)) idj = r.id;
+                mj = mn;
+            }
+            if ((p + 1) % w.ppc != 0) continue;
+            // chunk jj complete: its triple, then fold it into the row
+            const int jj = p / w.ppc;
+            if (triples && threadIdx.x == 0) {
+                float* o = triples + ((int64_t)jj * n_rows + cp.cell) * 3;
+                o[0] = mj;
+                o[1] = (mj > kNegInf) ? mj + __builtin_logf(sj) : kNegInf;
+                o[2] = __int_as_float(idj);
+            }
+            if (mj > kNegInf) {
+                const float mn = __builtin_fmaxf(M, mj);
+                S = ((M > kNegInf) ? S * __builtin_amdgcn_exp2f((M - mn) * kLog2e) : 0.0f) +
+                    sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e);
+                if (mj > M || (mj == M && idj < id)) id = idj;
+                M = mn;
+            }
+            mj = kNegInf;
+            sj = 0.0f;
+            idj = 0x7FFFFFFF;
         }
-        if (triples && threadIdx.x == 0) {
-            float* o = triples + ((int64_t)jj * n_rows + cp.cell) * 3;
-            o[0] = mj;
-            o[1] = (mj > kNegInf) ? mj + __builtin_logf(sj) : kNegInf;
-            o[2] = __int_as_float(idj);
-        }
-        if (!(mj > kNegInf)) continue;
-        const float mn = __builtin_fmaxf(M, mj);
-        S = ((M > kNegInf) ? S * __builtin_amdgcn_exp2f((M - mn) * kLog2e) : 0.0f) +
-            sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e);
-        if (mj > M || (mj == M && idj < id)) id = idj;
-        M = mn;
     }
     const float lse = M + __builtin_logf(S);
     if (!sampled) {
@@ -703,7 +706,9 @@ __device__ __forceinline__ CellParams greedy_cell(const GreedyArgs& a, int64_t s
 }
 
 // Block b is part (b % nparts) of row slot (b / nparts), so neighbouring
-// workgroups stream neighbouring memory.  At most 64 VGPRs: four workgroups per CU.
+// workgroups stream neighbouring memory.  The greedy parts kernel keeps to 64
+// VGPRs (four workgroups per CU); the sampled one may take 80 (three), which the
+// race's noise code needs without spilling.
 template <bool BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_sample_parts(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x / a.w.nparts;
@@ -747,6 +752,7 @@ int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells) {
 
 hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
     const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
+    if (parts == 0) return hipSuccess;
     if (bf16) {
         hipLaunchKernelGGL(k_sample_parts<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
         hipLaunchKernelGGL(k_sample_merge<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, rq);
