@@ -87,9 +87,10 @@ def make_workload(name: str):
 
 class Runner:
     """Device copies of one workload and a sampler handle; `step(i)` issues one
-    call on rotating buffers."""
+    call on rotating buffers (asking for the top-ratio thresholds too when
+    `threshold` is set)."""
 
-    def __init__(self, w, kind: str):
+    def __init__(self, w, kind: str, threshold: bool = False):
         import torch
 
         import vocab_wise_logit_amd as ds
@@ -119,7 +120,8 @@ class Runner:
                                   vocab_chunks=w.vocab_chunks)
             shape = (w.rows, w.positions)
             self.out = (torch.empty(shape, dtype=torch.int32, device="cuda"),
-                        torch.empty(shape, dtype=torch.float32, device="cuda"), None)
+                        torch.empty(shape, dtype=torch.float32, device="cuda"),
+                        torch.empty(shape, dtype=torch.float32, device="cuda") if threshold else None)
             self.cells = w.cells
 
     def step(self, i: int) -> None:
@@ -129,7 +131,8 @@ class Runner:
             self.smp.greedy_lse(self.x[s], out=self.out)
         else:
             self.smp.sample(w.request_ids, self.c[s], self.u[s] if self.u else None, w.seq_lens,
-                            w.iterations, w.guidance, w.temperature, seed=w.seed, out=self.out)
+                            w.iterations, w.guidance, w.temperature, seed=w.seed,
+                            threshold=self.out[2] is not None, out=self.out)
 
     def close(self):
         self.smp.close()
@@ -176,23 +179,34 @@ def describe(w, kind: str) -> dict:
             "vocab_chunks": w.vocab_chunks}
 
 
-def bench_one(name: str, steps: int, warmup: int) -> dict:
+def launches_per_step(w, kind: str) -> int:
+    """Kernel launches of one call: one for the wave-per-cell kernel, a parts and a
+    merge kernel for the streaming path (every workload here fits one batch)."""
+    return 1 if kernel_name(w, kind).startswith("k_sample_small") else 2
+
+
+def bench_one(name: str, steps: int, warmup: int, threshold: bool = False) -> dict:
     import torch
 
     kind = "draft" if name == "draft" else "sample"
     w = make_workload(name)
-    r = Runner(w, kind)
+    r = Runner(w, kind, threshold)
     ms_step, ms_kernel, med, p10, p90 = time_runner(r, steps, warmup)
     r.close()
     del r
     torch.cuda.empty_cache()
     alg = w.algorithmic_bytes()
     cells = w.n_rows if kind == "draft" else w.cells
-    # one step is exactly one kernel launch (every workload here has <= 64
-    # requests), so the back-to-back time per step is the kernel's average
-    # duration on its stream
+    # every workload here has <= 64 requests, so one step is one launch of the
+    # wave-per-cell kernel (its back-to-back time per step is that kernel's
+    # average duration on its stream) or one parts + merge pair
     achieved = alg / (ms_step * 1e-3) / 1e9
-    return {"config": describe(w, kind), "kernel": kernel_name(w, kind), "positions_per_s": cells / (ms_step * 1e-3),
+    cfg = describe(w, kind)
+    if threshold:
+        cfg["workload"] += "+threshold"
+        cfg["threshold_out"] = True
+    return {"config": cfg, "kernel": kernel_name(w, kind), "launches_per_step": launches_per_step(w, kind),
+            "positions_per_s": cells / (ms_step * 1e-3),
             "ms_per_step": ms_step, "kernel_ms_mean": ms_step, "bracketed_ms_mean": ms_kernel,
             "bracketed_ms_median": med, "bracketed_ms_p10": p10, "bracketed_ms_p90": p90, "algorithmic_bytes": alg,
             "achieved_GBs": achieved, "frac_of_peak": achieved / HBM_PEAK_GBS, "workload_obj": w}
@@ -263,11 +277,16 @@ def main() -> int:
                 "kernel_ms_mean": head["kernel_ms_mean"], "bracketed_ms_mean": head["bracketed_ms_mean"]}
     per_config = {}
     if not args.no_suite:
-        for name in ("tiny", "omnivoice", "mixed", "draft", "stress"):
-            if name == args.workload:
+        # every workload, then the two sampled shapes again with the threshold
+        # output requested (it needs the exact k-th largest h of every row)
+        runs = [(n, False) for n in ("tiny", "omnivoice", "mixed", "draft", "stress")]
+        runs += [("omnivoice", True), ("stress", True)]
+        for name, thr in runs:
+            if name == args.workload and not thr:
                 res = head
             else:
-                res = bench_one(name, max(10, args.steps // 2), max(3, args.warmup // 2))
+                st = max(10, args.steps // 2) if name != "stress" or not thr else 5
+                res = bench_one(name, st, max(3, args.warmup // 2) if st > 5 else 2, threshold=thr)
                 res.pop("workload_obj", None)
             per_config[res["config"]["workload"]] = {
                 k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}

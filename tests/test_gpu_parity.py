@@ -118,6 +118,47 @@ def test_row_kernel_mid_vocab(dtype, V):
     check_sample(w, run_sample(w, force_fallback=True), ref)
 
 
+@pytest.mark.parametrize("dtype,V,chunks", [("bf16", 3000, 1), ("bf16", 4103, 3), ("f32", 5000, 2),
+                                             ("bf16", 60000, 4)])
+def test_row_kernel_race_without_threshold(dtype, V, chunks):
+    # the production path: the parts' Gumbel race decides the token and the
+    # threshold is never located
+    w = synth.diffusion(f"race_{dtype}_{V}", seed=V + 11, vocab=V, rows=2, seq_lens=[4, 3], dtype=dtype,
+                        sigma=4.0, guidance=[1.5, 0.0], temperature=[1.0, 0.7], vocab_chunks=chunks)
+    check_sample(w, run_sample(w, threshold=False), oracle.sample_workload(w))
+
+
+def test_row_kernel_flat_rows_take_the_exact_path():
+    # nearly flat h at a high temperature: every id can still win, far more than
+    # top_k of them, so the merge must locate the threshold itself
+    w = synth.diffusion("flat", seed=21, vocab=8000, rows=1, seq_lens=[6], sigma=0.3, guidance=0.5,
+                        temperature=1.5)
+    ref = oracle.sample_workload(w)
+    for thr in (False, True):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+
+
+def test_row_kernel_small_temperature_and_masked_ids():
+    # |h / tau| near 1e5 (the pruning bounds' relative margin) and masked ids
+    # with guidance on, where c - u is (-inf) - (-inf)
+    w = synth.diffusion("row_tau", seed=23, vocab=20000, rows=2, seq_lens=[3, 3], sigma=4.0, guidance=2.0,
+                        temperature=[1e-3, 0.05], masked_ids=[0, 5, 19999], vocab_chunks=2)
+    ref = oracle.sample_workload(w)
+    for thr in (False, True):
+        got = run_sample(w, threshold=thr)
+        check_sample(w, got, ref)
+        assert not np.isin(got[0], [0, 5, 19999]).any()
+
+
+def test_row_kernel_many_parts_per_row():
+    # 4 positions x 4 chunks: each chunk is cut into several parts, each running
+    # its own race
+    w = synth.stress(positions=4)
+    ref = oracle.sample_workload(w)
+    for thr in (False, True):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+
+
 def test_masked_ids_stay_masked():
     V = 1025
     w = synth.diffusion("masked", seed=5, vocab=V, rows=4, seq_lens=[30, 20], sigma=3.0,
