@@ -36,11 +36,23 @@ METRIC = "sampled positions/sec + achieved HBM GB/s (% of MI355X peak) per confi
 ROTATE_BYTES = 1 << 30
 
 
-def kernel_source_digest() -> str:
+# Sources each kernel is built from: a stored counter reading is valid only while
+# these files are unchanged.
+KERNEL_SOURCES = {
+    "small": ("ds_small.hip", "ds_device.h", "ds_kernels.h"),
+    "row": ("ds_row.hip", "ds_device.h", "ds_kernels.h"),
+}
+
+
+def kernel_family(workload: str) -> str:
+    return "small" if workload in ("tiny", "omnivoice", "mixed") else "row"
+
+
+def kernel_source_digest(family: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "vocab_wise_logit_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "vocab_wise_logit_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -48,13 +60,13 @@ def kernel_source_digest() -> str:
 def stored_traffic(workload: str):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
     WRITE_SIZE, scaled by a copy-kernel calibration), if they were taken on the
-    current kernel sources; otherwise None."""
+    current sources of the workload's kernels; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_digest") != kernel_source_digest():
+    if t.get("kernel_source_digest") != kernel_source_digest(kernel_family(workload)):
         return None
     return t.get("bytes_per_launch")
 
@@ -288,8 +300,10 @@ def main() -> int:
                 st = max(10, args.steps // 2) if name != "stress" or not thr else 5
                 res = bench_one(name, st, max(3, args.warmup // 2) if st > 5 else 2, threshold=thr)
                 res.pop("workload_obj", None)
-            per_config[res["config"]["workload"]] = {
-                k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}
+            entry = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}
+            if not thr:
+                entry["traffic"] = stored_traffic(name)
+            per_config[res["config"]["workload"]] = entry
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     line = {
         "metric": METRIC,
