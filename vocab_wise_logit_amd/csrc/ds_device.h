@@ -41,6 +41,10 @@ __device__ __forceinline__ gptr<T> as_global(const void* p) {
     return (gptr<T>)p;
 }
 
+// Word 3 of a gfx9 buffer resource for raw 32-bit loads (no swizzle, no stride):
+// the hardware returns 0 for any dword outside [0, num_records).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // ------------------------------------------------------------ element decode
 
 // bf16 is the upper half of a binary32, so widening is a shift (exact).

@@ -186,22 +186,15 @@ __device__ __forceinline__ void gumbel_list(Entry* list, int n, float cthr, bool
     }
 }
 
-// Load one row's dwords: slots below `nfull` are in range for every lane, the
-// rest only where j * 64 + lane < ndw (missing dwords read as `fill`).
+// Load one row's dwords through a buffer resource that covers exactly the row:
+// the hardware range check returns 0 for dwords past it, so no load is branched
+// or masked.  Slot j of lane l is dword 64 j + l.
 template <int NS>
-__device__ __forceinline__ void load_slots(gptr<uint32_t> base, int lane, int ndw, uint32_t fill,
-                                           uint32_t (&w)[NS]) {
-    const int nfull = ndw >> 6;
-    const gptr<uint32_t> p = base + lane;
+__device__ __forceinline__ void load_slots(const void* base, int lane, int ndw, uint32_t (&w)[NS]) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, ndw * 4, kBufferRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        if (j < nfull) {
-            w[j] = p[j * kWave];
-        } else {
-            w[j] = fill;
-            if (j * kWave + lane < ndw) w[j] = p[j * kWave];
-        }
-    }
+    for (int j = 0; j < NS; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (lane + j * kWave) * 4, 0, 0);
 }
 
 template <bool BF16, int NS>
@@ -210,13 +203,13 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     constexpr int NE = R_t::NE;
     __shared__ Entry s_list[kWavesPerBlock][kListCap];
 
-    // every per-cell quantity below is wave-uniform (scalar registers)
+    // every per-cell quantity below is wave-uniform (scalar registers); the grid
+    // is (positions / 4, rows) with rows beyond 65535 folded into z
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = lane_id();
-    const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + wv;
-    if (wid >= (int64_t)a.rows * rq.npos) return;  // whole wave leaves together
-    const int row = (int)(wid / rq.npos);
-    const int pl = (int)(wid - (int64_t)row * rq.npos);
+    const int pl = (int)blockIdx.x * kWavesPerBlock + wv;
+    const int row = (int)(blockIdx.z * gridDim.y + blockIdx.y);
+    if (pl >= rq.npos || row >= a.rows) return;  // whole wave leaves together
     const int r = find_request(rq, pl);
     const int64_t cell = (int64_t)row * rq.P + rq.pos0 + pl;
     const int V = a.V;
@@ -229,18 +222,20 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     if (BF16) {
         const uintptr_t cb = (uintptr_t)a.c;
         // dword-aligned view of c (u has the same address modulo 16)
-        const gptr<uint32_t> c32 = as_global<uint32_t>((const char*)a.c - (cb & 3));
         const int64_t g = (int64_t)((cb & 3) >> 1) + cell * V;
         const int par = (int)(g & 1);
-        const int64_t d0 = g >> 1;
+        const int64_t off = (g >> 1) * 4 - (int64_t)(cb & 3);  // byte offset of the row's first dword
         const int ndw = (par + V + 1) >> 1;
         R.ebase = 2 * lane - par;
         uint32_t cw[NS];
-        load_slots<NS>(c32 + d0, lane, ndw, 0xFF80FF80u, cw);
+        load_slots<NS>((const char*)a.c + off, lane, ndw, cw);
+        // dwords past the row read as 0; c becomes -inf there, which makes h -inf
+        // whatever u reads (guided maps the NaN of -inf - -inf back to -inf)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) cw[j] = (lane + j * kWave < ndw) ? cw[j] : 0xFF80FF80u;
         if (s != 0.0f) {
-            const gptr<uint32_t> u32 = as_global<uint32_t>((const char*)a.u - (cb & 3));
             uint32_t uw[NS];
-            load_slots<NS>(u32 + d0, lane, ndw, 0xFF80FF80u, uw);
+            load_slots<NS>((const char*)a.u + off, lane, ndw, uw);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 R.h[2 * j] = guided(bf16_lo(cw[j]), bf16_lo(uw[j]), s);
@@ -263,13 +258,13 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
         }
     } else {
         R.ebase = lane;
-        const gptr<uint32_t> c = as_global<uint32_t>(a.c) + cell * V;
         uint32_t cw[NS];
-        load_slots<NS>(c, lane, V, 0xFF800000u, cw);
+        load_slots<NS>((const float*)a.c + cell * V, lane, V, cw);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) cw[j] = (lane + j * kWave < V) ? cw[j] : 0xFF800000u;
         if (s != 0.0f) {
-            const gptr<uint32_t> u = as_global<uint32_t>(a.u) + cell * V;
             uint32_t uw[NS];
-            load_slots<NS>(u, lane, V, 0xFF800000u, uw);
+            load_slots<NS>((const float*)a.u + cell * V, lane, V, uw);
 #pragma unroll
             for (int j = 0; j < NS; ++j) R.h[j] = guided(__uint_as_float(cw[j]), __uint_as_float(uw[j]), s);
         } else {
@@ -476,15 +471,16 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small_wide(Sa
 
 template <bool BF16, int NS>
 hipError_t launch_ns(const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
-    const int64_t cells = (int64_t)a.rows * rq.npos;
-    const int64_t blocks = (cells + kWavesPerBlock - 1) / kWavesPerBlock;
+    const unsigned bx = (unsigned)((rq.npos + kWavesPerBlock - 1) / kWavesPerBlock);
+    const unsigned by = (unsigned)(a.rows < 65535 ? a.rows : 65535);
+    const unsigned bz = (unsigned)((a.rows + 65534) / 65535);
     constexpr bool kOcc = BF16 ? NS <= 9 : NS <= 16;
     if constexpr (kOcc)
-        hipLaunchKernelGGL((k_sample_small<BF16, NS>), dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
-                           st, a, rq);
+        hipLaunchKernelGGL((k_sample_small<BF16, NS>), dim3(bx, by, bz), dim3(kWavesPerBlock * kWave), 0, st, a,
+                           rq);
     else
-        hipLaunchKernelGGL((k_sample_small_wide<BF16, NS>), dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave),
-                           0, st, a, rq);
+        hipLaunchKernelGGL((k_sample_small_wide<BF16, NS>), dim3(bx, by, bz), dim3(kWavesPerBlock * kWave), 0, st,
+                           a, rq);
     return hipGetLastError();
 }
 
