@@ -51,12 +51,15 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// [ISSUE] CFG combine in fp32 with one rounding of s*(c-u)+c.  The max with -inf
-// maps the NaN of (-inf) - (-inf) at masked ids back to -inf (IEEE maxNum returns
-// the non-NaN operand); every other input passes through unchanged.
+// [ISSUE] CFG combine in fp32 with one rounding of s*(c-u)+c.  At a masked id
+// (c = u = -inf) the difference is NaN.  `guided` maps it back to -inf (IEEE
+// maxNum returns the non-NaN operand; every other input passes through
+// unchanged).  `guided_raw` leaves it: max, argmax and every >= / == test skip a
+// NaN, so a streaming pass only has to check its exp-sum, which a NaN turns into
+// NaN, and redo the sum with `guided` in that (masked, guided) case.
+__device__ __forceinline__ float guided_raw(float c, float u, float s) { return __builtin_fmaf(s, c - u, c); }
 __device__ __forceinline__ float guided(float c, float u, float s) {
-    float h = __builtin_fmaf(s, c - u, c);
-    return __builtin_fmaxf(h, kNegInf);
+    return __builtin_fmaxf(guided_raw(c, u, s), kNegInf);
 }
 
 // Order-preserving map binary32 -> uint32 (negative values: all bits flipped,

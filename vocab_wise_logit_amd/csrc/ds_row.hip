@@ -112,7 +112,8 @@ struct Piece {
     float h[EPP];
 };
 
-template <bool BF16>
+// FIX = false leaves the NaN of a masked id under guidance in h (see guided_raw).
+template <bool BF16, bool FIX = true>
 __device__ __forceinline__ void decode_piece(const u32x4 cw, const u32x4 uw, float s, bool use_u,
                                              Piece<BF16>& P) {
     if (BF16) {
@@ -121,8 +122,10 @@ __device__ __forceinline__ void decode_piece(const u32x4 cw, const u32x4 uw, flo
             const uint32_t uu[4] = {uw.x, uw.y, uw.z, uw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                P.h[2 * i] = guided(bf16_lo(cc[i]), bf16_lo(uu[i]), s);
-                P.h[2 * i + 1] = guided(bf16_hi(cc[i]), bf16_hi(uu[i]), s);
+                P.h[2 * i] = FIX ? guided(bf16_lo(cc[i]), bf16_lo(uu[i]), s)
+                                 : guided_raw(bf16_lo(cc[i]), bf16_lo(uu[i]), s);
+                P.h[2 * i + 1] = FIX ? guided(bf16_hi(cc[i]), bf16_hi(uu[i]), s)
+                                     : guided_raw(bf16_hi(cc[i]), bf16_hi(uu[i]), s);
             }
         } else {
 #pragma unroll
@@ -138,7 +141,7 @@ __device__ __forceinline__ void decode_piece(const u32x4 cw, const u32x4 uw, flo
             const float uf[4] = {__uint_as_float(uw.x), __uint_as_float(uw.y), __uint_as_float(uw.z),
                                  __uint_as_float(uw.w)};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) P.h[i] = guided(cf[i], uf[i], s);
+            for (int i = 0; i < 4; ++i) P.h[i] = FIX ? guided(cf[i], uf[i], s) : guided_raw(cf[i], uf[i], s);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) P.h[i] = cf[i];
@@ -261,6 +264,7 @@ struct CellParams {
 struct PartOut {
     float m, s;
     int id;
+    bool nan;  // (all threads) some wave's exp-sum is NaN: redo the part with FIX
     // Gumbel race of a sampled part: best (score, id, h) among the queued ids and
     // how many ids were queued
     float bz, bh;
@@ -273,7 +277,7 @@ struct PartOut {
 // `race`, each wave also runs the Gumbel race over the ids that can still win
 // (queued in LDS, scored 64 at a time).  At most 64 VGPRs: four workgroups per CU
 // keep enough loads in flight.
-template <bool BF16, bool SAMPLE>
+template <bool BF16, bool SAMPLE, bool FIX>
 __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, const CellParams& cp, bool use_u,
                                bool race, PartLDS<BF16, SAMPLE>& sh) {
     constexpr int EPP = Piece<BF16>::EPP;
@@ -367,7 +371,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             const int j = it * NT * U + uu * NT + (int)threadIdx.x;
-            decode_piece<BF16>(rc[uu], ru[uu], s, use_u, P[uu]);
+            decode_piece<BF16, FIX>(rc[uu], ru[uu], s, use_u, P[uu]);
             if (EDGE) {
                 const int v0 = vbase + j * EPP;
                 if (v0 < pr.lo || v0 + EPP > pr.hi) {
@@ -497,6 +501,11 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
     if (lane == 0) sh.r.w[wv] = WaveRec{wm, ws, wid, bz, bh, be, qtot, 0};
     __syncthreads();
     PartOut o;
+    o.nan = false;
+    if (!FIX && use_u) {
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) o.nan |= sh.r.w[i].s != sh.r.w[i].s;
+    }
     o.m = kNegInf;
     o.s = 0.0f;
     o.id = 0x7FFFFFFF;
@@ -556,7 +565,12 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
     const bool race = SAMPLE && cp.tau != 0.0f && !force_fallback;
     const RowGeom G = row_geom<BF16>(cptr, uptr, use_u, cp.cell, V, nch, w.ppc);
     const PartRange<BF16> pr(G, j, q);
-    const PartOut po = stream_part<BF16, SAMPLE>(G, pr, cp, use_u, race, sh);
+    PartOut po = stream_part<BF16, SAMPLE, false>(G, pr, cp, use_u, race, sh);
+    if (po.nan) {
+        // a masked id under guidance: stream the part again with h = -inf there
+        __syncthreads();
+        po = stream_part<BF16, SAMPLE, true>(G, pr, cp, use_u, race, sh);
+    }
     if (threadIdx.x == 0) {
         PartRec* rec = w.part + slot * w.nparts + part;
         rec->m = po.m;
@@ -728,11 +742,64 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     const int part = (int)(blockIdx.x - slot * a.w.nparts);
     part_body<BF16, false>(a.x, nullptr, a.V, a.vocab_chunks, false, a.w, greedy_cell(a, slot), slot, part);
 }
-template <bool BF16>
-__global__ __launch_bounds__(NT) void k_greedy_merge(GreedyArgs a) {
-    const int64_t slot = blockIdx.x;
-    merge_body<BF16, false>(a.x, nullptr, a.V, a.vocab_chunks, 1, false, a.w, greedy_cell(a, slot), slot, a.token,
-                            a.logprob, a.lse, nullptr, a.triples, a.n_rows);
+// Greedy rows need no pass over the row after the parts, so one wave merges a
+// row: lane i loads record i of each 64, and the fold walks them in order with
+// the record broadcast from its lane.
+__global__ __launch_bounds__(kWave) void k_greedy_merge(GreedyArgs a) {
+    const int64_t cell = a.w.cell_base + blockIdx.x;
+    const PartRec* recs = a.w.part + (int64_t)blockIdx.x * a.w.nparts;
+    const int lane = lane_id();
+    float M = kNegInf, S = 0.0f, mj = kNegInf, sj = 0.0f;
+    int id = 0x7FFFFFFF, idj = 0x7FFFFFFF;
+    for (int t0 = 0; t0 < a.w.nparts; t0 += kWave) {
+        const int n = min(kWave, a.w.nparts - t0);
+        float rm = kNegInf, rs = 0.0f;
+        int rid = 0x7FFFFFFF;
+        if (lane < n) {
+            const PartRec r = recs[t0 + lane];
+            rm = r.m;
+            rs = r.s;
+            rid = r.id;
+        }
+        for (int i = 0; i < n; ++i) {
+            const int p = t0 + i;
+            const float m = readlane_f(rm, i);
+            const float sm = readlane_f(rs, i);
+            const int im = __builtin_amdgcn_readlane(rid, i);
+            if (m > kNegInf) {
+                const float mn = __builtin_fmaxf(mj, m);
+                sj = ((mj > kNegInf) ? sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e) : 0.0f) +
+                     sm * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+                if (m > mj || (m == mj && im < idj)) idj = im;
+                mj = mn;
+            }
+            if ((p + 1) % a.w.ppc != 0) continue;
+            // chunk jj complete: its triple, then fold it into the row
+            const int jj = p / a.w.ppc;
+            if (a.triples && lane == 0) {
+                float* o = a.triples + ((int64_t)jj * a.n_rows + cell) * 3;
+                o[0] = mj;
+                o[1] = (mj > kNegInf) ? mj + __builtin_logf(sj) : kNegInf;
+                o[2] = __int_as_float(idj);
+            }
+            if (mj > kNegInf) {
+                const float mn = __builtin_fmaxf(M, mj);
+                S = ((M > kNegInf) ? S * __builtin_amdgcn_exp2f((M - mn) * kLog2e) : 0.0f) +
+                    sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e);
+                if (mj > M || (mj == M && idj < id)) id = idj;
+                M = mn;
+            }
+            mj = kNegInf;
+            sj = 0.0f;
+            idj = 0x7FFFFFFF;
+        }
+    }
+    if (lane == 0) {
+        const float lse = M + __builtin_logf(S);
+        a.token[cell] = id;
+        a.lse[cell] = lse;
+        a.logprob[cell] = M - lse;
+    }
 }
 
 }  // namespace
@@ -768,11 +835,10 @@ hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st) {
     if (parts == 0) return hipSuccess;
     if (bf16) {
         hipLaunchKernelGGL(k_greedy_parts<true>, dim3((unsigned)parts), dim3(NT), 0, st, a);
-        hipLaunchKernelGGL(k_greedy_merge<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a);
     } else {
         hipLaunchKernelGGL(k_greedy_parts<false>, dim3((unsigned)parts), dim3(NT), 0, st, a);
-        hipLaunchKernelGGL(k_greedy_merge<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a);
     }
+    hipLaunchKernelGGL(k_greedy_merge, dim3((unsigned)a.w.ncells), dim3(kWave), 0, st, a);
     return hipGetLastError();
 }
 

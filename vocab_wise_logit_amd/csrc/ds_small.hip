@@ -238,8 +238,8 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
             load_slots<NS>((const char*)a.u + off, lane, ndw, uw);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-                R.h[2 * j] = guided(bf16_lo(cw[j]), bf16_lo(uw[j]), s);
-                R.h[2 * j + 1] = guided(bf16_hi(cw[j]), bf16_hi(uw[j]), s);
+                R.h[2 * j] = guided_raw(bf16_lo(cw[j]), bf16_lo(uw[j]), s);
+                R.h[2 * j + 1] = guided_raw(bf16_hi(cw[j]), bf16_hi(uw[j]), s);
             }
         } else {
 #pragma unroll
@@ -266,7 +266,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
             uint32_t uw[NS];
             load_slots<NS>((const float*)a.u + cell * V, lane, V, uw);
 #pragma unroll
-            for (int j = 0; j < NS; ++j) R.h[j] = guided(__uint_as_float(cw[j]), __uint_as_float(uw[j]), s);
+            for (int j = 0; j < NS; ++j) R.h[j] = guided_raw(__uint_as_float(cw[j]), __uint_as_float(uw[j]), s);
         } else {
 #pragma unroll
             for (int j = 0; j < NS; ++j) R.h[j] = __uint_as_float(cw[j]);
@@ -307,7 +307,16 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(R.h[i], kLog2e, -mL));
-    const float S = wave_sum(acc);
+    float S = wave_sum(acc);
+    if (S != S) {
+        // a masked id under guidance left a NaN h: make it -inf and sum again
+#pragma unroll
+        for (int i = 0; i < NE; ++i) R.h[i] = __builtin_fmaxf(R.h[i], kNegInf);
+        acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(R.h[i], kLog2e, -mL));
+        S = wave_sum(acc);
+    }
     // exact residual of the rounded M*log2(e) shifts every exponent equally
     const float err = __builtin_fmaf(M, kLog2e, -mL);
     const float lse = M + (log2f(S) - err) * kLn2;
