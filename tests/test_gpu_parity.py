@@ -150,6 +150,19 @@ def test_row_kernel_small_temperature_and_masked_ids():
         assert not np.isin(got[0], [0, 5, 19999]).any()
 
 
+def test_row_kernel_threshold_bin_overflow():
+    # every h lies in [0.9, 1.3): the threshold's first 11-bit key digit is shared
+    # by far more ids than the select keeps in LDS, so its last two digits take
+    # passes over the row; bf16 values tie heavily at the threshold
+    w = synth.diffusion("bin_overflow", seed=31, vocab=30000, rows=1, seq_lens=[3], sigma=0.05, guidance=0.0,
+                        temperature=1.0, top_k=3000)
+    w.c = synth.bf16_from_f32(oracle.bf16_to_f32(w.c) + np.float32(1.1))
+    ref = oracle.sample_workload(w)
+    for thr in (False, True):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+    check_sample(w, run_sample(w, force_fallback=True), ref)
+
+
 def test_row_kernel_many_parts_per_row():
     # 4 positions x 4 chunks: each chunk is cut into several parts, each running
     # its own race

@@ -55,6 +55,7 @@ struct Red {
     int i[NWAVES];
     WaveRec w[NWAVES];
     uint32_t bcast_u;
+    int bcast_i;
 };
 
 // A sampled part's Gumbel race queues, per wave: pieces holding an id at or
@@ -72,10 +73,21 @@ struct PartLDS {
     Red r;
 };
 
-// The merge's staged part records and radix-select histogram.
+// The exact threshold select: digits of 11, 11 and 10 bits of the order key;
+// the keys sharing the first digit with the answer are kept in LDS when they fit.
+constexpr int kDigitShift[3] = {21, 10, 0};
+constexpr int kDigitBits[3] = {11, 11, 10};
+constexpr int kHistBins = 2048;
+constexpr int kKeyCap = 8192;
+
+// The merge's staged part records (or the threshold select's keys) and histogram.
 struct MergeLDS {
-    PartRec rec[NT];
-    uint32_t hist[256];
+    union {
+        PartRec rec[NT];
+        uint32_t keys[kKeyCap];
+    } u;
+    uint32_t hist[kHistBins];
+    int nkeys;
     Red r;
 };
 
@@ -213,42 +225,103 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
     }
 }
 
-// Pick the 8-bit digit holding the kk-th largest key from the histogram.
-__device__ __forceinline__ void pick_digit(MergeLDS& sh, int& kk, uint32_t& prefix, uint32_t& pmask, int shift) {
-    if (threadIdx.x == 0) {
-        int above = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-            const int c = (int)sh.hist[d];
-            if (above + c >= kk) break;
+// The digit (histogram bin) holding the kk-th largest key among those counted
+// in sh.hist[0, nbins), with 1 <= kk <= their number; kk becomes the rank inside
+// that bin.  Thread j owns bins nbins-1-j*b .. nbins-b-j*b (b = nbins / NT), so a
+// block prefix sum over the threads counts the keys in higher bins.
+__device__ uint32_t find_digit(MergeLDS& sh, int nbins, int& kk) {
+    const int bpt = nbins / NT;
+    const int lane = lane_id();
+    const int wv = threadIdx.x >> 6;
+    int own = 0;
+    for (int i = 0; i < bpt; ++i) own += (int)sh.hist[nbins - 1 - ((int)threadIdx.x * bpt + i)];
+    int x = own;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) sh.r.i[wv] = x;
+    __syncthreads();
+    int base = 0;
+    for (int w2 = 0; w2 < wv; ++w2) base += sh.r.i[w2];
+    const int incl = base + x;
+    const int excl = incl - own;
+    if (excl < kk && kk <= incl) {
+        int above = excl;
+        for (int i = 0; i < bpt; ++i) {
+            const int bin = nbins - 1 - ((int)threadIdx.x * bpt + i);
+            const int c = (int)sh.hist[bin];
+            if (above + c >= kk) {
+                sh.r.bcast_u = (uint32_t)bin;
+                sh.r.bcast_i = above;
+                break;
+            }
             above += c;
         }
-        sh.r.bcast_u = (uint32_t)d | ((uint32_t)above << 8);
     }
     __syncthreads();
-    const uint32_t d = sh.r.bcast_u & 255u;
-    kk -= (int)(sh.r.bcast_u >> 8);
-    prefix |= d << shift;
-    pmask |= 255u << shift;
+    const uint32_t d = sh.r.bcast_u;
+    kk -= sh.r.bcast_i;
     __syncthreads();
+    return d;
 }
 
-// Exact top_k-th largest h of the row: four 8-bit radix passes over re-reads.
+// Wave-aggregated append to an LDS counter; returns this lane's slot or -1.
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+    const uint64_t m = ballot(pred);
+    if (!m) return -1;
+    int base = 0;
+    const int leader = (int)__builtin_ctzll(m);
+    if (lane_id() == leader) base = atomicAdd(counter, popc(m));
+    base = __builtin_amdgcn_readlane(base, leader);
+    return pred ? base + lanes_below(m) : -1;
+}
+
+// Exact top_k-th largest h of the row (an LDS radix select on order keys).  One
+// pass over the row histograms the first 11-bit digit; a second collects the
+// keys in the chosen bin into LDS, where the last two digits are selected.  If
+// that bin holds more than kKeyCap keys, the last digits take a pass over the
+// row each instead.
 template <bool BF16>
 __device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, MergeLDS& sh) {
     uint32_t prefix = 0, pmask = 0;
     int kk = k;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0;
+    auto hist_pass = [&](int dg, bool from_lds, int n) {
+        const int shift = kDigitShift[dg];
+        const uint32_t dmask = (1u << kDigitBits[dg]) - 1u;
+        for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
         __syncthreads();
-        for_each_id<BF16>(G, s, use_u, [&](int, float h) {
-            const uint32_t key = order_key(h + 0.0f);
-            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-        });
+        if (from_lds) {
+            for (int i = threadIdx.x; i < n; i += NT) {
+                const uint32_t key = sh.u.keys[i];
+                if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+            }
+        } else {
+            for_each_id<BF16>(G, s, use_u, [&](int, float h) {
+                const uint32_t key = order_key(h + 0.0f);
+                if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+            });
+        }
         __syncthreads();
-        pick_digit(sh, kk, prefix, pmask, shift);
-    }
+        const uint32_t d = find_digit(sh, 1 << kDigitBits[dg], kk);
+        prefix |= d << shift;
+        pmask |= dmask << shift;
+    };
+    hist_pass(0, false, 0);
+    // keep the keys that share the first digit with the answer
+    if (threadIdx.x == 0) sh.nkeys = 0;
+    __syncthreads();
+    for_each_id<BF16>(G, s, use_u, [&](int, float h) {
+        const uint32_t key = order_key(h + 0.0f);
+        const int at = wave_append((key & pmask) == prefix, &sh.nkeys);
+        if (at >= 0 && at < kKeyCap) sh.u.keys[at] = key;
+    });
+    __syncthreads();
+    const int n = sh.nkeys;
+    const bool fit = n <= kKeyCap;
+    hist_pass(1, fit, n);
+    hist_pass(2, fit, n);
     return key_value(prefix);
 }
 
@@ -607,11 +680,11 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
     for (int t0 = 0; t0 < w.nparts; t0 += NT) {
         const int n = min(NT, w.nparts - t0);
         __syncthreads();
-        if ((int)threadIdx.x < n) sh.rec[threadIdx.x] = recs[t0 + threadIdx.x];
+        if ((int)threadIdx.x < n) sh.u.rec[threadIdx.x] = recs[t0 + threadIdx.x];
         __syncthreads();
         for (int i = 0; i < n; ++i) {
             const int p = t0 + i;
-            const PartRec r = sh.rec[i];
+            const PartRec r = sh.u.rec[i];
             if (sampled) {
                 raced &= r.nq >= 0;
                 queued += r.nq;
