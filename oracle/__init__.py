@@ -68,6 +68,8 @@ def _setup(lib):
                                C.c_int32, C.c_uint64, P, C.c_int64, P, P, P, P, P, P, P]
     lib.dso_merge_triples.argtypes = [P, P, P]
     lib.dso_greedy_lse.restype = C.c_int
+    lib.dso_reveal_topk.restype = C.c_int
+    lib.dso_reveal_topk.argtypes = [P, C.c_int32, C.c_int64, P, P, C.c_int32, P, P]
     lib.dso_greedy_lse.argtypes = [C.c_int, C.c_int32, P, P, C.c_int64, C.c_int32, P, P, P, P,
                                    P, P]
     return lib
@@ -253,3 +255,21 @@ def greedy_lse(x: np.ndarray, vocab_chunks: int = 1, rows: Optional[np.ndarray] 
         raise ValueError(_err(lib))
     return GreedyResult(rows=rows, token=token, lse=lse_, logprob=lp, triples=trip,
                         dense_token=dtok, dense_lse=dlse)
+
+
+def reveal_topk(scores: np.ndarray, seq_lens, reveal_counts, lib=None):
+    """Per request, the reveal_counts[r] best cells of its [C, T_r] block of the
+    packed [C, P] scores: (flattened indices c * T_r + t, scores), concatenated
+    over the requests in order, each request's best first."""
+    lib = lib or _load()
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    Cn, P = scores.shape
+    seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    rev = np.ascontiguousarray(reveal_counts, dtype=np.int32)
+    total = int(rev.sum())
+    idx = np.empty(max(total, 1), dtype=np.int64)
+    val = np.empty(max(total, 1), dtype=np.float32)
+    rc = lib.dso_reveal_topk(_ptr(scores), Cn, P, _ptr(seq), _ptr(rev), int(seq.size), _ptr(idx), _ptr(val))
+    if rc != 0:
+        raise ValueError(_err(lib))
+    return idx[:total], val[:total]

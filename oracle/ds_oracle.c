@@ -42,6 +42,9 @@
  *     (v >> 2, t, (row & 0xFFFF) | (iteration << 16), (uint32)request_id), word
  *     v & 3; U = ((x >> 9) * 2 + 1) * 2^-24; G = -log(-log U); the token
  *     maximises h / tau + G over the kept ids, smallest id on exact ties.
+ *   - Confidence reveal ([ISSUE], the top-k over the flattened [C, T] scores):
+ *     per request, the reveal_count largest scores of its [C, T] block flattened
+ *     row-major, best first, the smaller flattened index first on equal scores.
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off, no fast-math, so that
  * float expressions round exactly as written (IEEE-754 binary32 / binary64,
@@ -473,5 +476,62 @@ int dso_greedy_lse(int dtype, int32_t V, const void *x, const int64_t *rows, int
         }
     }
     free(work);
+    return 0;
+}
+
+/* ---------------------------------------------------- confidence reveal */
+
+/* The step after the sampler on the issue page ([ISSUE], comment on the API
+ * shape): every position of a request is scored by a confidence, and the caller
+ * commits the reveal_count best, as a top-k over the request's [C, T] scores
+ * flattened row-major (f = c * T + t).  Order: the larger score first; equal
+ * scores keep the smaller flattened index first ([DRAFT]'s smallest-id rule,
+ * applied to this decision as to every other). */
+typedef struct {
+    float s;
+    int64_t f;
+} dso_ranked;
+
+static int cmp_ranked(const void *pa, const void *pb) {
+    const dso_ranked *a = (const dso_ranked *)pa, *b = (const dso_ranked *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->f < b->f) ? -1 : (a->f > b->f);
+}
+
+/* scores: [C, P] row-major with the requests packed along positions in argument
+ * order; reveal[r] in [0, C * seq_lens[r]].  Writes sum(reveal) entries, request
+ * by request in argument order: the flattened index and the score of each
+ * revealed cell, best first. */
+int dso_reveal_topk(const float *scores, int32_t C, int64_t P, const int32_t *seq_lens,
+                    const int32_t *reveal, int32_t R, int64_t *idx_out, float *val_out) {
+    int64_t off = 0, out = 0;
+    for (int32_t r = 0; r < R; r++) {
+        const int64_t T = seq_lens[r];
+        const int64_t n = (int64_t)C * T;
+        if (T < 0 || off + T > P) return fail("seq_lens exceed the positions of scores");
+        if (reveal[r] < 0 || reveal[r] > n) return fail("reveal count outside [0, C * T]");
+        dso_ranked *buf = (dso_ranked *)malloc(sizeof(dso_ranked) * (size_t)(n > 0 ? n : 1));
+        if (!buf) return fail("out of memory");
+        for (int32_t c = 0; c < C; c++) {
+            for (int64_t t = 0; t < T; t++) {
+                const float s = scores[(int64_t)c * P + off + t];
+                if (isnan(s)) {
+                    free(buf);
+                    return fail("NaN score");
+                }
+                buf[c * T + t].s = s;
+                buf[c * T + t].f = c * T + t;
+            }
+        }
+        qsort(buf, (size_t)n, sizeof(dso_ranked), cmp_ranked);
+        for (int32_t j = 0; j < reveal[r]; j++) {
+            idx_out[out + j] = buf[j].f;
+            val_out[out + j] = buf[j].s;
+        }
+        out += reveal[r];
+        off += T;
+        free(buf);
+    }
     return 0;
 }

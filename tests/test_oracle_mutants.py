@@ -49,6 +49,13 @@ MUTANTS = {
     "no_canonical_zero": ("    return h + 0.0f;\n}", "    return h;\n}"),
     "draft_lp_dense": ("logprob[i] = (double)load_elem(row, dtype, acc.id) - acc.lse;",
                        "logprob[i] = (double)load_elem(row, dtype, acc.id);"),
+    "reveal_tie_larger": ("return (a->f < b->f) ? -1 : (a->f > b->f);",
+                          "return (a->f > b->f) ? -1 : (a->f < b->f);"),
+    "reveal_ascending": ("if (a->s > b->s) return -1;\n    if (a->s < b->s) return 1;",
+                         "if (a->s < b->s) return -1;\n    if (a->s > b->s) return 1;"),
+    "reveal_flatten_transposed": ("buf[c * T + t].f = c * T + t;", "buf[c * T + t].f = t * C + c;"),
+    "reveal_count_short": ("for (int32_t j = 0; j < reveal[r]; j++) {",
+                           "for (int32_t j = 0; j + 1 < reveal[r]; j++) {"),
 }
 
 
@@ -170,8 +177,23 @@ def check_draft(lib):
         assert np.max(np.abs(r.logprob - (x[np.arange(40), r.token] - lse))) < 1e-12
 
 
+def check_reveal(lib):
+    # increasing scores in flattened order, then all-equal scores, on two requests
+    C, seq = 3, [4, 5]
+    s = np.zeros((C, 9), np.float32)
+    s[:, :4] = np.arange(12, dtype=np.float32).reshape(C, 4)
+    s[:, 4:] = 1.0
+    idx, val = oracle.reveal_topk(s, seq, [5, 6], lib=lib)
+    assert idx.tolist() == [11, 10, 9, 8, 7, 0, 1, 2, 3, 4, 5]
+    assert val.tolist() == [11.0, 10.0, 9.0, 8.0, 7.0] + [1.0] * 6
+    # a transposed flattening shows on a non-square block
+    s2 = np.zeros((2, 3), np.float32)
+    s2[0, 2] = 5.0
+    assert oracle.reveal_topk(s2, [3], [1], lib=lib)[0].tolist() == [2]
+
+
 CHECKS = [check_guided, check_bf16, check_logprobs, check_philox, check_gumbel,
-          check_threshold, check_greedy, check_sampling, check_draft]
+          check_threshold, check_greedy, check_sampling, check_draft, check_reveal]
 
 
 def _failures(lib):

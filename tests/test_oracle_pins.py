@@ -503,3 +503,88 @@ def test_validation_errors():
         oracle.sample(c=w.c, u=w.u, seq_lens=w.seq_lens, request_ids=w.request_ids,
                       iterations=w.iterations, guidance=w.guidance, temperature=w.temperature,
                       rows=w.rows, seed=1, top_k=w.vocab + 1)
+
+
+# ------------------------------------------------------ confidence reveal
+
+def _reveal_case(seed, C, seq, grid):
+    rng = np.random.default_rng(seed)
+    P = int(np.sum(seq))
+    s = (np.round(rng.normal(size=(C, P)) * grid) / grid).astype(np.float32)
+    s[rng.random((C, P)) < 0.05] = -np.inf
+    return s
+
+
+def test_reveal_closed_forms():
+    # increasing scores in flattened order: the best are the last cells, last first
+    C, seq = 3, [4, 0, 5]
+    P = sum(seq)
+    s = np.zeros((C, P), np.float32)
+    off = 0
+    for T in seq:
+        for c in range(C):
+            s[c, off:off + T] = c * T + np.arange(T)
+        off += T
+    idx, val = oracle.reveal_topk(s, seq, [5, 0, 15])
+    assert idx.tolist() == [11, 10, 9, 8, 7] + list(range(14, -1, -1))
+    assert val.tolist() == [float(i) for i in idx]
+    # equal scores: the smallest flattened indices, in order
+    idx, _ = oracle.reveal_topk(np.ones((2, 6), np.float32), [6], [4])
+    assert idx.tolist() == [0, 1, 2, 3]
+    # a single finite cell among -inf comes first, then -inf cells by index
+    s = np.full((2, 3), -np.inf, np.float32)
+    s[1, 1] = -7.0
+    idx, val = oracle.reveal_topk(s, [3], [3])
+    assert idx.tolist() == [4, 0, 1] and val[0] == -7.0 and np.isneginf(val[1:]).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_reveal_invariants_with_heavy_ties(seed):
+    C, seq = 4, [7, 1, 13, 0, 9]
+    s = _reveal_case(seed, C, seq, grid=2)
+    rev = [3, 4, 20, 0, 36]
+    idx, val = oracle.reveal_topk(s, seq, rev)
+    o = off = 0
+    for T, k in zip(seq, rev):
+        blk = s[:, off:off + T].reshape(-1)  # the request's [C, T] cells, row-major
+        sel, sv = idx[o:o + k], val[o:o + k]
+        assert len(set(sel.tolist())) == k and (sel >= 0).all() and (sel < C * T).all()
+        assert np.array_equal(sv, blk[sel])
+        # best first; equal scores in increasing index
+        for a in range(k - 1):
+            assert sv[a] > sv[a + 1] or (sv[a] == sv[a + 1] and sel[a] < sel[a + 1])
+        rest = np.setdiff1d(np.arange(C * T), sel)
+        if k and rest.size:
+            low = sv.min()
+            assert (blk[rest] <= low).all()
+            # at the boundary score, every unselected cell comes after every selected one
+            tied = rest[blk[rest] == low]
+            assert tied.size == 0 or tied.min() > sel[sv == low].max()
+        o += k
+        off += T
+
+
+def test_reveal_matches_torch_topk_on_distinct_scores():
+    import torch
+
+    rng = np.random.default_rng(9)
+    C, seq = 8, [37, 120, 5]
+    s = rng.permutation(C * sum(seq)).astype(np.float32).reshape(C, -1)
+    rev = [10, 96, 40]
+    idx, _ = oracle.reveal_topk(s, seq, rev)
+    o = off = 0
+    for T, k in zip(seq, rev):
+        flat = torch.from_numpy(np.ascontiguousarray(s[:, off:off + T])).flatten()
+        want = torch.topk(flat, k).indices.numpy()
+        assert np.array_equal(idx[o:o + k], want)
+        o += k
+        off += T
+
+
+def test_reveal_rejects_bad_counts_and_nan():
+    s = np.zeros((2, 3), np.float32)
+    with pytest.raises(ValueError):
+        oracle.reveal_topk(s, [3], [7])
+    s[0, 1] = np.nan
+    with pytest.raises(ValueError):
+        oracle.reveal_topk(s, [3], [1])

@@ -3,8 +3,10 @@
 // Validates every argument before anything is enqueued, splits a call into
 // launches of at most 64 requests (their per-request parameters travel by value in
 // the kernel argument segment, so no host-to-device copy precedes a launch), and
-// picks the kernel: one wavefront per cell when the row fits in registers, one
-// workgroup per cell otherwise.
+// picks the path: one wavefront per cell when the row fits in registers;
+// otherwise a parts kernel (one workgroup per vocabulary part of a row) and a
+// merge kernel (one per row), in batches of rows that fit the handle's record
+// workspace.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
