@@ -41,10 +41,13 @@ ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = {
     "small": ("ds_small.hip", "ds_device.h", "ds_kernels.h"),
     "row": ("ds_row.hip", "ds_device.h", "ds_kernels.h"),
+    "reveal": ("ds_reveal.hip", "ds_device.h", "ds_kernels.h"),
 }
 
 
 def kernel_family(workload: str) -> str:
+    if workload == "reveal":
+        return "reveal"
     return "small" if workload in ("tiny", "omnivoice", "mixed") else "row"
 
 
@@ -81,6 +84,8 @@ def to_dev(arr: np.ndarray):
 
 
 def kernel_name(w, kind: str) -> str:
+    if kind == "reveal":
+        return "k_reveal_topk"
     if kind == "draft":
         return "k_greedy_parts+k_greedy_merge"
     slots = ((w.vocab + 2) // 2 if w.dtype == "bf16" else w.vocab + 63) // 64
@@ -108,7 +113,18 @@ class Runner:
         import vocab_wise_logit_amd as ds
 
         self.w, self.kind = w, kind
-        if kind == "draft":
+        if kind == "reveal":
+            x = torch.from_numpy(np.ascontiguousarray(w.scores)).cuda()
+            per_set = x.numel() * x.element_size()
+            self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
+            self.x = [x] + [x.clone() for _ in range(self.n_sets - 1)]
+            self.smp = ds.Sampler(16, "f32", max_rows=w.rows, max_positions=w.positions,
+                                  max_requests=len(w.seq_lens))
+            total = int(w.reveal_counts.sum())
+            self.out = (torch.empty(total, dtype=torch.int32, device="cuda"),
+                        torch.empty(total, dtype=torch.float32, device="cuda"))
+            self.cells = w.rows * w.positions
+        elif kind == "draft":
             x = to_dev(w.logits)
             per_set = x.numel() * x.element_size()
             self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
@@ -139,7 +155,9 @@ class Runner:
     def step(self, i: int) -> None:
         s = i % self.n_sets
         w = self.w
-        if self.kind == "draft":
+        if self.kind == "reveal":
+            self.smp.reveal_topk(self.x[s], w.seq_lens, w.reveal_counts, out=self.out)
+        elif self.kind == "draft":
             self.smp.greedy_lse(self.x[s], out=self.out)
         else:
             self.smp.sample(w.request_ids, self.c[s], self.u[s] if self.u else None, w.seq_lens,
@@ -181,6 +199,9 @@ def time_runner(r: Runner, steps: int, warmup: int):
 
 
 def describe(w, kind: str) -> dict:
+    if kind == "reveal":
+        return {"workload": "confidence_reveal", "requests": int(len(w.seq_lens)), "rows": w.rows,
+                "positions": w.positions, "revealed": int(w.reveal_counts.sum())}
     if kind == "draft":
         return {"workload": "draft_greedy", "rows": w.n_rows, "vocab": w.vocab,
                 "input_dtype": w.dtype, "vocab_chunks": w.vocab_chunks}
@@ -194,13 +215,13 @@ def describe(w, kind: str) -> dict:
 def launches_per_step(w, kind: str) -> int:
     """Kernel launches of one call: one for the wave-per-cell kernel, a parts and a
     merge kernel for the streaming path (every workload here fits one batch)."""
-    return 1 if kernel_name(w, kind).startswith("k_sample_small") else 2
+    return 1 if kernel_name(w, kind).startswith(("k_sample_small", "k_reveal")) else 2
 
 
 def bench_one(name: str, steps: int, warmup: int, threshold: bool = False) -> dict:
     import torch
 
-    kind = "draft" if name == "draft" else "sample"
+    kind = name if name in ("draft", "reveal") else "sample"
     w = make_workload(name)
     r = Runner(w, kind, threshold)
     ms_step, ms_kernel, med, p10, p90 = time_runner(r, steps, warmup)
@@ -208,7 +229,8 @@ def bench_one(name: str, steps: int, warmup: int, threshold: bool = False) -> di
     del r
     torch.cuda.empty_cache()
     alg = w.algorithmic_bytes()
-    cells = w.n_rows if kind == "draft" else w.cells
+    # positions: cells sampled, draft rows reduced, or cells ranked by the reveal
+    cells = {"draft": lambda: w.n_rows, "reveal": lambda: w.rows * w.positions}.get(kind, lambda: w.cells)()
     # every workload here has <= 64 requests, so one step is one launch of the
     # wave-per-cell kernel (its back-to-back time per step is that kernel's
     # average duration on its stream) or one parts + merge pair
@@ -291,7 +313,7 @@ def main() -> int:
     if not args.no_suite:
         # every workload, then the two sampled shapes again with the threshold
         # output requested (it needs the exact k-th largest h of every row)
-        runs = [(n, False) for n in ("tiny", "omnivoice", "mixed", "draft", "stress")]
+        runs = [(n, False) for n in ("tiny", "omnivoice", "mixed", "draft", "stress", "reveal")]
         runs += [("omnivoice", True), ("stress", True)]
         for name, thr in runs:
             if name == args.workload and not thr:

@@ -152,6 +152,35 @@ int ds_sample(ds_sampler *s, const int64_t *request_ids, const void *c_logits,
 int ds_greedy_lse(ds_sampler *s, const void *logits, int64_t n_rows, int32_t *token_out,
                   float *lse_out, float *logprob_out, float *triples_out, void *stream);
 
+/*
+ * ds_reveal_topk -- the confidence reveal that follows a sampling step
+ * ([ISSUE], comment on the API shape: the step scores every position, ranks
+ * them by confidence and commits the best, a top-k over the request's [C, T]
+ * scores flattened row-major).  For every request r, returns its reveal_counts[r]
+ * best cells, best first; equal scores keep the smaller flattened index first
+ * (the smallest-id rule of [DRAFT] "Design and invariants").
+ *
+ *   scores         device float [C, P], requests packed along positions as in
+ *                  ds_sample (for example ds_sample's logprobs_out, or the
+ *                  caller's confidence with committed positions set to -inf);
+ *                  4-byte aligned; values finite or -inf (NaN unsupported).
+ *   num_rows       C, 1 .. max_rows.
+ *   seq_lens       host [R], each >= 0; P = sum <= max_positions.
+ *   reveal_counts  host [R]; 0 <= reveal_counts[r] <= C * seq_lens[r], and at
+ *                  most 16384 per request (DS_ERR_UNSUPPORTED above).
+ *   num_requests   R, 1 .. max_requests.
+ *   index_out      device int32 [sum(reveal_counts)]: request by request in
+ *                  argument order, the flattened index c * seq_lens[r] + t of each
+ *                  revealed cell (row c, position t of the request).
+ *   score_out      device float [sum(reveal_counts)] or NULL: their scores.
+ *   stream         hipStream_t.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY, DS_ERR_UNSUPPORTED or
+ * DS_ERR_HIP.  Nothing is written when every reveal count is 0.
+ */
+int ds_reveal_topk(ds_sampler *s, const float *scores, int32_t num_rows, const int32_t *seq_lens,
+                   const int32_t *reveal_counts, int32_t num_requests, int32_t *index_out,
+                   float *score_out, void *stream);
+
 /* Release a handle and its device scratch.  NULL is a no-op.  The caller must
  * make sure no call on the handle is still pending on a stream. */
 void ds_sample_destroy(ds_sampler *s);

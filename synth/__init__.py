@@ -9,11 +9,13 @@ exactly these arrays.
 from .workloads import (  # noqa: F401
     DiffusionWorkload,
     DraftWorkload,
+    RevealWorkload,
     bf16_from_f32,
     diffusion,
     draft,
     mixed,
     omnivoice,
+    reveal,
     stress,
     tiny,
     WORKLOADS,

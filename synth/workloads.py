@@ -287,6 +287,48 @@ def draft(n_rows: int = 256, vocab: int = 248320, seed: int = 3, vocab_chunks: i
                          vocab_chunks=vocab_chunks, tie_rows=tie_rows)
 
 
+@dataclass
+class RevealWorkload:
+    """Confidence scores [C, P] packed like the sampler's outputs, and how many
+    cells each request reveals."""
+    name: str
+    scores: np.ndarray        # float32 [C, P]
+    seq_lens: np.ndarray      # int32 [R]
+    reveal_counts: np.ndarray  # int32 [R]
+
+    @property
+    def rows(self) -> int:
+        return int(self.scores.shape[0])
+
+    @property
+    def positions(self) -> int:
+        return int(self.scores.shape[1])
+
+    def algorithmic_bytes(self) -> int:
+        """Scores read once, one (index, score) pair written per revealed cell."""
+        return int(self.scores.size * 4 + 8 * int(self.reveal_counts.sum()))
+
+
+def reveal(n_requests: int = 8, rows: int = 8, seed: int = 5, lo: int = 80, hi: int = 120,
+           committed: float = 1.0 / 3.0, ratio: float = 0.1, grid: float = 16.0,
+           name: str = "reveal") -> RevealWorkload:
+    """Confidence reveal after an OmniVoice-shaped step: ragged lengths uniform in
+    [lo, hi], scores shaped like log-probabilities (-|N(0, 2)| rounded to 1/grid,
+    so equal scores occur), a seeded fraction of cells already committed (-inf),
+    and ceil(ratio * C * T_r) cells revealed per request."""
+    root = np.random.SeedSequence([seed, 11])
+    s_len, s_val, s_mask = root.spawn(3)
+    g = np.random.Generator(np.random.PCG64(s_len))
+    seq_lens = g.integers(lo, hi + 1, n_requests).astype(np.int32)
+    P = int(seq_lens.sum())
+    vals = -np.abs(_normal_f32(s_val, rows * P, 2.0))
+    vals = (np.round(vals * grid) / grid).astype(np.float32).reshape(rows, P)
+    gm = np.random.Generator(np.random.PCG64(s_mask))
+    vals[gm.random((rows, P)) < committed] = -np.inf
+    counts = np.ceil(ratio * rows * seq_lens).astype(np.int32)
+    return RevealWorkload(name=name, scores=vals, seq_lens=seq_lens, reveal_counts=counts)
+
+
 WORKLOADS: Dict[str, Callable[[], object]] = {
     "tiny_greedy": lambda: tiny(0.0),
     "tiny_sampled": lambda: tiny(0.9),
@@ -294,4 +336,5 @@ WORKLOADS: Dict[str, Callable[[], object]] = {
     "mixed": mixed,
     "draft": draft,
     "stress": stress,
+    "reveal": reveal,
 }

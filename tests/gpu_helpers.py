@@ -133,3 +133,27 @@ def check_greedy(x: np.ndarray, got, ref: "oracle.GreedyResult", name: str = "")
         assert np.max(np.abs(tri[:, :, 1][fin] - rt[:, :, 1][fin])) <= LP_TOL
         assert np.all(np.isneginf(tri[:, :, 1][~fin]))
     log(f"[check] greedy {name}: rows={rows.size} ok")
+
+
+def run_reveal(w, *, scores_dev=None, max_positions=None):
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    log(f"[gpu] ds_reveal_topk {w.name}: C={w.rows} P={w.positions} R={len(w.seq_lens)} "
+        f"reveal={int(w.reveal_counts.sum())} max_k={int(w.reveal_counts.max(initial=0))}")
+    with ds.Sampler(16, "f32", max_rows=w.rows, max_positions=max(1, max_positions or w.positions),
+                    max_requests=len(w.seq_lens)) as smp:
+        s = scores_dev if scores_dev is not None else torch.from_numpy(np.ascontiguousarray(w.scores)).cuda()
+        idx, val = smp.reveal_topk(s, w.seq_lens, w.reveal_counts)
+        torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def check_reveal(w, got) -> None:
+    ref_idx, ref_val = oracle.reveal_topk(w.scores, w.seq_lens, w.reveal_counts)
+    idx, val = got
+    bad = np.nonzero(idx.astype(np.int64) != ref_idx)[0]
+    assert bad.size == 0, f"reveal index mismatch at {bad[:10]}: gpu {idx[bad[:10]]} oracle {ref_idx[bad[:10]]}"
+    assert np.array_equal(val.view(np.uint32), ref_val.view(np.uint32)), "reveal scores differ"
+    log(f"[check] {w.name}: {idx.size} revealed cells match")

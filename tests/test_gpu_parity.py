@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import (check_greedy, check_sample, log, run_greedy, run_sample, to_dev)
+from gpu_helpers import (check_greedy, check_reveal, check_sample, log, run_greedy, run_reveal, run_sample,
+                         to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -257,6 +258,64 @@ def test_greedy_lse_shapes_and_chunks(V, chunks):
             x = synth.bf16_from_f32(x)
         ref = oracle.greedy_lse(x, vocab_chunks=chunks)
         check_greedy(x, run_greedy(x, chunks), ref, f"V={V} chunks={chunks} {dtype}")
+
+
+# ------------------------------------------------------ confidence reveal
+
+def test_reveal_omnivoice_shaped():
+    w = synth.reveal()
+    check_reveal(w, run_reveal(w))
+
+
+def test_reveal_ties_edges_and_several_launches():
+    # coarse grid (many equal scores at the boundary), empty requests, reveal 0,
+    # reveal everything, a single row, and 150 requests over three launches
+    rng = np.random.default_rng(12)
+    R = 150
+    seq = rng.integers(0, 30, R).astype(np.int32)
+    seq[:3] = [0, 5, 17]
+    C = 3
+    scores = (np.round(rng.normal(size=(C, int(seq.sum()))) * 2) / 2).astype(np.float32)
+    scores[rng.random(scores.shape) < 0.2] = -np.inf
+    k = np.minimum(rng.integers(0, 40, R), C * seq).astype(np.int32)
+    k[1] = 0
+    k[2] = C * seq[2]
+    w = synth.RevealWorkload("reveal_edges", scores, seq, k)
+    check_reveal(w, run_reveal(w))
+    w1 = synth.reveal(n_requests=5, rows=1, seed=13, name="reveal_one_row")
+    check_reveal(w1, run_reveal(w1))
+
+
+@pytest.mark.parametrize("T,counts", [(400, [1, 3200, 700]), (1500, [12000, 5, 4096]),
+                                      (3000, [16384, 1, 12000])])
+def test_reveal_largest_sizes(T, counts):
+    # 8 x T cells per request: keys held 4 or 16 per thread in registers, or (at
+    # 24000 cells) read on every pass; reveal counts up to the 16384 cap
+    w = synth.reveal(n_requests=3, rows=8, seed=14 + T, lo=T, hi=T, ratio=0.5, name=f"reveal_{T}")
+    w.reveal_counts = np.array(counts, np.int32)
+    check_reveal(w, run_reveal(w))
+
+
+def test_reveal_rejects_bad_counts():
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    s = torch.zeros((2, 10), dtype=torch.float32, device="cuda")
+    # room for every requested slot, so that even an accepted call stays in bounds
+    idx = torch.full((16400,), -7, dtype=torch.int32, device="cuda")
+    with ds.Sampler(16, "f32", max_rows=2, max_positions=40000, max_requests=4) as smp:
+        for seq, k, code in (([4, 6], [9, 1], ds.DS_ERR_INVALID_ARG), ([4, 6], [-1, 1], ds.DS_ERR_INVALID_ARG),
+                             ([10], [21], ds.DS_ERR_INVALID_ARG)):
+            with pytest.raises(ds.DSError) as e:
+                ds.ds_reveal_topk(smp._h, s, 2, seq, k, idx)
+            assert e.value.code == code
+        big = torch.zeros((2, 20000), dtype=torch.float32, device="cuda")
+        with pytest.raises(ds.DSError) as e:
+            ds.ds_reveal_topk(smp._h, big, 2, [20000], [16385], idx)
+        assert e.value.code == ds.DS_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+    assert (idx.cpu() == -7).all()
 
 
 def test_invalid_calls_are_rejected_before_launch():

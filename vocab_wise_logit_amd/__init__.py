@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     ds_greedy_lse,
     ds_last_error,
+    ds_reveal_topk,
     ds_sample,
     ds_sample_create,
     ds_sample_destroy,
@@ -40,7 +41,9 @@ class Sampler:
     ``sample`` follows the diffusion sampler contract
     ``sample(request_ids, c_logits, u_logits, seq_lens, iterations) -> (tokens,
     logprobs)`` with per-request guidance scale and temperature;
-    ``greedy_lse`` is the draft path's (token, lse, logprob) reduction.
+    ``greedy_lse`` is the draft path's (token, lse, logprob) reduction;
+    ``reveal_topk`` ranks each request's cells by a confidence score and returns
+    the best ones.
     """
 
     def __init__(self, vocab: int, dtype: str = "bf16", *, max_rows: int = 8,
@@ -106,3 +109,19 @@ class Sampler:
             tok, lse, lp, tri = out
         ds_greedy_lse(self._h, logits, n, tok, lse, lp, tri, stream)
         return (tok, lse, lp, tri) if triples else (tok, lse, lp)
+
+    def reveal_topk(self, scores, seq_lens: Sequence[int], reveal_counts: Sequence[int], out=None,
+                    stream=None):
+        """scores float32 [C, P] -> (index int32 [sum(reveal_counts)], score float32
+        [sum(reveal_counts)]): per request, the flattened indices c * T_r + t of
+        its best cells, best first, and their scores."""
+        import torch
+
+        total = int(sum(int(k) for k in reveal_counts))
+        if out is None:
+            idx = torch.empty(max(total, 1), dtype=torch.int32, device=scores.device)[:total]
+            val = torch.empty(max(total, 1), dtype=torch.float32, device=scores.device)[:total]
+        else:
+            idx, val = out
+        ds_reveal_topk(self._h, scores, int(scores.shape[0]), seq_lens, reveal_counts, idx, val, stream)
+        return idx, val

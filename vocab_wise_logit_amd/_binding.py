@@ -1,7 +1,7 @@
 """ctypes binding of libdssample.so: argument marshalling only.
 
 Functions carry the C entry points' names (ds_sample_create, ds_sample,
-ds_greedy_lse, ds_sample_destroy, ds_last_error, ds_version).  Device buffers are
+ds_greedy_lse, ds_reveal_topk, ds_sample_destroy, ds_last_error, ds_version).  Device buffers are
 torch tensors on a HIP device (torch supplies memory and streams); per-request
 arrays are host sequences.  Every computation happens in the HIP library; when the
 library is missing the calls raise instead of falling back to anything else.
@@ -21,8 +21,8 @@ DS_DTYPE_F32, DS_DTYPE_BF16 = 0, 1
 DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY, DS_ERR_HIP = range(6)
 DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK = 0, 1
 
-EXPORTED = ("ds_sample_create", "ds_sample", "ds_greedy_lse", "ds_sample_destroy", "ds_last_error",
-            "ds_version")
+EXPORTED = ("ds_sample_create", "ds_sample", "ds_greedy_lse", "ds_reveal_topk", "ds_sample_destroy",
+            "ds_last_error", "ds_version")
 
 _lib = None
 
@@ -47,6 +47,8 @@ def lib():
         L.ds_sample.argtypes = [P, P, P, P, P, P, P, P, I32, I32, U64, P, P, P, P]
         L.ds_greedy_lse.restype = C.c_int
         L.ds_greedy_lse.argtypes = [P, P, I64, P, P, P, P, P]
+        L.ds_reveal_topk.restype = C.c_int
+        L.ds_reveal_topk.argtypes = [P, P, I32, P, P, I32, P, P, P]
         L.ds_sample_destroy.restype = None
         L.ds_sample_destroy.argtypes = [P]
         L.ds_last_error.restype = C.c_char_p
@@ -146,3 +148,16 @@ def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_
                                _dev_ptr(logprob_out, "logprob_out", torch.float32),
                                _dev_ptr(triples_out, "triples_out", torch.float32),
                                _stream_ptr(stream)))
+
+
+def ds_reveal_topk(handle: int, scores, num_rows: int, seq_lens: Sequence[int],
+                   reveal_counts: Sequence[int], index_out, score_out=None, stream=None) -> None:
+    import torch
+
+    sl = _host(seq_lens, np.int32)
+    rc = _host(reveal_counts, np.int32)
+    if sl.size != rc.size:
+        raise ValueError("seq_lens and reveal_counts must have num_requests entries")
+    _check(lib().ds_reveal_topk(handle, _dev_ptr(scores, "scores", torch.float32), num_rows, sl.ctypes.data,
+                                rc.ctypes.data, sl.size, _dev_ptr(index_out, "index_out", torch.int32),
+                                _dev_ptr(score_out, "score_out", torch.float32), _stream_ptr(stream)))

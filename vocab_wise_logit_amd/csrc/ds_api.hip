@@ -95,7 +95,7 @@ extern "C" {
 
 const char* ds_last_error(void) { return g_err.c_str(); }
 
-int ds_version(void) { return 100; }
+int ds_version(void) { return 200; }
 
 int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype, int32_t max_rows,
                      int64_t max_positions, int32_t max_requests, int32_t top_k,
@@ -310,6 +310,69 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
         a.w.ncells = (int32_t)(n_rows - c0 < slots ? n_rows - c0 : slots);
         const hipError_t e = ds::launch_greedy_lse(bf16, a, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "greedy kernel launch");
+    }
+    return DS_OK;
+}
+
+
+int ds_reveal_topk(ds_sampler* s, const float* scores, int32_t num_rows, const int32_t* seq_lens,
+                   const int32_t* reveal_counts, int32_t num_requests, int32_t* index_out, float* score_out,
+                   void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    if (num_requests < 1) return fail(DS_ERR_INVALID_ARG, "num_requests must be >= 1");
+    if (num_requests > s->max_requests)
+        return fail(DS_ERR_CAPACITY, "num_requests %d exceeds max_requests %d", num_requests, s->max_requests);
+    if (num_rows < 1) return fail(DS_ERR_INVALID_ARG, "num_rows must be >= 1");
+    if (num_rows > s->max_rows)
+        return fail(DS_ERR_CAPACITY, "num_rows %d exceeds max_rows %d", num_rows, s->max_rows);
+    if (!seq_lens || !reveal_counts) return fail(DS_ERR_INVALID_ARG, "seq_lens and reveal_counts must be non-NULL");
+    int64_t P = 0, total = 0;
+    for (int32_t r = 0; r < num_requests; ++r) {
+        if (seq_lens[r] < 0) return fail(DS_ERR_INVALID_ARG, "seq_lens[%d] = %d is negative", r, seq_lens[r]);
+        const int64_t n = (int64_t)num_rows * seq_lens[r];
+        if (n > INT32_MAX) return fail(DS_ERR_UNSUPPORTED, "request %d has more than 2^31 - 1 cells", r);
+        if (reveal_counts[r] < 0 || reveal_counts[r] > n)
+            return fail(DS_ERR_INVALID_ARG, "reveal_counts[%d] = %d is outside [0, %lld]", r, reveal_counts[r],
+                        (long long)n);
+        if (reveal_counts[r] > ds::kRevealCap)
+            return fail(DS_ERR_UNSUPPORTED, "reveal_counts[%d] = %d exceeds %d", r, reveal_counts[r],
+                        ds::kRevealCap);
+        P += seq_lens[r];
+        total += reveal_counts[r];
+    }
+    if (P > s->max_positions)
+        return fail(DS_ERR_CAPACITY, "sum(seq_lens) %lld exceeds max_positions %lld", (long long)P,
+                    (long long)s->max_positions);
+    if (total == 0) return DS_OK;
+    if (!scores || !index_out) return fail(DS_ERR_INVALID_ARG, "scores and index_out must be non-NULL");
+    if (!aligned(scores, 4) || !aligned(index_out, 4) || (score_out && !aligned(score_out, 4)))
+        return fail(DS_ERR_INVALID_ARG, "scores and outputs must be 4-byte aligned");
+
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    ds::RevealArgs a;
+    a.scores = scores;
+    a.P = P;
+    a.C = num_rows;
+    a.index_out = index_out;
+    a.score_out = score_out;
+    // one launch per group of up to 64 requests, each with its table by value
+    int64_t off = 0, out = 0;
+    for (int32_t r0 = 0; r0 < num_requests; r0 += ds::kMaxRevealPerLaunch) {
+        ds::RevealTable rt;
+        rt.n = 0;
+        for (int32_t r = r0; r < num_requests && rt.n < ds::kMaxRevealPerLaunch; ++r) {
+            rt.T[rt.n] = seq_lens[r];
+            rt.k[rt.n] = reveal_counts[r];
+            rt.off[rt.n] = off;
+            rt.out[rt.n] = out;
+            ++rt.n;
+            off += seq_lens[r];
+            out += reveal_counts[r];
+        }
+        const hipError_t e = ds::launch_reveal_topk(a, rt, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "reveal kernel launch");
     }
     return DS_OK;
 }

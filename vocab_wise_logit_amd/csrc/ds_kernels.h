@@ -81,4 +81,27 @@ int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells);
 
 hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st);
 
+// Confidence reveal: one workgroup per request, its selected cells sorted in LDS.
+constexpr int kRevealThreads = 1024;
+constexpr int kRevealCap = 16384;        // cells one request may reveal
+constexpr int kMaxRevealPerLaunch = 64;  // requests per launch (kernel-argument table)
+
+struct RevealTable {
+    int32_t n;                        // requests in this launch
+    int32_t T[kMaxRevealPerLaunch];   // positions of the request
+    int32_t k[kMaxRevealPerLaunch];   // cells to reveal
+    int64_t off[kMaxRevealPerLaunch]; // first packed position
+    int64_t out[kMaxRevealPerLaunch]; // first output slot
+};
+
+struct RevealArgs {
+    const float* scores;  // [C, P]
+    int64_t P;
+    int32_t C;
+    int32_t* index_out;
+    float* score_out;     // or nullptr
+};
+
+hipError_t launch_reveal_topk(const RevealArgs& a, const RevealTable& rt, hipStream_t st);
+
 }  // namespace ds
