@@ -419,32 +419,40 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
 
     // ids [lo, hi) cover every element of pieces 1 .. nq-2; only the first and the
     // last iteration can hold a partial or missing piece
-    auto group = [&](int it, auto edge_tag) {
-        constexpr bool EDGE = decltype(edge_tag)::value;
-        u32x4 rc[U], ru[U];
+    // raw 16-byte pieces of one group (u only when it is read)
+    struct Raw {
+        u32x4 c[U];
+        u32x4 u[U];
+    };
+    auto load = [&](int it, Raw& R, bool edge) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             const int j = it * NT * U + uu * NT + (int)threadIdx.x;
-            if (!EDGE) {
-                rc[uu] = pc[j];
-                if (use_u) ru[uu] = pu[j];
+            if (!edge) {
+                R.c[uu] = pc[j];
+                if (use_u) R.u[uu] = pu[j];
             } else {
                 const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
-                rc[uu] = u32x4{ninf, ninf, ninf, ninf};
-                ru[uu] = rc[uu];
+                R.c[uu] = u32x4{ninf, ninf, ninf, ninf};
+                R.u[uu] = R.c[uu];
                 if (j < nqi) {
-                    rc[uu] = pc[j];
-                    if (use_u) ru[uu] = pu[j];
+                    R.c[uu] = pc[j];
+                    if (use_u) R.u[uu] = pu[j];
                 }
             }
         }
+    };
+    auto group = [&](int it, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        Raw raw;
+        load(it, raw, EDGE);
         Piece<BF16> P[U];
         float pm[U];
         float gm = kNegInf;
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             const int j = it * NT * U + uu * NT + (int)threadIdx.x;
-            decode_piece<BF16, FIX>(rc[uu], ru[uu], s, use_u, P[uu]);
+            decode_piece<BF16, FIX>(raw.c[uu], raw.u[uu], s, use_u, P[uu]);
             if (EDGE) {
                 const int v0 = vbase + j * EPP;
                 if (v0 < pr.lo || v0 + EPP > pr.hi) {

@@ -53,8 +53,8 @@ struct Row {
     }
 
     // Count the ids whose h is >= x and write them, as (h, id) in register-slot
-    // order, to `list`; entries past kListCap are dropped (the caller checks the
-    // returned count before using the list).
+    // order, to `list`.  Once the count passes kListCap the pass stops: the
+    // caller then only learns that the list overflowed (a count > kListCap).
     __device__ __forceinline__ int count_compact(float x, Entry* list) const {
         int base = 0;
 #pragma unroll
@@ -65,6 +65,7 @@ struct Row {
                 const int o = base + lanes_below(m);
                 if (pred && o < kListCap) list[o] = Entry{h[i], id_of(i)};
                 base += popc(m);
+                if (base > kListCap) break;  // wave-uniform
             }
         }
         __builtin_amdgcn_wave_barrier();
