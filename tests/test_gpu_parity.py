@@ -318,6 +318,48 @@ def test_reveal_rejects_bad_counts():
     assert (idx.cpu() == -7).all()
 
 
+def test_calls_replay_from_a_captured_graph():
+    # ds_sample (both paths) and ds_reveal_topk allocate, synchronise and clear
+    # nothing, so a stream capture of them replays; every replay, with eager work
+    # in between, must equal the eager result bit for bit
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    for w in (synth.omnivoice(n_requests=3), synth.stress(positions=6)):
+        log(f"[gpu] graph capture {w.name}")
+        c = to_dev(w.c)
+        u = to_dev(w.u)
+        with ds.Sampler(w.vocab, w.dtype, max_rows=w.rows, max_positions=w.positions,
+                        max_requests=len(w.seq_lens), vocab_chunks=w.vocab_chunks) as smp:
+            ref = [t.clone() for t in smp.sample(w.request_ids, c, u, w.seq_lens, w.iterations, w.guidance,
+                                                 w.temperature, seed=w.seed)]
+            counts = np.minimum(np.ceil(0.1 * w.rows * w.seq_lens), 16384).astype(np.int32)
+            ref_rev = [t.clone() for t in smp.reveal_topk(ref[1], w.seq_lens, counts)]
+            out = tuple(torch.empty_like(t) for t in ref) + (None,)
+            rev = tuple(torch.empty_like(t) for t in ref_rev)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):  # warm-up on the capture stream
+                smp.sample(w.request_ids, c, u, w.seq_lens, w.iterations, w.guidance, w.temperature,
+                           seed=w.seed, out=out)
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                smp.sample(w.request_ids, c, u, w.seq_lens, w.iterations, w.guidance, w.temperature,
+                           seed=w.seed, out=out)
+                smp.reveal_topk(out[1], w.seq_lens, counts, out=rev)
+            for rep in range(3):
+                for t in out[:2] + rev:
+                    t.fill_(-1)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                for a, b in zip(out[:2] + rev, ref + ref_rev):
+                    assert torch.equal(a, b), f"replay {rep} differs from the eager call"
+            del g
+
+
 def test_invalid_calls_are_rejected_before_launch():
     import torch
 
