@@ -353,7 +353,11 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     // larger than any of them), so the filter is satisfied without locating its
     // exact threshold; otherwise the threshold is above `prune` and is found
     // among them.
-    if (!want_t) {
+    // The first register slot (64 ids spread over the row) predicts an overflow
+    // of the list; such rows (flat next to tau * (Gmax - Gmin)) go straight to
+    // the exact search.  A wrong guess costs time, never the result.
+    const bool fits = popc(ballot(R.h[0] >= prune)) * NE <= kListCap;
+    if (!want_t && fits) {
         const int nb = R.count_compact(prune, list);
         if (nb <= kListCap) {
             n_list = nb;
