@@ -127,7 +127,13 @@ __device__ void reveal_body(const RevealArgs& a, const RevealTable& rt, RevealLD
     const int64_t off = rt.off[r];
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
-    Cells<KPT> cells{a.scores, a.P, off, a.C, T, a.C * T};
+    Cells<KPT> cells;
+    cells.scores = a.scores;
+    cells.P = a.P;
+    cells.off = off;
+    cells.C = a.C;
+    cells.T = T;
+    cells.n = a.C * T;
     cells.load();
 
     // ---- 1. radix select of the k-th largest key

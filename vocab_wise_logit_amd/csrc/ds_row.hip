@@ -12,19 +12,20 @@
 // workgroup ever waits for another.
 //
 // Sampling ([ISSUE] comment on the API shape: top-ratio filter plus Gumbel).
-// While it streams, each wave keeps a bound below which no id can win the
-// Gumbel race: first from its running maximum (an id more than
-// tau * (Gmax - Gmin) below some other id always loses to it), then from the
-// best perturbed score it has drawn so far.  Ids at or above the bound are
-// queued in LDS and scored 64 at a time, one per lane, so the noise costs one
-// Philox block per queued id and nothing for the rest.  The part records its
-// best (score, id, h) and how many ids it queued.  Every id that can win the
-// row's race was queued by its part, so if the parts queued at most top_k ids in
-// all, every id that can win lies inside the top-ratio set and the best of the
-// part winners is the row's winner.  Otherwise (a flat row), when the fallback
-// is forced, or for the threshold output, the merge runs the exact multi-pass
-// path over the row: a radix select of the threshold and a Gumbel pass over
-// every kept id.
+// While it streams, a part keeps a bound below which no id can win the Gumbel
+// race: after its first group every lane scores its own maximum so far and the
+// block adopts the bound of the best score (an id whose h is below
+// (z - Gmax) * tau loses to the id that scored z); every later batch of scores
+// raises it.  Pieces, then ids, at or above the bound are queued in LDS and
+// scored 64 at a time, one per lane, so the noise costs one Philox block per
+// queued id and nothing for the rest.  The part records its best (score, id, h)
+// and how many ids it queued.  Every id that can win the row's race was queued
+// by its part, so if the parts queued at most top_k ids in all, every id that
+// can win lies inside the top-ratio set and the best of the part winners is the
+// row's winner.  Otherwise (a flat row), when the fallback is forced, or for the
+// threshold output, the merge runs the exact path over the row: a radix select
+// of the threshold (two passes over the row when the threshold's first-digit
+// bin fits in LDS) and, without a certificate, a Gumbel pass over every kept id.
 #include <stdint.h>
 
 #include "ds_device.h"
@@ -90,7 +91,6 @@ struct MergeLDS {
     int nkeys;
     Red r;
 };
-
 
 // Block argmax of (z, id, h): larger z, then smaller id.
 __device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Red& r) {
@@ -194,34 +194,38 @@ struct PartRange {
     }
 };
 
-template <bool BF16>
-__device__ __forceinline__ void load_piece(const RowGeom& G, int64_t q, float s, bool use_u, int lo, int hi,
-                                           Piece<BF16>& P) {
-    constexpr int EPP = Piece<BF16>::EPP;
-    const u32x4 cw = G.c16[q];
-    const u32x4 uw = use_u ? G.u16[q] : cw;
-    decode_piece<BF16>(cw, uw, s, use_u, P);
-    const int64_t v0 = q * EPP - G.gbase;
-    if (v0 < lo || v0 + EPP > hi) {
-#pragma unroll
-        for (int i = 0; i < EPP; ++i)
-            if (v0 + i < lo || v0 + i >= hi) P.h[i] = kNegInf;
-    }
-}
-
-// Visit every id of the row: f(v, h).  Used by the exact multi-pass path.
+// Visit every id of the row: f(v, h).  Used by the exact multi-pass path; four
+// pieces per thread are loaded before any is decoded, so that a single
+// workgroup keeps enough loads in flight to stream its row.
 template <bool BF16, typename F>
 __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_u, F&& f) {
     constexpr int EPP = Piece<BF16>::EPP;
+    constexpr int UF = 4;
     const int64_t q0 = G.gbase / EPP;
     const int64_t q1 = (G.gbase + G.V - 1) / EPP;
-    for (int64_t q = q0 + threadIdx.x; q <= q1; q += NT) {
-        Piece<BF16> P;
-        load_piece<BF16>(G, q, s, use_u, 0, G.V, P);
-        const int64_t v0 = q * EPP - G.gbase;
+    for (int64_t qb = q0 + threadIdx.x; qb <= q1; qb += (int64_t)NT * UF) {
+        u32x4 cw[UF], uw[UF];
 #pragma unroll
-        for (int i = 0; i < EPP; ++i)
-            if (v0 + i >= 0 && v0 + i < G.V) f((int)(v0 + i), P.h[i]);
+        for (int i = 0; i < UF; ++i) {
+            const int64_t q = qb + (int64_t)i * NT;
+            cw[i] = u32x4{0u, 0u, 0u, 0u};
+            uw[i] = cw[i];
+            if (q <= q1) {
+                cw[i] = G.c16[q];
+                if (use_u) uw[i] = G.u16[q];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < UF; ++i) {
+            const int64_t q = qb + (int64_t)i * NT;
+            if (q > q1) break;
+            Piece<BF16> P;
+            decode_piece<BF16>(cw[i], uw[i], s, use_u, P);
+            const int64_t v0 = q * EPP - G.gbase;
+#pragma unroll
+            for (int e = 0; e < EPP; ++e)
+                if (v0 + e >= 0 && v0 + e < G.V) f((int)(v0 + e), P.h[e]);
+        }
     }
 }
 
