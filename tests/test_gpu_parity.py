@@ -129,6 +129,20 @@ def test_row_kernel_race_without_threshold(dtype, V, chunks):
     check_sample(w, run_sample(w, threshold=False), oracle.sample_workload(w))
 
 
+def test_row_kernel_extreme_top_k_and_negative_guidance():
+    # top_k = 1 (only the argmax is kept: the race can never certify) and top_k = V
+    # (every id kept: the race always certifies), with a negative guidance scale
+    # and masked ids, where a -inf c with a finite u also gives a NaN before the fix
+    V = 6000
+    for k in (1, V):
+        w = synth.diffusion(f"row_k{k}", seed=40 + k, vocab=V, rows=2, seq_lens=[3, 2], sigma=3.0,
+                            guidance=[-0.5, 1.5], temperature=[0.8, 1.3], top_k=k, vocab_chunks=3,
+                            masked_ids=[7, 4000])
+        ref = oracle.sample_workload(w)
+        for thr in (False, True):
+            check_sample(w, run_sample(w, threshold=thr), ref)
+
+
 def test_row_kernel_flat_rows_take_the_exact_path():
     # nearly flat h at a high temperature: every id can still win, far more than
     # top_k of them, so the merge must locate the threshold itself
