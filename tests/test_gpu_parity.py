@@ -153,6 +153,20 @@ def test_row_kernel_flat_rows_take_the_exact_path():
         check_sample(w, run_sample(w, threshold=thr), ref)
 
 
+def test_row_kernel_flat_rows_kept_and_dropped_race_winners():
+    # flat rows queue more than top_k ids; the race's winner (the oracle's token
+    # with top_k = V, the same noise) is inside the top-ratio set at some cells
+    # and outside it at others, so both ends of the merge's decision are taken
+    kw = dict(seed=22, vocab=8000, rows=1, seq_lens=[40], sigma=0.6, guidance=0.5, temperature=1.2)
+    w = synth.diffusion("flat_kept", **kw)
+    ref = oracle.sample_workload(w)
+    free = oracle.sample_workload(synth.diffusion("flat_all", top_k=8000, **kw))
+    kept = ref.tokens == free.tokens
+    assert kept.any() and not kept.all(), int(kept.sum())
+    for thr in (False, True):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+
+
 def test_row_kernel_small_temperature_and_masked_ids():
     # |h / tau| near 1e5 (the pruning bounds' relative margin) and masked ids
     # with guidance on, where c - u is (-inf) - (-inf)

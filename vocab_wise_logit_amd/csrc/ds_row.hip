@@ -23,9 +23,11 @@
 // by its part, so if the parts queued at most top_k ids in all, every id that
 // can win lies inside the top-ratio set and the best of the part winners is the
 // row's winner.  Otherwise (a flat row), when the fallback is forced, or for the
-// threshold output, the merge runs the exact path over the row: a radix select
-// of the threshold (two passes over the row when the threshold's first-digit
-// bin fits in LDS) and, without a certificate, a Gumbel pass over every kept id.
+// threshold output, the merge runs a radix select of the threshold (two passes
+// over the row when the threshold's first-digit bin fits in LDS).  The race's
+// winner is the argmax over every id, kept or not, so once it is known to be
+// kept it is the row's winner; only when it is not, or without a race, does a
+// Gumbel pass over every kept id follow.
 #include <stdint.h>
 
 #include "ds_device.h"
@@ -748,10 +750,13 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
     // ---- Gumbel-max over the top-ratio set.  Every id that can win was queued by
     // its part; when at most top_k ids were queued they all lie inside the set.
     const int k = top_k;
-    const bool done = raced && queued <= (int64_t)k;
+    // Past that, the race's winner is still the argmax over all ids (an id it did
+    // not score has a smaller key), so it is the answer as soon as it is kept.
+    bool done = raced && queued <= (int64_t)k;
     float t = kNegInf;
     const RowGeom G = row_geom<BF16>(cptr, uptr, use_u, cp.cell, V, nch, w.ppc);
     if (!done || thresholds) t = radix_select_row<BF16>(G, cp.s, use_u, k, sh);
+    done = done || (raced && bz > kNegInf && bh >= t);
     if (!done) {
         // exact pass over the kept ids that can beat the argmax
         const float cthr = __builtin_fmaxf(t, max_bound(M, cp.inv_tau, cp.tau));
