@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "sampled positions/sec + achieved HBM GB/s (% of MI355X peak) per config"
 ROTATE_BYTES = 1 << 30
+SUITE_BUDGET_S = 0.03  # timed work per suite entry
 
 
 # Sources each kernel is built from: a stored counter reading is valid only while
@@ -218,12 +219,32 @@ def launches_per_step(w, kind: str) -> int:
     return 1 if kernel_name(w, kind).startswith(("k_sample_small", "k_reveal")) else 2
 
 
-def bench_one(name: str, steps: int, warmup: int, threshold: bool = False) -> dict:
+def auto_steps(r: "Runner", budget_s: float = SUITE_BUDGET_S) -> tuple:
+    """(steps, warmup) for a suite entry: enough steps for about `budget_s` of
+    timed work, so that short steps are not timed over a few microseconds."""
+    import torch
+
+    for i in range(3):
+        r.step(i)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(10):
+        r.step(i)
+    torch.cuda.synchronize()
+    est = (time.perf_counter() - t) / 10
+    steps = int(min(max(budget_s / max(est, 1e-7), 10), 5000))
+    return steps, max(steps // 5, 3)
+
+
+def bench_one(name: str, steps, warmup, threshold: bool = False) -> dict:
+    """Times one workload; steps=None sizes the run with auto_steps."""
     import torch
 
     kind = name if name in ("draft", "reveal") else "sample"
     w = make_workload(name)
     r = Runner(w, kind, threshold)
+    if steps is None:
+        steps, warmup = auto_steps(r)
     ms_step, ms_kernel, med, p10, p90 = time_runner(r, steps, warmup)
     r.close()
     del r
@@ -240,7 +261,7 @@ def bench_one(name: str, steps: int, warmup: int, threshold: bool = False) -> di
         cfg["workload"] += "+threshold"
         cfg["threshold_out"] = True
     return {"config": cfg, "kernel": kernel_name(w, kind), "launches_per_step": launches_per_step(w, kind),
-            "positions_per_s": cells / (ms_step * 1e-3),
+            "steps": steps, "warmup": warmup, "positions_per_s": cells / (ms_step * 1e-3),
             "ms_per_step": ms_step, "kernel_ms_mean": ms_step, "bracketed_ms_mean": ms_kernel,
             "bracketed_ms_median": med, "bracketed_ms_p10": p10, "bracketed_ms_p90": p90, "algorithmic_bytes": alg,
             "achieved_GBs": achieved, "frac_of_peak": achieved / HBM_PEAK_GBS, "workload_obj": w}
@@ -270,8 +291,8 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="omnivoice")
     ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -319,8 +340,7 @@ def main() -> int:
             if name == args.workload and not thr:
                 res = head
             else:
-                st = max(10, args.steps // 2) if name != "stress" or not thr else 5
-                res = bench_one(name, st, max(3, args.warmup // 2) if st > 5 else 2, threshold=thr)
+                res = bench_one(name, None, None, threshold=thr)
                 res.pop("workload_obj", None)
             entry = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}
             if not thr:

@@ -81,3 +81,23 @@ def test_binding_refuses_to_run_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _binding.lib()
+
+
+def test_request_stage_copies_values_and_refuses_what_does_not_fit():
+    import numpy as np
+
+    st = ds.RequestStage(4)
+    assert st.fill([7, 8], [3, 0], [1, 2], [2.0, 0.5], [0.9, 0.0]) == 2
+    assert st.rid[:2].tolist() == [7, 8] and st.sl[:2].tolist() == [3, 0]
+    assert st.it[:2].tolist() == [1, 2]
+    assert st.gs[:2].tolist() == [2.0, 0.5] and st.tp[:2].tolist() == [np.float32(0.9), 0.0]
+    # the addresses handed to the C call are those of the staged arrays
+    assert st.ptrs[0] == st.rid.ctypes.data and st.ptrs[4] == st.tp.ctypes.data
+    # more requests than the capacity, unequal lengths, no requests, a 2-D array
+    assert st.fill(list(range(5)), [1] * 5, [0] * 5, [1.0] * 5, [1.0] * 5) == -1
+    assert st.fill([1, 2], [1], [0, 0], [1.0, 1.0], [1.0, 1.0]) == -1
+    assert st.fill([], [], [], [], []) == -1
+    assert st.fill([1, 2], np.ones((2, 2), np.int32), [0, 0], [1.0, 1.0], [1.0, 1.0]) == -1
+    assert st.fill_reveal([5, 6, 7], [1, 2, 3]) == 3
+    assert st.sl[:3].tolist() == [5, 6, 7] and st.rc[:3].tolist() == [1, 2, 3]
+    assert st.fill_reveal([5], [1, 2]) == -1

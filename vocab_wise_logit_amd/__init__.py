@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     DSError,
     EXPORTED,
     LIB_PATH,
+    RequestStage,
     ds_greedy_lse,
     ds_last_error,
     ds_reveal_topk,
@@ -58,6 +59,7 @@ class Sampler:
         flags = DS_FLAG_FORCE_FALLBACK if force_fallback else DS_FLAG_NONE
         self._h = ds_sample_create(device, vocab, DS_DTYPE_BF16 if dtype == "bf16" else DS_DTYPE_F32,
                                    max_rows, max_positions, max_requests, top_k, vocab_chunks, flags)
+        self._stage = RequestStage(max_requests)
 
     def close(self) -> None:
         if getattr(self, "_h", None):
@@ -79,18 +81,18 @@ class Sampler:
                out=None, stream=None):
         """Returns (tokens int32 [C, P], logprobs float32 [C, P]) and, with
         threshold=True, the per-cell top-ratio threshold as a third tensor."""
-        import torch
-
-        C_, P = int(c_logits.shape[0]), int(c_logits.shape[1])
-        dev = c_logits.device
+        C_ = int(c_logits.shape[0])
         if out is None:
+            import torch
+
+            P, dev = int(c_logits.shape[1]), c_logits.device
             tokens = torch.empty((C_, P), dtype=torch.int32, device=dev)
             logprobs = torch.empty((C_, P), dtype=torch.float32, device=dev)
             thr = torch.empty((C_, P), dtype=torch.float32, device=dev) if threshold else None
         else:
             tokens, logprobs, thr = out
         ds_sample(self._h, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
-                  temperature, C_, seed, tokens, logprobs, thr, stream)
+                  temperature, C_, seed, tokens, logprobs, thr, stream, stage=self._stage)
         return (tokens, logprobs, thr) if threshold else (tokens, logprobs)
 
     def greedy_lse(self, logits, triples: bool = False, out=None, stream=None):
@@ -115,13 +117,14 @@ class Sampler:
         """scores float32 [C, P] -> (index int32 [sum(reveal_counts)], score float32
         [sum(reveal_counts)]): per request, the flattened indices c * T_r + t of
         its best cells, best first, and their scores."""
-        import torch
-
-        total = int(sum(int(k) for k in reveal_counts))
         if out is None:
+            import torch
+
+            total = int(sum(int(k) for k in reveal_counts))
             idx = torch.empty(max(total, 1), dtype=torch.int32, device=scores.device)[:total]
             val = torch.empty(max(total, 1), dtype=torch.float32, device=scores.device)[:total]
         else:
             idx, val = out
-        ds_reveal_topk(self._h, scores, int(scores.shape[0]), seq_lens, reveal_counts, idx, val, stream)
+        ds_reveal_topk(self._h, scores, int(scores.shape[0]), seq_lens, reveal_counts, idx, val, stream,
+                       stage=self._stage)
         return idx, val

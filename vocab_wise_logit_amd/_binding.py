@@ -64,14 +64,25 @@ def _check(rc: int) -> None:
         raise DSError(rc, lib().ds_last_error().decode())
 
 
+_torch = None
+
+
+def _t():
+    global _torch
+    if _torch is None:
+        import torch
+
+        _torch = torch
+    return _torch
+
+
 def _dev_ptr(t, what: str, dtype=None) -> Optional[int]:
     if t is None:
         return None
-    import torch
-
+    torch = _t()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what} must be a torch tensor on a HIP device")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{what} must live on a HIP device (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
@@ -81,14 +92,18 @@ def _dev_ptr(t, what: str, dtype=None) -> Optional[int]:
 
 
 def _host(a, dtype) -> np.ndarray:
-    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+    if type(a) is np.ndarray and a.dtype == dtype and a.flags.c_contiguous:
+        return a
+    return np.ascontiguousarray(a, dtype=dtype)
 
 
-def _stream_ptr(stream) -> Optional[int]:
+def _stream_ptr(stream, like=None) -> Optional[int]:
+    """The stream handle: the given one, else torch's current stream on the device
+    of tensor `like` (read without building a Stream object)."""
     if stream is None:
-        import torch
-
-        return torch.cuda.current_stream().cuda_stream
+        torch = _t()
+        dev = like.get_device() if like is not None else torch.cuda.current_device()
+        return torch._C._cuda_getCurrentRawStream(dev)
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -114,50 +129,104 @@ def ds_sample_destroy(handle: int) -> None:
     lib().ds_sample_destroy(handle)
 
 
+class RequestStage:
+    """Host arrays for the per-request arguments of ``ds_sample``, allocated once
+    with room for `capacity` requests.  Reading a numpy array's address costs about
+    a microsecond per array, so a sampler copies each call's values into these
+    arrays, whose addresses are read once, instead.  Not for concurrent use."""
+
+    def __init__(self, capacity: int):
+        self.capacity = capacity
+        self.rid = np.zeros(max(capacity, 1), np.int64)
+        self.sl = np.zeros(max(capacity, 1), np.int32)
+        self.it = np.zeros(max(capacity, 1), np.int32)
+        self.gs = np.zeros(max(capacity, 1), np.float32)
+        self.tp = np.zeros(max(capacity, 1), np.float32)
+        self.rc = np.zeros(max(capacity, 1), np.int32)
+        self.ptrs = tuple(a.ctypes.data for a in (self.rid, self.sl, self.it, self.gs, self.tp))
+        self.reveal_ptrs = (self.sl.ctypes.data, self.rc.ctypes.data)
+
+    def fill(self, request_ids, seq_lens, iterations, guidance_scale, temperature) -> int:
+        """Copies the values in; returns the request count, or -1 when they do not
+        fit (more than `capacity` requests, unequal lengths, not one-dimensional)."""
+        try:
+            n = len(request_ids)
+            if not (0 < n <= self.capacity and len(seq_lens) == len(iterations) == len(guidance_scale)
+                    == len(temperature) == n):
+                return -1
+            self.rid[:n] = request_ids
+            self.sl[:n] = seq_lens
+            self.it[:n] = iterations
+            self.gs[:n] = guidance_scale
+            self.tp[:n] = temperature
+        except (TypeError, ValueError):
+            return -1
+        return n
+
+    def fill_reveal(self, seq_lens, reveal_counts) -> int:
+        """As `fill`, for the arguments of ``ds_reveal_topk``."""
+        try:
+            n = len(seq_lens)
+            if not (0 < n <= self.capacity and len(reveal_counts) == n):
+                return -1
+            self.sl[:n] = seq_lens
+            self.rc[:n] = reveal_counts
+        except (TypeError, ValueError):
+            return -1
+        return n
+
+
 def ds_sample(handle: int, request_ids: Sequence[int], c_logits, u_logits, seq_lens: Sequence[int],
               iterations: Sequence[int], guidance_scale: Sequence[float],
               temperature: Sequence[float], num_rows: int, seed: int, tokens_out, logprobs_out,
-              threshold_out=None, stream=None) -> None:
-    import torch
-
-    rid = _host(request_ids, np.int64)
-    sl = _host(seq_lens, np.int32)
-    it = _host(iterations, np.int32)
-    gs = _host(guidance_scale, np.float32)
-    tp = _host(temperature, np.float32)
-    n = rid.size
-    if not (sl.size == it.size == gs.size == tp.size == n):
-        raise ValueError("per-request arrays must all have num_requests entries")
+              threshold_out=None, stream=None, stage: Optional[RequestStage] = None) -> None:
+    torch = _t()
+    n = stage.fill(request_ids, seq_lens, iterations, guidance_scale, temperature) if stage is not None else -1
+    if n > 0:
+        prid, psl, pit, pgs, ptp = stage.ptrs
+    else:
+        rid = _host(request_ids, np.int64)
+        sl = _host(seq_lens, np.int32)
+        it = _host(iterations, np.int32)
+        gs = _host(guidance_scale, np.float32)
+        tp = _host(temperature, np.float32)
+        n = rid.size
+        if not (sl.size == it.size == gs.size == tp.size == n):
+            raise ValueError("per-request arrays must all have num_requests entries")
+        prid, psl, pit, pgs, ptp = (a.ctypes.data for a in (rid, sl, it, gs, tp))
     cp = _dev_ptr(c_logits, "c_logits")
     up = _dev_ptr(u_logits, "u_logits")
-    _check(lib().ds_sample(handle, rid.ctypes.data, cp, up, sl.ctypes.data, it.ctypes.data,
-                           gs.ctypes.data, tp.ctypes.data, n, num_rows, seed & (2**64 - 1),
+    _check(lib().ds_sample(handle, prid, cp, up, psl, pit, pgs, ptp, n, num_rows, seed & (2**64 - 1),
                            _dev_ptr(tokens_out, "tokens_out", torch.int32),
                            _dev_ptr(logprobs_out, "logprobs_out", torch.float32),
                            _dev_ptr(threshold_out, "threshold_out", torch.float32),
-                           _stream_ptr(stream)))
+                           _stream_ptr(stream, c_logits)))
 
 
 def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_out,
                   triples_out=None, stream=None) -> None:
-    import torch
-
+    torch = _t()
     _check(lib().ds_greedy_lse(handle, _dev_ptr(logits, "logits"), n_rows,
                                _dev_ptr(token_out, "token_out", torch.int32),
                                _dev_ptr(lse_out, "lse_out", torch.float32),
                                _dev_ptr(logprob_out, "logprob_out", torch.float32),
                                _dev_ptr(triples_out, "triples_out", torch.float32),
-                               _stream_ptr(stream)))
+                               _stream_ptr(stream, logits)))
 
 
 def ds_reveal_topk(handle: int, scores, num_rows: int, seq_lens: Sequence[int],
-                   reveal_counts: Sequence[int], index_out, score_out=None, stream=None) -> None:
-    import torch
-
-    sl = _host(seq_lens, np.int32)
-    rc = _host(reveal_counts, np.int32)
-    if sl.size != rc.size:
-        raise ValueError("seq_lens and reveal_counts must have num_requests entries")
-    _check(lib().ds_reveal_topk(handle, _dev_ptr(scores, "scores", torch.float32), num_rows, sl.ctypes.data,
-                                rc.ctypes.data, sl.size, _dev_ptr(index_out, "index_out", torch.int32),
-                                _dev_ptr(score_out, "score_out", torch.float32), _stream_ptr(stream)))
+                   reveal_counts: Sequence[int], index_out, score_out=None, stream=None,
+                   stage: Optional[RequestStage] = None) -> None:
+    torch = _t()
+    n = stage.fill_reveal(seq_lens, reveal_counts) if stage is not None else -1
+    if n > 0:
+        psl, prc = stage.reveal_ptrs
+    else:
+        sl = _host(seq_lens, np.int32)
+        rc = _host(reveal_counts, np.int32)
+        if sl.size != rc.size:
+            raise ValueError("seq_lens and reveal_counts must have num_requests entries")
+        n, psl, prc = sl.size, sl.ctypes.data, rc.ctypes.data
+    _check(lib().ds_reveal_topk(handle, _dev_ptr(scores, "scores", torch.float32), num_rows, psl, prc, n,
+                                _dev_ptr(index_out, "index_out", torch.int32),
+                                _dev_ptr(score_out, "score_out", torch.float32), _stream_ptr(stream, scores)))

@@ -228,6 +228,25 @@ __device__ __forceinline__ int wave_argmax(float& z, int& id) {
     return (int)__builtin_ctzll(m);
 }
 
+// Inclusive prefix sum over lanes 0..lane: four shifted adds inside each row of
+// 16 lanes (a lane with no source lane reads 0), then each row adds the totals
+// of the rows below it, read into scalar registers.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xF, 0xF, true);
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r01 = r0 + __builtin_amdgcn_readlane(x, 31);
+    const int r012 = r01 + __builtin_amdgcn_readlane(x, 47);
+    const int row = lane_id() >> 4;
+    return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r01 : r012);
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 // Number of set bits of m in lanes below this one.

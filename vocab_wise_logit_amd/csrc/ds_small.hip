@@ -7,12 +7,15 @@
 //      do?": guidance 0 never reads u), row max, smallest-id argmax, log-sum-exp;
 //   2. greedy cells (temperature 0): token = argmax, logprob = max - LSE;
 //   3. sampled cells: the exact top_k-th largest h ([ISSUE] top-ratio filter),
-//      found by counting ids above pivots with wave ballots; the ids above the
-//      final pivot are compacted into a per-wave LDS list, so refinement runs on a
-//      few registers instead of the whole row;
+//      found by counting ids above pivots; the ids above the final pivot are
+//      compacted into a per-wave LDS list (per-lane counts and a wave prefix
+//      sum), so refinement runs on a few registers instead of the whole row;
 //   4. Gumbel-max ([ISSUE]) over the kept ids that can still win: an id whose
 //      h/tau + max-noise is below the argmax's h/tau + min-noise never wins, so
 //      only ids with h >= max(t, M - tau * (Gmax - Gmin)) draw Philox noise.
+//      When more than top_k ids can win, all of them are raced before any
+//      threshold is located: the winner stands if fewer than top_k ids have a
+//      larger h, and step 3 runs only when it does not.
 // Ties: smallest id for the greedy argmax and for exact Gumbel ties ([DRAFT]
 // "Design and invariants" rule, applied to every decision).
 #include <stdint.h>
@@ -52,24 +55,30 @@ struct Row {
         return n;
     }
 
-    // Count the ids whose h is >= x and write them, as (h, id) in register-slot
-    // order, to `list`.  Once the count passes kListCap the pass stops: the
-    // caller then only learns that the list overflowed (a count > kListCap).
-    __device__ __forceinline__ int count_compact(float x, Entry* list) const {
-        int base = 0;
+    // Count the ids whose h is >= x and, if there are at most kListCap of them,
+    // write them to `list` as (h, id).  Each lane counts its own ids, a wave
+    // prefix sum places each lane's run, and the lane writes its ids there in
+    // register order.  Every lane stores every slot, the ids below x to its own
+    // spare entry past kListCap, so the pass has no per-slot ballot or branch.
+    // Returns the count.
+    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane) const {
+        int mine = 0;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const bool pred = h[i] >= x;
-            const uint64_t m = ballot(pred);
-            if (m) {
-                const int o = base + lanes_below(m);
-                if (pred && o < kListCap) list[o] = Entry{h[i], id_of(i)};
-                base += popc(m);
-                if (base > kListCap) break;  // wave-uniform
+        for (int i = 0; i < NE; ++i) mine += (h[i] >= x) ? 1 : 0;
+        const int incl = wave_incl_scan(mine);
+        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (total <= kListCap) {
+            const int spare = kListCap + lane;
+            int o = incl - mine;  // < total for every id this lane writes
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                const bool p = h[i] >= x;
+                list[p ? o : spare] = Entry{h[i], id_of(i)};
+                o += p ? 1 : 0;
             }
         }
         __builtin_amdgcn_wave_barrier();
-        return base;
+        return total;
     }
 };
 
@@ -187,6 +196,17 @@ __device__ __forceinline__ void gumbel_list(Entry* list, int n, float cthr, bool
     }
 }
 
+// Number of list entries whose h is above x.  The list has kWave spare entries
+// past kListCap, so every lane reads in bounds; entries past n are ignored.
+__device__ __forceinline__ int count_list_above(const Entry* list, int n, float x, int lane) {
+    int c = 0;
+    for (int b0 = 0; b0 < n; b0 += kWave) {
+        const float hv = list[b0 + lane].h;
+        c += popc(ballot(b0 + lane < n && hv > x));
+    }
+    return c;
+}
+
 // Load one row's dwords through a buffer resource that covers exactly the row:
 // the hardware range check returns 0 for dwords past it, so no load is branched
 // or masked.  Slot j of lane l is dword 64 j + l.
@@ -202,7 +222,7 @@ template <bool BF16, int NS>
 __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const ReqTable& rq) {
     using R_t = Row<BF16, NS>;
     constexpr int NE = R_t::NE;
-    __shared__ Entry s_list[kWavesPerBlock][kListCap];
+    __shared__ Entry s_list[kWavesPerBlock][kListCap + kWave];  // + one spare entry per lane
 
     // every per-cell quantity below is wave-uniform (scalar registers); the grid
     // is (positions / 4, rows) with rows beyond 65535 folded into z
@@ -348,22 +368,35 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     float t = kNegInf;
     float cthr = prune;  // draw noise for list entries with h >= cthr
     int n_list = -1;     // entries in the LDS list (all ids >= the list floor), or -1
+    float bz = kNegInf, bh = kNegInf;
+    int be = 0x7FFFFFFF;
+    bool decided = false;  // (bz, be, bh) is the row's winner, wave-uniform
     // Fast path: the ids that can still win.  If at most top_k of them reach
     // `prune`, they all lie inside the top-ratio set (fewer than top_k ids are
     // larger than any of them), so the filter is satisfied without locating its
-    // exact threshold; otherwise the threshold is above `prune` and is found
-    // among them.
-    // The first register slot (64 ids spread over the row) predicts an overflow
-    // of the list; such rows (flat next to tau * (Gmax - Gmin)) go straight to
-    // the exact search.  A wrong guess costs time, never the result.
-    const bool fits = popc(ballot(R.h[0] >= prune)) * NE <= kListCap;
-    if (!want_t && fits) {
-        const int nb = R.count_compact(prune, list);
+    // exact threshold.  Otherwise they are all raced: the winner is the argmax
+    // over every id, and it is inside the set when fewer than top_k ids have a
+    // larger h (those all lie above it, so all are listed).  Only when it is not
+    // is the threshold found among them and the race rerun over the kept ids.
+    // Rows flat next to tau * (Gmax - Gmin) overflow the list and take the exact
+    // search below.
+    if (!want_t) {
+        const int nb = R.count_compact(prune, list, lane);
         if (nb <= kListCap) {
             n_list = nb;
             if (nb > k) {
-                t = list_kth(list, nb, k, prune, M, lane);
-                cthr = __builtin_fmaxf(t, prune);
+                gumbel_list(list, nb, prune, false, inv_tau, nk, lane, bz, be, bh);
+                const int wl = wave_argmax(bz, be);
+                bh = readlane_f(bh, wl);
+                if (count_list_above(list, nb, bh, lane) < k) {
+                    decided = true;
+                } else {
+                    bz = kNegInf;
+                    bh = kNegInf;
+                    be = 0x7FFFFFFF;
+                    t = list_kth(list, nb, k, prune, M, lane);
+                    cthr = __builtin_fmaxf(t, prune);
+                }
             }
         }
     }
@@ -388,7 +421,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
         float hi = M;
         int c_hi = -1;
         for (int tries = 0; tries < 8; ++tries) {
-            const int c_lo = R.count_compact(lo, list);
+            const int c_lo = R.count_compact(lo, list, lane);
             if (c_lo >= k && c_lo <= kListCap) {
                 t = list_kth(list, c_lo, k, lo, M, lane);
                 n_list = c_lo;
@@ -434,9 +467,9 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     }
 
     // ------------------------------------------------------------ Gumbel-max
-    float bz = kNegInf, bh = kNegInf;
-    int be = 0x7FFFFFFF;
-    if (n_list >= 0) {
+    if (decided) {
+        // the race above settled it
+    } else if (n_list >= 0) {
         gumbel_list(list, n_list, cthr, cthr > prune, inv_tau, nk, lane, bz, be, bh);
     } else {
         // every valid id with h >= cthr, straight from the row registers (rare:
@@ -461,8 +494,10 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
             }
         }
     }
-    const int wl = wave_argmax(bz, be);
-    bh = readlane_f(bh, wl);
+    if (!decided) {
+        const int wl = wave_argmax(bz, be);
+        bh = readlane_f(bh, wl);
+    }
     if (lane == 0) {
         a.tokens[cell] = be;
         a.logprobs[cell] = bh - lse;
