@@ -4,8 +4,9 @@
 // and holds the whole guided row h[0..V) in VGPRs (dword slots of two bf16 or one
 // f32 per lane).  Everything after the load is register / LDS work:
 //   1. h = CFG combine ([ISSUE] comment on the API shape; [PR] "What does this PR
-//      do?": guidance 0 never reads u), row max, smallest-id argmax, log-sum-exp;
-//   2. greedy cells (temperature 0): token = argmax, logprob = max - LSE;
+//      do?": guidance 0 never reads u), row max, log-sum-exp;
+//   2. greedy cells (temperature 0): token = smallest-id argmax, logprob =
+//      max - LSE;
 //   3. sampled cells: the exact top_k-th largest h ([ISSUE] top-ratio filter),
 //      found by counting ids above pivots; the ids above the final pivot are
 //      compacted into a per-wave LDS list (per-lane counts and a wave prefix
@@ -294,35 +295,11 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
         }
     }
 
-    // ------------------------------------------------ max, argmax, log-sum-exp
+    // ---------------------------------------------------- max, log-sum-exp
     float mx = R.h[0];
 #pragma unroll
     for (int i = 1; i < NE; ++i) mx = __builtin_fmaxf(mx, R.h[i]);
     const float M = wave_max(mx);
-
-    // smallest id attaining M: ids grow with the register index inside a lane,
-    // so the first register slot (across lanes) holding M decides.
-    int am = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        if (BF16) {
-            const uint64_t m0 = ballot(R.h[2 * j] == M);
-            const uint64_t m1 = ballot(R.h[2 * j + 1] == M);
-            if (m0 | m1) {
-                const int a0 = m0 ? 2 * (j * kWave + (int)__builtin_ctzll(m0)) : 0x7FFFFFFF;
-                const int a1 = m1 ? 2 * (j * kWave + (int)__builtin_ctzll(m1)) + 1 : 0x7FFFFFFF;
-                am = (a0 < a1 ? a0 : a1) - (R.ebase & 1);  // ebase & 1 == parity
-                break;
-            }
-        } else {
-            const uint64_t m0 = ballot(R.h[j] == M);
-            if (m0) {
-                am = j * kWave + (int)__builtin_ctzll(m0);
-                break;
-            }
-        }
-    }
-    am = __builtin_amdgcn_readfirstlane(am);
 
     const float mL = M * kLog2e;
     float acc = 0.0f;
@@ -343,6 +320,31 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     const float lse = M + (log2f(S) - err) * kLn2;
 
     if (tau == 0.0f) {
+        // Only greedy cells need the argmax of h (sampled cells take the Gumbel
+        // winner): the smallest id attaining M.  Ids grow with the register index
+        // inside a lane, so the first register slot (across lanes) holding M
+        // decides.
+        int am = 0x7FFFFFFF;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (BF16) {
+                const uint64_t m0 = ballot(R.h[2 * j] == M);
+                const uint64_t m1 = ballot(R.h[2 * j + 1] == M);
+                if (m0 | m1) {
+                    const int a0 = m0 ? 2 * (j * kWave + (int)__builtin_ctzll(m0)) : 0x7FFFFFFF;
+                    const int a1 = m1 ? 2 * (j * kWave + (int)__builtin_ctzll(m1)) + 1 : 0x7FFFFFFF;
+                    am = (a0 < a1 ? a0 : a1) - (R.ebase & 1);  // ebase & 1 == parity
+                    break;
+                }
+            } else {
+                const uint64_t m0 = ballot(R.h[j] == M);
+                if (m0) {
+                    am = j * kWave + (int)__builtin_ctzll(m0);
+                    break;
+                }
+            }
+        }
+        am = __builtin_amdgcn_readfirstlane(am);
         if (lane == 0) {
             a.tokens[cell] = am;
             a.logprobs[cell] = M - lse;
