@@ -106,14 +106,17 @@ def make_workload(name: str):
 class Runner:
     """Device copies of one workload and a sampler handle; `step(i)` issues one
     call on rotating buffers (asking for the top-ratio thresholds too when
-    `threshold` is set)."""
+    `threshold` is set).  For sampling workloads, `mode` picks the entry point:
+    "eager" calls ds_sample, "device_params" calls ds_sample_device_params with
+    the per-request parameters in device memory, and "graph" replays a HIP graph
+    holding that call (one captured graph per buffer set)."""
 
-    def __init__(self, w, kind: str, threshold: bool = False):
+    def __init__(self, w, kind: str, threshold: bool = False, mode: str = "eager"):
         import torch
 
         import vocab_wise_logit_amd as ds
 
-        self.w, self.kind = w, kind
+        self.w, self.kind, self.mode = w, kind, mode
         if kind == "reveal":
             x = torch.from_numpy(np.ascontiguousarray(w.scores)).cuda()
             per_set = x.numel() * x.element_size()
@@ -152,6 +155,30 @@ class Runner:
                         torch.empty(shape, dtype=torch.float32, device="cuda"),
                         torch.empty(shape, dtype=torch.float32, device="cuda") if threshold else None)
             self.cells = w.cells
+            if mode != "eager":
+                self.prm = (torch.tensor(np.asarray(w.request_ids, np.int64), device="cuda"),
+                            torch.tensor(np.asarray(w.seq_lens, np.int32), device="cuda"),
+                            torch.tensor(np.asarray(w.iterations, np.int32), device="cuda"),
+                            torch.tensor(np.asarray(w.guidance, np.float32), device="cuda"),
+                            torch.tensor(np.asarray(w.temperature, np.float32), device="cuda"))
+            if mode == "graph":
+                self.graphs = []
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    self._dev_call(0)
+                torch.cuda.current_stream().wait_stream(side)
+                for k in range(self.n_sets):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        self._dev_call(k)
+                    self.graphs.append(g)
+                torch.cuda.synchronize()
+
+    def _dev_call(self, s: int) -> None:
+        w = self.w
+        self.smp.sample_device_params(self.prm[0], self.c[s], self.u[s] if self.u else None, *self.prm[1:],
+                                      seed=w.seed, threshold=self.out[2] is not None, out=self.out)
 
     def step(self, i: int) -> None:
         s = i % self.n_sets
@@ -160,12 +187,17 @@ class Runner:
             self.smp.reveal_topk(self.x[s], w.seq_lens, w.reveal_counts, out=self.out)
         elif self.kind == "draft":
             self.smp.greedy_lse(self.x[s], out=self.out)
+        elif self.mode == "graph":
+            self.graphs[s].replay()
+        elif self.mode == "device_params":
+            self._dev_call(s)
         else:
             self.smp.sample(w.request_ids, self.c[s], self.u[s] if self.u else None, w.seq_lens,
                             w.iterations, w.guidance, w.temperature, seed=w.seed,
                             threshold=self.out[2] is not None, out=self.out)
 
     def close(self):
+        self.graphs = None
         self.smp.close()
 
 
@@ -236,13 +268,13 @@ def auto_steps(r: "Runner", budget_s: float = SUITE_BUDGET_S) -> tuple:
     return steps, max(steps // 5, 3)
 
 
-def bench_one(name: str, steps, warmup, threshold: bool = False) -> dict:
+def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "eager") -> dict:
     """Times one workload; steps=None sizes the run with auto_steps."""
     import torch
 
     kind = name if name in ("draft", "reveal") else "sample"
     w = make_workload(name)
-    r = Runner(w, kind, threshold)
+    r = Runner(w, kind, threshold, mode)
     if steps is None:
         steps, warmup = auto_steps(r)
     ms_step, ms_kernel, med, p10, p90 = time_runner(r, steps, warmup)
@@ -260,7 +292,12 @@ def bench_one(name: str, steps, warmup, threshold: bool = False) -> dict:
     if threshold:
         cfg["workload"] += "+threshold"
         cfg["threshold_out"] = True
-    return {"config": cfg, "kernel": kernel_name(w, kind), "launches_per_step": launches_per_step(w, kind),
+    kname = kernel_name(w, kind)
+    if mode != "eager":
+        cfg["workload"] += "+" + mode
+        cfg["entry_point"] = "ds_sample_device_params" + (" in a replayed HIP graph" if mode == "graph" else "")
+        kname = kname.replace("k_sample_small", "k_sample_small_dev")
+    return {"config": cfg, "kernel": kname, "launches_per_step": launches_per_step(w, kind),
             "steps": steps, "warmup": warmup, "positions_per_s": cells / (ms_step * 1e-3),
             "ms_per_step": ms_step, "kernel_ms_mean": ms_step, "bracketed_ms_mean": ms_kernel,
             "bracketed_ms_median": med, "bracketed_ms_p10": p10, "bracketed_ms_p90": p90, "algorithmic_bytes": alg,
@@ -336,14 +373,17 @@ def main() -> int:
         # output requested (it needs the exact k-th largest h of every row)
         runs = [(n, False) for n in ("tiny", "omnivoice", "mixed", "draft", "stress", "reveal")]
         runs += [("omnivoice", True), ("stress", True)]
-        for name, thr in runs:
-            if name == args.workload and not thr:
+        runs = [(n, thr, "eager") for n, thr in runs]
+        # the fixed-shape entry point with device-resident parameters, called and replayed
+        runs += [("omnivoice", False, "device_params"), ("omnivoice", False, "graph")]
+        for name, thr, mode in runs:
+            if name == args.workload and not thr and mode == "eager":
                 res = head
             else:
-                res = bench_one(name, None, None, threshold=thr)
+                res = bench_one(name, None, None, threshold=thr, mode=mode)
                 res.pop("workload_obj", None)
             entry = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}
-            if not thr:
+            if not thr and mode == "eager":
                 entry["traffic"] = stored_traffic(name)
             per_config[res["config"]["workload"]] = entry
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)

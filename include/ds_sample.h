@@ -8,7 +8,8 @@
  *
  * Sources, cited by page title and section:
  *   [ISSUE] mstar issue "Sampler support for discrete diffusion" -- opening
- *           request and the comment on the API shape.
+ *           request, the comment on the API shape, and the comment measuring
+ *           graphs at batch 1 and batch 8.
  *   [PR]    mstar PR "Add a sampler resource for discrete diffusion" -- section
  *           "What does this PR do?" (the sample(request_ids, c_logits, u_logits,
  *           seq_lens, iterations) contract).
@@ -132,6 +133,51 @@ int ds_sample(ds_sampler *s, const int64_t *request_ids, const void *c_logits,
               const float *guidance_scale, const float *temperature, int32_t num_requests,
               int32_t num_rows, uint64_t seed, int32_t *tokens_out, float *logprobs_out,
               float *threshold_out, void *stream);
+
+/*
+ * ds_sample_device_params -- ds_sample with a fixed launch shape and the
+ * per-request parameters in device memory, for a call captured once in a HIP
+ * graph and replayed while the batch changes: the GPU reads the parameters when
+ * the call runs, so updating the arrays between replays (a new iteration, other
+ * lengths, guidance or temperature) changes what the next replay computes.  The
+ * pages capture their sampler in graphs and pad the batch to the captured shape
+ * ([DRAFT] "Design and invariants": graph pad/unpad keeps the per-row results),
+ * and graphs pay off where launch overhead dominates, at batch 1 ([ISSUE],
+ * comment measuring graphs at batch 1 and batch 8).
+ *
+ * Same computation and outputs as ds_sample, cell for cell, for valid values.
+ * The packed layout is [C, positions, V] with `positions` fixed at capture:
+ * request r owns positions [off_r, off_r + seq_lens[r]) as in ds_sample, the
+ * positions from sum(seq_lens) to `positions` are padding, and their outputs are
+ * not written.
+ *
+ *   request_ids, seq_lens, iterations, guidance_scale, temperature
+ *                  device arrays [num_requests], aligned to their element size,
+ *                  read on the GPU when the call runs.  A negative length counts
+ *                  as 0; lengths past `positions` are cut there.  A guidance scale
+ *                  that is not finite, or any scale when u_logits is NULL, counts
+ *                  as 0.  A temperature that is not a positive finite number
+ *                  samples greedily.  (ds_sample rejects such values instead.)
+ *   c_logits       device [C, positions, V]; alignment as in ds_sample.
+ *   u_logits       device, same layout, or NULL (then every request is unguided).
+ *   num_requests   1 .. min(64, max_requests); pad with zero-length requests.
+ *   num_rows       C, 1 .. max_rows.
+ *   positions      1 .. min(max_positions, 2^24): the row stride of the layout and
+ *                  the extent of the launch.
+ *   seed, tokens_out [C, positions], logprobs_out [C, positions],
+ *   threshold_out [C, positions] or NULL, stream: as in ds_sample.
+ * Only vocabularies the wave-per-cell kernel holds in registers are supported
+ * (V <= 2046 bf16, V <= 2048 f32); others return DS_ERR_UNSUPPORTED.  The
+ * handle's DS_FLAG_FORCE_FALLBACK does not apply.  Returns DS_OK,
+ * DS_ERR_INVALID_ARG, DS_ERR_CAPACITY, DS_ERR_UNSUPPORTED or DS_ERR_HIP; the
+ * host-side checks run before anything is enqueued.
+ */
+int ds_sample_device_params(ds_sampler *s, const int64_t *request_ids, const void *c_logits,
+                            const void *u_logits, const int32_t *seq_lens, const int32_t *iterations,
+                            const float *guidance_scale, const float *temperature,
+                            int32_t num_requests, int32_t num_rows, int64_t positions, uint64_t seed,
+                            int32_t *tokens_out, float *logprobs_out, float *threshold_out,
+                            void *stream);
 
 /*
  * ds_greedy_lse -- draft greedy reduction of plain logit rows ([DRAFT]).

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     out = os.popen(f"nm -D --defined-only {ds.LIB_PATH}").read()
     exported = set(re.findall(r" T (ds_\w+)", out))
     assert set(declared_functions()) <= exported
-    assert ds.ds_version() == 200
+    assert ds.ds_version() == 300
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -63,6 +63,9 @@ def test_calls_on_a_null_handle_fail_cleanly():
     rc = L.ds_sample(None, None, None, None, None, None, None, None, 1, 1, 0, None, None, None, None)
     assert rc == ds.DS_ERR_INVALID_ARG
     assert "sampler is NULL" in ds.ds_last_error()
+    rc = L.ds_sample_device_params(None, None, None, None, None, None, None, None, 1, 1, 1, 0, None, None, None,
+                                   None)
+    assert rc == ds.DS_ERR_INVALID_ARG and "sampler is NULL" in ds.ds_last_error()
     rc = L.ds_greedy_lse(None, None, 1, None, None, None, None, None)
     assert rc == ds.DS_ERR_INVALID_ARG
     rc = L.ds_reveal_topk(None, None, 1, None, None, 1, None, None, None)

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     ds_sample,
     ds_sample_create,
     ds_sample_destroy,
+    ds_sample_device_params,
     ds_version,
     lib,
 )
@@ -93,6 +94,26 @@ class Sampler:
             tokens, logprobs, thr = out
         ds_sample(self._h, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
                   temperature, C_, seed, tokens, logprobs, thr, stream, stage=self._stage)
+        return (tokens, logprobs, thr) if threshold else (tokens, logprobs)
+
+    def sample_device_params(self, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
+                             temperature, seed: int = 0, threshold: bool = False, out=None, stream=None):
+        """``sample`` with the per-request parameters as device tensors, read when
+        the call runs (so a captured graph replays with their current values), and
+        a fixed layout of c_logits.shape[1] positions: those past sum(seq_lens)
+        are padding and their outputs are left as they were."""
+        C_ = int(c_logits.shape[0])
+        if out is None:
+            import torch
+
+            P, dev = int(c_logits.shape[1]), c_logits.device
+            tokens = torch.empty((C_, P), dtype=torch.int32, device=dev)
+            logprobs = torch.empty((C_, P), dtype=torch.float32, device=dev)
+            thr = torch.empty((C_, P), dtype=torch.float32, device=dev) if threshold else None
+        else:
+            tokens, logprobs, thr = out
+        ds_sample_device_params(self._h, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
+                                temperature, C_, seed, tokens, logprobs, thr, stream)
         return (tokens, logprobs, thr) if threshold else (tokens, logprobs)
 
     def greedy_lse(self, logits, triples: bool = False, out=None, stream=None):

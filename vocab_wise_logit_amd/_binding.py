@@ -1,7 +1,8 @@
 """ctypes binding of libdssample.so: argument marshalling only.
 
 Functions carry the C entry points' names (ds_sample_create, ds_sample,
-ds_greedy_lse, ds_reveal_topk, ds_sample_destroy, ds_last_error, ds_version).  Device buffers are
+ds_sample_device_params, ds_greedy_lse, ds_reveal_topk, ds_sample_destroy,
+ds_last_error, ds_version).  Device buffers are
 torch tensors on a HIP device (torch supplies memory and streams); per-request
 arrays are host sequences.  Every computation happens in the HIP library; when the
 library is missing the calls raise instead of falling back to anything else.
@@ -21,8 +22,8 @@ DS_DTYPE_F32, DS_DTYPE_BF16 = 0, 1
 DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY, DS_ERR_HIP = range(6)
 DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK = 0, 1
 
-EXPORTED = ("ds_sample_create", "ds_sample", "ds_greedy_lse", "ds_reveal_topk", "ds_sample_destroy",
-            "ds_last_error", "ds_version")
+EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_greedy_lse", "ds_reveal_topk",
+            "ds_sample_destroy", "ds_last_error", "ds_version")
 
 _lib = None
 
@@ -45,6 +46,8 @@ def lib():
         L.ds_sample_create.argtypes = [C.POINTER(P), C.c_int, I32, I32, I32, I64, I32, I32, I32, U32]
         L.ds_sample.restype = C.c_int
         L.ds_sample.argtypes = [P, P, P, P, P, P, P, P, I32, I32, U64, P, P, P, P]
+        L.ds_sample_device_params.restype = C.c_int
+        L.ds_sample_device_params.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I64, U64, P, P, P, P]
         L.ds_greedy_lse.restype = C.c_int
         L.ds_greedy_lse.argtypes = [P, P, I64, P, P, P, P, P]
         L.ds_reveal_topk.restype = C.c_int
@@ -201,6 +204,30 @@ def ds_sample(handle: int, request_ids: Sequence[int], c_logits, u_logits, seq_l
                            _dev_ptr(logprobs_out, "logprobs_out", torch.float32),
                            _dev_ptr(threshold_out, "threshold_out", torch.float32),
                            _stream_ptr(stream, c_logits)))
+
+
+def ds_sample_device_params(handle: int, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
+                            temperature, num_rows: int, seed: int, tokens_out, logprobs_out,
+                            threshold_out=None, stream=None) -> None:
+    """Per-request parameters are device tensors of num_requests entries (int64
+    ids, int32 lengths and iterations, float32 guidance and temperature); the
+    packed layout's positions are c_logits.shape[1]."""
+    torch = _t()
+    if not isinstance(request_ids, torch.Tensor):
+        raise TypeError("request_ids must be a device tensor")
+    n = int(request_ids.numel())
+    for t, what in ((seq_lens, "seq_lens"), (iterations, "iterations"), (guidance_scale, "guidance_scale"),
+                    (temperature, "temperature")):
+        if not isinstance(t, torch.Tensor) or int(t.numel()) != n:
+            raise ValueError(f"{what} must be a device tensor with as many entries as request_ids")
+    _check(lib().ds_sample_device_params(
+        handle, _dev_ptr(request_ids, "request_ids", torch.int64), _dev_ptr(c_logits, "c_logits"),
+        _dev_ptr(u_logits, "u_logits"), _dev_ptr(seq_lens, "seq_lens", torch.int32),
+        _dev_ptr(iterations, "iterations", torch.int32), _dev_ptr(guidance_scale, "guidance_scale", torch.float32),
+        _dev_ptr(temperature, "temperature", torch.float32), n, num_rows, int(c_logits.shape[1]),
+        seed & (2**64 - 1), _dev_ptr(tokens_out, "tokens_out", torch.int32),
+        _dev_ptr(logprobs_out, "logprobs_out", torch.float32),
+        _dev_ptr(threshold_out, "threshold_out", torch.float32), _stream_ptr(stream, c_logits)))
 
 
 def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_out,

@@ -6,7 +6,8 @@
 // picks the path: one wavefront per cell when the row fits in registers;
 // otherwise a parts kernel (one workgroup per vocabulary part of a row) and a
 // merge kernel (one per row), in batches of rows that fit the handle's record
-// workspace.
+// workspace.  ds_sample_device_params is the fixed-shape variant whose
+// per-request parameters stay in device memory, for graph replay.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -82,12 +83,19 @@ struct DeviceGuard {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-bool use_small_kernel(const ds_sampler* s) {
-    if (s->flags & DS_FLAG_FORCE_FALLBACK) return false;
+// The row fits the wave-per-cell kernel's registers.
+bool small_fits(const ds_sampler* s) {
     const bool bf16 = s->dtype == DS_DTYPE_BF16;
     const int ns = ds::small_slots_needed(bf16, s->vocab);
     return ns <= (bf16 ? ds::kSmallMaxSlotsBf16 : ds::kSmallMaxSlotsF32);
 }
+
+bool use_small_kernel(const ds_sampler* s) { return !(s->flags & DS_FLAG_FORCE_FALLBACK) && small_fits(s); }
+
+// Limits of ds_sample_device_params: one wave reads every request's length,
+// and 64 clamped lengths must sum below 2^31.
+constexpr int32_t kDevParamsMaxRequests = ds::kWave;
+constexpr int64_t kDevParamsMaxPositions = int64_t(1) << 24;
 
 }  // namespace
 
@@ -95,7 +103,7 @@ extern "C" {
 
 const char* ds_last_error(void) { return g_err.c_str(); }
 
-int ds_version(void) { return 200; }
+int ds_version(void) { return 300; }
 
 int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype, int32_t max_rows,
                      int64_t max_positions, int32_t max_requests, int32_t top_k,
@@ -270,6 +278,71 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         }
         pos += rel;
     }
+    return DS_OK;
+}
+
+int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
+                            const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
+                            const float* temperature, int32_t num_requests, int32_t num_rows, int64_t positions,
+                            uint64_t seed, int32_t* tokens_out, float* logprobs_out, float* threshold_out,
+                            void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    if (!request_ids || !seq_lens || !iterations || !guidance_scale || !temperature)
+        return fail(DS_ERR_INVALID_ARG, "a per-request device array is NULL");
+    if (!c_logits || !tokens_out || !logprobs_out)
+        return fail(DS_ERR_INVALID_ARG, "c_logits, tokens_out and logprobs_out must be non-NULL");
+    if (num_requests < 1 || num_requests > s->max_requests || num_requests > kDevParamsMaxRequests)
+        return fail(DS_ERR_CAPACITY, "num_requests %d outside [1, %d]", num_requests,
+                    s->max_requests < kDevParamsMaxRequests ? s->max_requests : kDevParamsMaxRequests);
+    if (num_rows < 1 || num_rows > s->max_rows)
+        return fail(DS_ERR_CAPACITY, "num_rows %d outside [1, %d]", num_rows, s->max_rows);
+    if (positions < 1 || positions > s->max_positions || positions > kDevParamsMaxPositions)
+        return fail(DS_ERR_CAPACITY, "positions %lld outside [1, %lld]", (long long)positions,
+                    (long long)(s->max_positions < kDevParamsMaxPositions ? s->max_positions : kDevParamsMaxPositions));
+    if (!small_fits(s))
+        return fail(DS_ERR_UNSUPPORTED, "device-resident parameters need the wave-per-cell kernel (V <= %d %s)",
+                    s->dtype == DS_DTYPE_BF16 ? 2046 : 2048, s->dtype == DS_DTYPE_BF16 ? "bf16" : "f32");
+    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(c_logits, es)) return fail(DS_ERR_INVALID_ARG, "c_logits is not %d-byte aligned", (int)es);
+    if (u_logits) {
+        if (!aligned(u_logits, es)) return fail(DS_ERR_INVALID_ARG, "u_logits is not %d-byte aligned", (int)es);
+        if ((((uintptr_t)u_logits - (uintptr_t)c_logits) & 15u) != 0)
+            return fail(DS_ERR_UNSUPPORTED, "u_logits and c_logits must have the same address modulo 16 bytes");
+    }
+    if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4) || (threshold_out && !aligned(threshold_out, 4)))
+        return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+    if (!aligned(request_ids, 8) || !aligned(seq_lens, 4) || !aligned(iterations, 4) || !aligned(guidance_scale, 4) ||
+        !aligned(temperature, 4))
+        return fail(DS_ERR_INVALID_ARG, "per-request device arrays must be aligned to their element size");
+
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    ds::SampleArgs a;
+    a.c = c_logits;
+    a.u = u_logits;
+    a.V = s->vocab;
+    a.rows = num_rows;
+    a.top_k = s->top_k;
+    a.vocab_chunks = s->vocab_chunks;
+    a.k0 = (uint32_t)seed;
+    a.k1 = (uint32_t)(seed >> 32);
+    a.z0 = s->z0;
+    a.force_fallback = 0;
+    a.tokens = tokens_out;
+    a.logprobs = logprobs_out;
+    a.thresholds = threshold_out;
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    ds::DevReq d;
+    d.request_ids = request_ids;
+    d.seq_lens = seq_lens;
+    d.iterations = iterations;
+    d.guidance = guidance_scale;
+    d.temperature = temperature;
+    d.n = num_requests;
+    d.P = (int32_t)positions;
+    const hipError_t e = ds::launch_sample_small_dev(s->dtype == DS_DTYPE_BF16, a, d, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
     return DS_OK;
 }
 

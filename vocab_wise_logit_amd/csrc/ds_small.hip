@@ -24,6 +24,8 @@
 #include "ds_device.h"
 #include "ds_kernels.h"
 
+#include <type_traits>
+
 namespace ds {
 namespace {
 
@@ -219,8 +221,61 @@ __device__ __forceinline__ void load_slots(const void* base, int lane, int ndw, 
     for (int j = 0; j < NS; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (lane + j * kWave) * 4, 0, 0);
 }
 
-template <bool BF16, int NS>
-__device__ __forceinline__ void sample_small_body(const SampleArgs& a, const ReqTable& rq) {
+// What a wave needs to know about its cell (all wave-uniform).
+struct CellInfo {
+    int64_t cell;       // index into the [C, P] outputs; times V, into the logits
+    float s, tau, inv_tau;
+    uint32_t t;         // position inside the request
+    uint32_t row_iter;  // (row & 0xFFFF) | (iteration << 16)
+    uint32_t rid;       // low 32 bits of the request id
+};
+
+// The cell at launch-relative position pl of `row`, from the kernel-argument
+// table; false past the launch's positions.
+__device__ __forceinline__ bool locate(const ReqTable& rq, int pl, int row, CellInfo& ci) {
+    if (pl >= rq.npos) return false;
+    const int r = find_request(rq, pl);
+    ci.cell = (int64_t)row * rq.P + rq.pos0 + pl;
+    ci.s = rq.scale[r];
+    ci.tau = rq.tau[r];
+    ci.inv_tau = rq.inv_tau[r];
+    ci.t = (uint32_t)(pl - rq.offs[r]);  // offs are launch-relative
+    ci.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
+    ci.rid = rq.rid[r];
+    return true;
+}
+
+// The same from per-request arrays in device memory, read as the wave starts.
+// Lane r holds request r's length (negative lengths count as 0, lengths are
+// clamped to d.P so the sums stay below 2^31); a wave prefix sum gives the
+// request starts and the number of positions in use, min(sum, d.P).  A
+// guidance scale that is not finite, or any scale when u is absent, counts as
+// 0; a temperature that is not a positive finite number samples greedily.
+__device__ __forceinline__ bool locate(const DevReq& d, bool have_u, int pl, int row, CellInfo& ci) {
+    const int lane = lane_id();
+    int T = 0;
+    if (lane < d.n) T = min(max(d.seq_lens[lane], 0), d.P);
+    const int incl = wave_incl_scan(T);
+    const int used = min(__builtin_amdgcn_readlane(incl, kWave - 1), d.P);
+    if (pl >= used) return false;
+    // the request holding pl: the first whose inclusive end passes it (r < d.n,
+    // since pl < the sum of the lengths)
+    const int r = popc(ballot(incl <= pl));
+    const int start = __builtin_amdgcn_readlane(incl - T, r);
+    const float s = d.guidance[r];
+    const float tau = d.temperature[r];
+    ci.cell = (int64_t)row * d.P + pl;
+    ci.s = (have_u && __builtin_isfinite(s)) ? s : 0.0f;
+    ci.tau = (tau > 0.0f && tau < __builtin_huge_valf()) ? tau : 0.0f;
+    ci.inv_tau = ci.tau > 0.0f ? 1.0f / ci.tau : 0.0f;
+    ci.t = (uint32_t)(pl - start);
+    ci.row_iter = ((uint32_t)row & 0xFFFFu) | ((uint32_t)d.iterations[r] << 16);
+    ci.rid = (uint32_t)d.request_ids[r];
+    return true;
+}
+
+template <bool BF16, int NS, typename Src>
+__device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src& src) {
     using R_t = Row<BF16, NS>;
     constexpr int NE = R_t::NE;
     __shared__ Entry s_list[kWavesPerBlock][kListCap + kWave];  // + one spare entry per lane
@@ -231,12 +286,18 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     const int lane = lane_id();
     const int pl = (int)blockIdx.x * kWavesPerBlock + wv;
     const int row = (int)(blockIdx.z * gridDim.y + blockIdx.y);
-    if (pl >= rq.npos || row >= a.rows) return;  // whole wave leaves together
-    const int r = find_request(rq, pl);
-    const int64_t cell = (int64_t)row * rq.P + rq.pos0 + pl;
+    if (row >= a.rows) return;  // whole wave leaves together
+    CellInfo ci;
+    bool here;
+    if constexpr (std::is_same<Src, DevReq>::value)
+        here = locate(src, a.u != nullptr, pl, row, ci);
+    else
+        here = locate(src, pl, row, ci);
+    if (!here) return;  // past the positions in use: the whole wave leaves
+    const int64_t cell = ci.cell;
     const int V = a.V;
-    const float s = rq.scale[r];
-    const float tau = rq.tau[r];
+    const float s = ci.s;
+    const float tau = ci.tau;
     Entry* list = s_list[wv];
 
     // ---------------------------------------------------------------- load
@@ -358,10 +419,10 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Req
     NoiseKey nk;
     nk.k0 = a.k0;
     nk.k1 = a.k1;
-    nk.t = (uint32_t)(pl - rq.offs[r]);  // offs are launch-relative
-    nk.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
-    nk.rid = rq.rid[r];
-    const float inv_tau = rq.inv_tau[r];
+    nk.t = ci.t;
+    nk.row_iter = ci.row_iter;
+    nk.rid = ci.rid;
+    const float inv_tau = ci.inv_tau;
     // No id with h below `prune` can beat the argmax: its h/tau plus the largest
     // possible noise stays below M/tau plus the smallest possible noise.
     const float prune = max_bound(M, inv_tau, tau);
@@ -519,35 +580,57 @@ template <bool BF16, int NS>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small_wide(SampleArgs a, ReqTable rq) {
     sample_small_body<BF16, NS>(a, rq);
 }
+// The same kernels with the per-request parameters in device memory.
+template <bool BF16, int NS>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) __attribute__((amdgpu_waves_per_eu(7, 8)))
+void k_sample_small_dev(SampleArgs a, DevReq d) {
+    sample_small_body<BF16, NS>(a, d);
+}
+template <bool BF16, int NS>
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void k_sample_small_dev_wide(SampleArgs a, DevReq d) {
+    sample_small_body<BF16, NS>(a, d);
+}
+
+// Grid (positions / 4, rows), rows beyond 65535 folded into z.
+inline dim3 small_grid(int64_t positions, int rows) {
+    return dim3((unsigned)((positions + kWavesPerBlock - 1) / kWavesPerBlock), (unsigned)(rows < 65535 ? rows : 65535),
+                (unsigned)((rows + 65534) / 65535));
+}
 
 template <bool BF16, int NS>
 hipError_t launch_ns(const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
-    const unsigned bx = (unsigned)((rq.npos + kWavesPerBlock - 1) / kWavesPerBlock);
-    const unsigned by = (unsigned)(a.rows < 65535 ? a.rows : 65535);
-    const unsigned bz = (unsigned)((a.rows + 65534) / 65535);
+    const dim3 g = small_grid(rq.npos, a.rows);
     constexpr bool kOcc = BF16 ? NS <= 9 : NS <= 16;
     if constexpr (kOcc)
-        hipLaunchKernelGGL((k_sample_small<BF16, NS>), dim3(bx, by, bz), dim3(kWavesPerBlock * kWave), 0, st, a,
-                           rq);
+        hipLaunchKernelGGL((k_sample_small<BF16, NS>), g, dim3(kWavesPerBlock * kWave), 0, st, a, rq);
     else
-        hipLaunchKernelGGL((k_sample_small_wide<BF16, NS>), dim3(bx, by, bz), dim3(kWavesPerBlock * kWave), 0, st,
-                           a, rq);
+        hipLaunchKernelGGL((k_sample_small_wide<BF16, NS>), g, dim3(kWavesPerBlock * kWave), 0, st, a, rq);
+    return hipGetLastError();
+}
+template <bool BF16, int NS>
+hipError_t launch_ns(const SampleArgs& a, const DevReq& d, hipStream_t st) {
+    const dim3 g = small_grid(d.P, a.rows);
+    constexpr bool kOcc = BF16 ? NS <= 9 : NS <= 16;
+    if constexpr (kOcc)
+        hipLaunchKernelGGL((k_sample_small_dev<BF16, NS>), g, dim3(kWavesPerBlock * kWave), 0, st, a, d);
+    else
+        hipLaunchKernelGGL((k_sample_small_dev_wide<BF16, NS>), g, dim3(kWavesPerBlock * kWave), 0, st, a, d);
     return hipGetLastError();
 }
 
 // Register-slot counts that get an instantiation (bf16 rows stop at 16 slots,
 // beyond which the compiler spills; those vocabularies use the row kernel).
-template <bool BF16>
-hipError_t dispatch(int ns, const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
-    if (ns <= 2) return launch_ns<BF16, 2>(a, rq, st);
-    if (ns <= 4) return launch_ns<BF16, 4>(a, rq, st);
-    if (ns <= 6) return launch_ns<BF16, 6>(a, rq, st);
-    if (ns <= 9) return launch_ns<BF16, 9>(a, rq, st);
-    if (ns <= 12) return launch_ns<BF16, 12>(a, rq, st);
-    if (ns <= 16 || BF16) return launch_ns<BF16, 16>(a, rq, st);
+template <bool BF16, typename Src>
+hipError_t dispatch(int ns, const SampleArgs& a, const Src& src, hipStream_t st) {
+    if (ns <= 2) return launch_ns<BF16, 2>(a, src, st);
+    if (ns <= 4) return launch_ns<BF16, 4>(a, src, st);
+    if (ns <= 6) return launch_ns<BF16, 6>(a, src, st);
+    if (ns <= 9) return launch_ns<BF16, 9>(a, src, st);
+    if (ns <= 12) return launch_ns<BF16, 12>(a, src, st);
+    if (ns <= 16 || BF16) return launch_ns<BF16, 16>(a, src, st);
     if constexpr (!BF16) {
-        if (ns <= 24) return launch_ns<BF16, 24>(a, rq, st);
-        return launch_ns<BF16, 32>(a, rq, st);
+        if (ns <= 24) return launch_ns<BF16, 24>(a, src, st);
+        return launch_ns<BF16, 32>(a, src, st);
     }
     return hipErrorInvalidValue;
 }
@@ -564,6 +647,13 @@ hipError_t launch_sample_small(bool bf16, const SampleArgs& a, const ReqTable& r
     const int ns = small_slots_needed(bf16, a.V);
     if (ns > (bf16 ? kSmallMaxSlotsBf16 : kSmallMaxSlotsF32)) return hipErrorInvalidValue;
     return bf16 ? dispatch<true>(ns, a, rq, st) : dispatch<false>(ns, a, rq, st);
+}
+
+hipError_t launch_sample_small_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st) {
+    const int ns = small_slots_needed(bf16, a.V);
+    if (ns > (bf16 ? kSmallMaxSlotsBf16 : kSmallMaxSlotsF32) || d.n < 1 || d.n > kWave || d.P < 1)
+        return hipErrorInvalidValue;
+    return bf16 ? dispatch<true>(ns, a, d, st) : dispatch<false>(ns, a, d, st);
 }
 
 }  // namespace ds
