@@ -166,11 +166,11 @@ int ds_sample(ds_sampler *s, const int64_t *request_ids, const void *c_logits,
  *                  the extent of the launch.
  *   seed, tokens_out [C, positions], logprobs_out [C, positions],
  *   threshold_out [C, positions] or NULL, stream: as in ds_sample.
- * Only vocabularies the wave-per-cell kernel holds in registers are supported
- * (V <= 2046 bf16, V <= 2048 f32); others return DS_ERR_UNSUPPORTED.  The
- * handle's DS_FLAG_FORCE_FALLBACK does not apply.  Returns DS_OK,
- * DS_ERR_INVALID_ARG, DS_ERR_CAPACITY, DS_ERR_UNSUPPORTED or DS_ERR_HIP; the
- * host-side checks run before anything is enqueued.
+ * Every vocabulary size is supported, through the same kernels as ds_sample
+ * (the streaming kernels run over every cell of the fixed layout, and padding
+ * cells leave at once); DS_FLAG_FORCE_FALLBACK applies as it does to ds_sample.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY, DS_ERR_UNSUPPORTED or
+ * DS_ERR_HIP; the host-side checks run before anything is enqueued.
  */
 int ds_sample_device_params(ds_sampler *s, const int64_t *request_ids, const void *c_logits,
                             const void *u_logits, const int32_t *seq_lens, const int32_t *iterations,

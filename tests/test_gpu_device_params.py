@@ -199,18 +199,58 @@ def test_device_params_take_invalid_values_as_documented():
             _check_padding_untouched(out[:2], P)
 
 
+@pytest.mark.parametrize("dtype,V,chunks,fallback", [("bf16", 5000, 1, False), ("bf16", 3000, 3, False),
+                                                     ("f32", 4100, 2, False), ("bf16", 1025, 1, True)])
+def test_device_params_streaming_path(dtype, V, chunks, fallback):
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    # vocabularies past the wave-per-cell kernel (and, with the forced fallback,
+    # one inside it) go through the streaming kernels over the fixed layout
+    w = synth.diffusion(f"devp_row_{dtype}_{V}", seed=64 + V, vocab=V, rows=2, seq_lens=[3, 0, 4], dtype=dtype,
+                        sigma=4.0, guidance=[1.5, 2.0, 0.0], temperature=[1.0, 0.5, 0.7], iterations=[2, 0, 5],
+                        vocab_chunks=chunks)
+    eager = run_sample(w, threshold=True, force_fallback=fallback)
+    check_sample(w, eager, oracle.sample_workload(w))
+    nan = synth.workloads.BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    extra = 5
+    c = to_dev(_padded(w.c, extra, nan))
+    u = to_dev(_padded(w.u, extra, nan))
+    P, Pc = w.positions, w.positions + extra
+    prm = _params(w.request_ids, w.seq_lens, w.iterations, w.guidance, w.temperature)
+    log(f"[gpu] ds_sample_device_params {w.name}: streaming path, positions={Pc}, chunks={chunks}, "
+        f"fallback={fallback}")
+    with ds.Sampler(V, dtype, max_rows=2, max_positions=Pc, max_requests=4, vocab_chunks=chunks,
+                    force_fallback=fallback) as smp:
+        out = _outputs(2, Pc, True)
+        smp.sample_device_params(prm[0], c, u, *prm[1:], seed=w.seed, threshold=True, out=out)
+        torch.cuda.synchronize()
+        _check_padding_untouched(out, P)
+        got = [t[:, :P].reshape(-1).cpu() for t in out]
+        _assert_same(got, [torch.from_numpy(a) for a in eager], "streaming device params vs ds_sample")
+        # and replayed from a graph after the iterations change
+        out2 = _outputs(2, Pc, False)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            smp.sample_device_params(prm[0], c, u, *prm[1:], seed=w.seed, out=out2)
+        it2 = [7, 7, 9]
+        prm[2].copy_(torch.tensor(np.asarray(it2, np.int32)))
+        g.replay()
+        ref = smp.sample(w.request_ids, c[:, :P].contiguous(), u[:, :P].contiguous(), w.seq_lens, it2, w.guidance,
+                         w.temperature, seed=w.seed)
+        torch.cuda.synchronize()
+        _assert_same([t[:, :P] for t in out2[:2]], ref, "streaming graph replay")
+        _check_padding_untouched(out2[:2], P)
+        del g
+
+
 def test_device_params_rejects_what_it_cannot_run():
     import torch
 
     import vocab_wise_logit_amd as ds
 
     prm = _params([1], [4], [0], [0.0], [0.0])
-    with ds.Sampler(3000, "bf16", max_rows=1, max_positions=8, max_requests=1) as smp:
-        c = torch.zeros((1, 8, 3000), dtype=torch.bfloat16, device="cuda")
-        log("[gpu] device params on a vocabulary the wave-per-cell kernel does not hold")
-        with pytest.raises(ds.DSError) as e:
-            smp.sample_device_params(prm[0], c, None, *prm[1:])
-        assert e.value.code == ds.DS_ERR_UNSUPPORTED
     with ds.Sampler(1025, "bf16", max_rows=1, max_positions=8, max_requests=128) as smp:
         c = torch.zeros((1, 16, 1025), dtype=torch.bfloat16, device="cuda")
         log("[gpu] device params beyond max_positions, and with 65 requests")

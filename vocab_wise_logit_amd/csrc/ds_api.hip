@@ -300,9 +300,6 @@ int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const voi
     if (positions < 1 || positions > s->max_positions || positions > kDevParamsMaxPositions)
         return fail(DS_ERR_CAPACITY, "positions %lld outside [1, %lld]", (long long)positions,
                     (long long)(s->max_positions < kDevParamsMaxPositions ? s->max_positions : kDevParamsMaxPositions));
-    if (!small_fits(s))
-        return fail(DS_ERR_UNSUPPORTED, "device-resident parameters need the wave-per-cell kernel (V <= %d %s)",
-                    s->dtype == DS_DTYPE_BF16 ? 2046 : 2048, s->dtype == DS_DTYPE_BF16 ? "bf16" : "f32");
     const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
     if (!aligned(c_logits, es)) return fail(DS_ERR_INVALID_ARG, "c_logits is not %d-byte aligned", (int)es);
     if (u_logits) {
@@ -328,7 +325,7 @@ int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const voi
     a.k0 = (uint32_t)seed;
     a.k1 = (uint32_t)(seed >> 32);
     a.z0 = s->z0;
-    a.force_fallback = 0;
+    a.force_fallback = (s->flags & DS_FLAG_FORCE_FALLBACK) ? 1 : 0;
     a.tokens = tokens_out;
     a.logprobs = logprobs_out;
     a.thresholds = threshold_out;
@@ -341,8 +338,25 @@ int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const voi
     d.temperature = temperature;
     d.n = num_requests;
     d.P = (int32_t)positions;
-    const hipError_t e = ds::launch_sample_small_dev(s->dtype == DS_DTYPE_BF16, a, d, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+    const bool bf16 = s->dtype == DS_DTYPE_BF16;
+    hipStream_t st = (hipStream_t)stream;
+    if (use_small_kernel(s)) {
+        const hipError_t e = ds::launch_sample_small_dev(bf16, a, d, st);
+        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+        return DS_OK;
+    }
+    // the streaming kernels over every cell of the fixed layout, in batches that
+    // fit the workspace; padding cells leave at once
+    const int64_t cells = (int64_t)num_rows * positions;
+    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
+    a.w.nparts = a.w.ppc * s->vocab_chunks;
+    const int64_t slots = ds::kWorkParts / a.w.nparts;
+    for (int64_t c0 = 0; c0 < cells; c0 += slots) {
+        a.w.cell_base = c0;
+        a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
+        const hipError_t e = ds::launch_sample_row_dev(bf16, a, d, st);
+        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+    }
     return DS_OK;
 }
 

@@ -275,6 +275,55 @@ struct ReqTable {
     uint32_t rid[kMaxReqPerLaunch];
 };
 
+// Per-request parameters read from device memory when the launch runs (the
+// fixed-shape entry point), instead of from the kernel-argument table.
+struct DevReq {
+    const int64_t* request_ids;  // [n]
+    const int32_t* seq_lens;     // [n]
+    const int32_t* iterations;   // [n]
+    const float* guidance;       // [n]
+    const float* temperature;    // [n]
+    int32_t n;                   // requests, <= kWave
+    int32_t P;                   // positions of the packed layout: row stride and grid extent
+};
+
+// What a cell takes from its request under DevReq.
+struct DevCell {
+    float s, tau, inv_tau;
+    uint32_t t;        // position inside the request
+    uint32_t iter_hi;  // iteration << 16
+    uint32_t rid;      // low 32 bits of the request id
+};
+
+// The request holding position pl, from DevReq's arrays; false when pl is
+// padding.  Every wave calls it whole: lane r holds request r's length (a
+// negative length counts as 0; lengths are clamped to d.P so the sums stay
+// below 2^31), a wave prefix sum gives the request starts and the positions in
+// use, min(sum, d.P).  A guidance scale that is not finite, or any scale when u
+// is absent, counts as 0; a temperature that is not a positive finite number
+// samples greedily.
+__device__ __forceinline__ bool dev_cell(const DevReq& d, bool have_u, int pl, DevCell& o) {
+    const int lane = lane_id();
+    int T = 0;
+    if (lane < d.n) T = min(max(d.seq_lens[lane], 0), d.P);
+    const int incl = wave_incl_scan(T);
+    const int used = min(__builtin_amdgcn_readlane(incl, kWave - 1), d.P);
+    if (pl >= used) return false;
+    // the first request whose inclusive end passes pl (r < d.n, since pl is
+    // below the sum of the lengths)
+    const int r = popc(ballot(incl <= pl));
+    const int start = __builtin_amdgcn_readlane(incl - T, r);
+    const float s = d.guidance[r];
+    const float tau = d.temperature[r];
+    o.s = (have_u && __builtin_isfinite(s)) ? s : 0.0f;
+    o.tau = (tau > 0.0f && tau < __builtin_huge_valf()) ? tau : 0.0f;
+    o.inv_tau = o.tau > 0.0f ? 1.0f / o.tau : 0.0f;
+    o.t = (uint32_t)(pl - start);
+    o.iter_hi = (uint32_t)d.iterations[r] << 16;
+    o.rid = (uint32_t)d.request_ids[r];
+    return true;
+}
+
 // The request owning launch-relative position pl: the last r with offs[r] <= pl.
 __device__ __forceinline__ int find_request(const ReqTable& rq, int pl) {
     int lo = 0, hi = rq.n - 1;

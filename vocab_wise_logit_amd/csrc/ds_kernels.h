@@ -54,18 +54,6 @@ struct SampleArgs {
     RowWork w;              // streaming kernel workspace (unused by the small kernel)
 };
 
-// Per-request parameters read from device memory when the launch runs (the
-// fixed-shape entry point), instead of from the kernel-argument table.
-struct DevReq {
-    const int64_t* request_ids;  // [n]
-    const int32_t* seq_lens;     // [n]
-    const int32_t* iterations;   // [n]
-    const float* guidance;       // [n]
-    const float* temperature;    // [n]
-    int32_t n;                   // requests, <= kWave
-    int32_t P;                   // positions of the packed layout: row stride and grid extent
-};
-
 // Largest row the wave-per-cell kernel keeps in registers, in dwords per lane.
 constexpr int kSmallMaxSlotsBf16 = 16;  // V <= 2046
 constexpr int kSmallMaxSlotsF32 = 32;   // V <= 2048
@@ -76,6 +64,7 @@ hipError_t launch_sample_small(bool bf16, const SampleArgs& a, const ReqTable& r
 hipError_t launch_sample_small_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st);
 hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq,
                              hipStream_t st);
+hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st);
 
 struct GreedyArgs {
     const void* x;      // [n_rows, V]

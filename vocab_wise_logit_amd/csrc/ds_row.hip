@@ -799,6 +799,26 @@ __device__ __forceinline__ CellParams sample_cell(const SampleArgs& a, const Req
     return cp;
 }
 
+// The cell of workspace slot `slot` under device-resident parameters; false
+// when it is padding (the whole workgroup leaves together).
+__device__ __forceinline__ bool sample_cell_dev(const SampleArgs& a, const DevReq& d, int64_t slot, CellParams& cp) {
+    const int64_t lin = a.w.cell_base + slot;  // row * d.P + position
+    const int row = (int)(lin / d.P);
+    const int pl = (int)(lin - (int64_t)row * d.P);
+    DevCell dc;
+    if (!dev_cell(d, a.u != nullptr, pl, dc)) return false;
+    cp.cell = lin;
+    cp.s = dc.s;
+    cp.tau = dc.tau;
+    cp.inv_tau = dc.inv_tau;
+    cp.nk.k0 = a.k0;
+    cp.nk.k1 = a.k1;
+    cp.nk.t = dc.t;
+    cp.nk.row_iter = ((uint32_t)row & 0xFFFFu) | dc.iter_hi;
+    cp.nk.rid = dc.rid;
+    return true;
+}
+
 __device__ __forceinline__ CellParams greedy_cell(const GreedyArgs& a, int64_t slot) {
     CellParams cp;
     cp.cell = a.w.cell_base + slot;
@@ -825,6 +845,23 @@ __global__ __launch_bounds__(NT) void k_sample_merge(SampleArgs a, ReqTable rq) 
     const int64_t slot = blockIdx.x;
     merge_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
                            sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr, a.thresholds, nullptr, 0);
+}
+// The same two kernels with the per-request parameters in device memory.
+template <bool BF16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_sample_parts_dev(SampleArgs a, DevReq d) {
+    const int64_t slot = blockIdx.x / a.w.nparts;
+    const int part = (int)(blockIdx.x - slot * a.w.nparts);
+    CellParams cp;
+    if (!sample_cell_dev(a, d, slot, cp)) return;
+    part_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part);
+}
+template <bool BF16>
+__global__ __launch_bounds__(NT) void k_sample_merge_dev(SampleArgs a, DevReq d) {
+    const int64_t slot = blockIdx.x;
+    CellParams cp;
+    if (!sample_cell_dev(a, d, slot, cp)) return;
+    merge_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w, cp, slot, a.tokens,
+                           a.logprobs, nullptr, a.thresholds, nullptr, 0);
 }
 template <bool BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_greedy_parts(GreedyArgs a) {
@@ -916,6 +953,20 @@ hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq,
     } else {
         hipLaunchKernelGGL(k_sample_parts<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
         hipLaunchKernelGGL(k_sample_merge<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, rq);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st) {
+    const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
+    if (parts == 0) return hipSuccess;
+    if (d.n < 1 || d.n > kWave || d.P < 1) return hipErrorInvalidValue;
+    if (bf16) {
+        hipLaunchKernelGGL(k_sample_parts_dev<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
+        hipLaunchKernelGGL(k_sample_merge_dev<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, d);
+    } else {
+        hipLaunchKernelGGL(k_sample_parts_dev<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
+        hipLaunchKernelGGL(k_sample_merge_dev<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, d);
     }
     return hipGetLastError();
 }

@@ -246,31 +246,16 @@ __device__ __forceinline__ bool locate(const ReqTable& rq, int pl, int row, Cell
 }
 
 // The same from per-request arrays in device memory, read as the wave starts.
-// Lane r holds request r's length (negative lengths count as 0, lengths are
-// clamped to d.P so the sums stay below 2^31); a wave prefix sum gives the
-// request starts and the number of positions in use, min(sum, d.P).  A
-// guidance scale that is not finite, or any scale when u is absent, counts as
-// 0; a temperature that is not a positive finite number samples greedily.
 __device__ __forceinline__ bool locate(const DevReq& d, bool have_u, int pl, int row, CellInfo& ci) {
-    const int lane = lane_id();
-    int T = 0;
-    if (lane < d.n) T = min(max(d.seq_lens[lane], 0), d.P);
-    const int incl = wave_incl_scan(T);
-    const int used = min(__builtin_amdgcn_readlane(incl, kWave - 1), d.P);
-    if (pl >= used) return false;
-    // the request holding pl: the first whose inclusive end passes it (r < d.n,
-    // since pl < the sum of the lengths)
-    const int r = popc(ballot(incl <= pl));
-    const int start = __builtin_amdgcn_readlane(incl - T, r);
-    const float s = d.guidance[r];
-    const float tau = d.temperature[r];
+    DevCell dc;
+    if (!dev_cell(d, have_u, pl, dc)) return false;
     ci.cell = (int64_t)row * d.P + pl;
-    ci.s = (have_u && __builtin_isfinite(s)) ? s : 0.0f;
-    ci.tau = (tau > 0.0f && tau < __builtin_huge_valf()) ? tau : 0.0f;
-    ci.inv_tau = ci.tau > 0.0f ? 1.0f / ci.tau : 0.0f;
-    ci.t = (uint32_t)(pl - start);
-    ci.row_iter = ((uint32_t)row & 0xFFFFu) | ((uint32_t)d.iterations[r] << 16);
-    ci.rid = (uint32_t)d.request_ids[r];
+    ci.s = dc.s;
+    ci.tau = dc.tau;
+    ci.inv_tau = dc.inv_tau;
+    ci.t = dc.t;
+    ci.row_iter = ((uint32_t)row & 0xFFFFu) | dc.iter_hi;
+    ci.rid = dc.rid;
     return true;
 }
 
