@@ -142,20 +142,26 @@ class Runner:
             self.cells = n
         else:
             c = to_dev(w.c)
-            u = to_dev(w.u) if w.u is not None else None
-            per_set = c.numel() * c.element_size() * (2 if u is not None else 1)
+            if mode == "compact_u" and w.u is not None:
+                # only the guided requests' positions of u, in request order
+                offs = np.concatenate([[0], np.cumsum(w.seq_lens)])
+                keep = [np.arange(offs[r], offs[r + 1]) for r in range(len(w.seq_lens)) if w.guidance[r] != 0]
+                u = to_dev(np.ascontiguousarray(w.u[:, np.concatenate(keep)])) if keep else None
+            else:
+                u = to_dev(w.u) if w.u is not None else None
+            per_set = c.numel() * c.element_size() + (u.numel() * u.element_size() if u is not None else 0)
             self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
             self.c = [c] + [c.clone() for _ in range(self.n_sets - 1)]
             self.u = [u] + [u.clone() for _ in range(self.n_sets - 1)] if u is not None else None
             self.smp = ds.Sampler(w.vocab, w.dtype, max_rows=w.rows, max_positions=w.positions,
                                   max_requests=len(w.seq_lens), top_k=w.top_k,
-                                  vocab_chunks=w.vocab_chunks)
+                                  vocab_chunks=w.vocab_chunks, compact_u=mode == "compact_u")
             shape = (w.rows, w.positions)
             self.out = (torch.empty(shape, dtype=torch.int32, device="cuda"),
                         torch.empty(shape, dtype=torch.float32, device="cuda"),
                         torch.empty(shape, dtype=torch.float32, device="cuda") if threshold else None)
             self.cells = w.cells
-            if mode != "eager":
+            if mode in ("device_params", "graph"):
                 self.prm = (torch.tensor(np.asarray(w.request_ids, np.int64), device="cuda"),
                             torch.tensor(np.asarray(w.seq_lens, np.int32), device="cuda"),
                             torch.tensor(np.asarray(w.iterations, np.int32), device="cuda"),
@@ -191,7 +197,7 @@ class Runner:
             self.graphs[s].replay()
         elif self.mode == "device_params":
             self._dev_call(s)
-        else:
+        else:  # eager, or eager with the compacted u layout
             self.smp.sample(w.request_ids, self.c[s], self.u[s] if self.u else None, w.seq_lens,
                             w.iterations, w.guidance, w.temperature, seed=w.seed,
                             threshold=self.out[2] is not None, out=self.out)
@@ -293,10 +299,13 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
         cfg["workload"] += "+threshold"
         cfg["threshold_out"] = True
     kname = kernel_name(w, kind)
-    if mode != "eager":
+    if mode in ("device_params", "graph"):
         cfg["workload"] += "+" + mode
         cfg["entry_point"] = "ds_sample_device_params" + (" in a replayed HIP graph" if mode == "graph" else "")
         kname = kname.replace("k_sample_small", "k_sample_small_dev")
+    elif mode == "compact_u":
+        cfg["workload"] += "+compact_u"
+        cfg["u_layout"] = "compacted: guided requests' positions only"
     return {"config": cfg, "kernel": kname, "launches_per_step": launches_per_step(w, kind),
             "steps": steps, "warmup": warmup, "positions_per_s": cells / (ms_step * 1e-3),
             "ms_per_step": ms_step, "kernel_ms_mean": ms_step, "bracketed_ms_mean": ms_kernel,
@@ -376,6 +385,8 @@ def main() -> int:
         runs = [(n, thr, "eager") for n, thr in runs]
         # the fixed-shape entry point with device-resident parameters, called and replayed
         runs += [("omnivoice", False, "device_params"), ("omnivoice", False, "graph")]
+        # the mixed batch with u holding only the guided requests' positions
+        runs += [("mixed", False, "compact_u")]
         for name, thr, mode in runs:
             if name == args.workload and not thr and mode == "eager":
                 res = head

@@ -61,7 +61,18 @@ enum {
      * radix select over re-reads, Gumbel over every kept id) instead of the
      * single-pass fast paths.  Results are identical; this exists so tests can
      * compare the two paths. */
-    DS_FLAG_FORCE_FALLBACK = 1
+    DS_FLAG_FORCE_FALLBACK = 1,
+    /* ds_sample reads u_logits in the compacted layout [C, P_u, V], holding only
+     * the positions of requests whose guidance scale is not 0, in request order:
+     * request r with guidance != 0 owns u positions [uoff_r, uoff_r + seq_lens[r])
+     * with uoff_r = the sum of seq_lens over the earlier guided requests, and P_u
+     * = the sum over all of them ([PR] "What does this PR do?": a request with
+     * guidance 0 builds no unconditional document).  The streaming kernels (V
+     * beyond the wave-per-cell kernel, or DS_FLAG_FORCE_FALLBACK) need V * b to
+     * be a multiple of 16 bytes for this (b = 2 for bf16, 4 for f32); otherwise
+     * ds_sample returns DS_ERR_UNSUPPORTED.  ds_sample_device_params does not
+     * take this layout (DS_ERR_UNSUPPORTED). */
+    DS_FLAG_COMPACT_U = 2
 };
 
 /*

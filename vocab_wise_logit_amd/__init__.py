@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     DS_ERR_INVALID_ARG,
     DS_ERR_NO_MEMORY,
     DS_ERR_UNSUPPORTED,
+    DS_FLAG_COMPACT_U,
     DS_FLAG_FORCE_FALLBACK,
     DS_FLAG_NONE,
     DS_OK,
@@ -45,19 +46,22 @@ class Sampler:
     logprobs)`` with per-request guidance scale and temperature;
     ``greedy_lse`` is the draft path's (token, lse, logprob) reduction;
     ``reveal_topk`` ranks each request's cells by a confidence score and returns
-    the best ones.
+    the best ones.  With ``compact_u`` the u logits of ``sample`` hold only the
+    positions of requests whose guidance scale is not 0, in request order.
     """
 
     def __init__(self, vocab: int, dtype: str = "bf16", *, max_rows: int = 8,
                  max_positions: int = 4096, max_requests: int = 64, top_k: int = 0,
-                 vocab_chunks: int = 1, device: int = 0, force_fallback: bool = False):
+                 vocab_chunks: int = 1, device: int = 0, force_fallback: bool = False,
+                 compact_u: bool = False):
         if dtype not in ("bf16", "f32"):
             raise ValueError("dtype must be 'bf16' or 'f32'")
         self.vocab = vocab
         self.dtype = dtype
         self.device = device
         self.vocab_chunks = vocab_chunks
-        flags = DS_FLAG_FORCE_FALLBACK if force_fallback else DS_FLAG_NONE
+        flags = (DS_FLAG_FORCE_FALLBACK if force_fallback else DS_FLAG_NONE) | (
+            DS_FLAG_COMPACT_U if compact_u else DS_FLAG_NONE)
         self._h = ds_sample_create(device, vocab, DS_DTYPE_BF16 if dtype == "bf16" else DS_DTYPE_F32,
                                    max_rows, max_positions, max_requests, top_k, vocab_chunks, flags)
         self._stage = RequestStage(max_requests)

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdssample
 
 DS_DTYPE_F32, DS_DTYPE_BF16 = 0, 1
 DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY, DS_ERR_HIP = range(6)
-DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK = 0, 1
+DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK, DS_FLAG_COMPACT_U = 0, 1, 2
 
 EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_greedy_lse", "ds_reveal_topk",
             "ds_sample_destroy", "ds_last_error", "ds_version")

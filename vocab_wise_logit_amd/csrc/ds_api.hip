@@ -123,7 +123,8 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
     const int32_t max_chunks = vocab < 1024 ? vocab : 1024;
     if (vocab_chunks < 1 || vocab_chunks > max_chunks)
         return fail(DS_ERR_INVALID_ARG, "vocab_chunks must be in [1, %d]", max_chunks);
-    if (flags & ~(uint32_t)DS_FLAG_FORCE_FALLBACK) return fail(DS_ERR_INVALID_ARG, "unknown flags");
+    if (flags & ~(uint32_t)(DS_FLAG_FORCE_FALLBACK | DS_FLAG_COMPACT_U))
+        return fail(DS_ERR_INVALID_ARG, "unknown flags");
     int ndev = 0;
     hipError_t e = hipGetDeviceCount(&ndev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
@@ -188,7 +189,7 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
     if (!aligned(c_logits, es)) return fail(DS_ERR_INVALID_ARG, "c_logits is not %d-byte aligned", (int)es);
     if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4) || (threshold_out && !aligned(threshold_out, 4)))
         return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
-    int64_t P = 0;
+    int64_t P = 0, Pu = 0;
     bool need_u = false;
     for (int32_t r = 0; r < num_requests; ++r) {
         if (seq_lens[r] < 0) return fail(DS_ERR_INVALID_ARG, "seq_lens[%d] = %d < 0", r, seq_lens[r]);
@@ -198,7 +199,9 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
             return fail(DS_ERR_INVALID_ARG, "temperature[%d] must be finite and >= 0", r);
         need_u |= guidance_scale[r] != 0.0f;
         P += seq_lens[r];
+        if (guidance_scale[r] != 0.0f) Pu += seq_lens[r];
     }
+    const bool compact_u = (s->flags & DS_FLAG_COMPACT_U) != 0;
     if (P > s->max_positions)
         return fail(DS_ERR_CAPACITY, "sum(seq_lens) = %lld exceeds max_positions %lld", (long long)P,
                     (long long)s->max_positions);
@@ -209,13 +212,15 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         if ((((uintptr_t)u_logits - (uintptr_t)c_logits) & 15u) != 0)
             return fail(DS_ERR_UNSUPPORTED, "u_logits and c_logits must have the same address modulo 16 bytes");
     }
+    const bool bf16 = s->dtype == DS_DTYPE_BF16;
+    const bool small = use_small_kernel(s);
+    if (compact_u && need_u && !small && ((int64_t)s->vocab * (int64_t)es) % 16 != 0)
+        return fail(DS_ERR_UNSUPPORTED, "a compacted u layout needs V * %d bytes to be a multiple of 16 here", (int)es);
     if (P == 0) return DS_OK;
 
     DeviceGuard dg(s->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t st = (hipStream_t)stream;
-    const bool bf16 = s->dtype == DS_DTYPE_BF16;
-    const bool small = use_small_kernel(s);
 
     ds::SampleArgs a;
     a.c = c_logits;
@@ -235,11 +240,12 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
 
     // one launch per group of up to 64 non-empty requests (contiguous positions)
     int32_t r = 0;
-    int64_t pos = 0;
+    int64_t pos = 0, upos = 0;  // packed position of the launch; next compacted u position
     while (r < num_requests) {
         ds::ReqTable rq;
         std::memset(&rq, 0, sizeof rq);
         rq.P = (int32_t)P;
+        rq.Pu = (int32_t)(compact_u ? Pu : P);
         while (r < num_requests && seq_lens[r] == 0) ++r;
         if (r >= num_requests) break;
         rq.pos0 = (int32_t)pos;
@@ -249,7 +255,10 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
                 rq.offs[n] = rel;
                 rq.scale[n] = guidance_scale[r];
                 rq.tau[n] = temperature[r];
-                rq.inv_tau[n] = temperature[r] > 0.0f ? 1.0f / temperature[r] : 0.0f;
+                // u position of the request's first cell: its own position, or the
+                // next compacted one (requests with guidance 0 read no u)
+                rq.uoff[n] = compact_u ? (int32_t)upos : (int32_t)(pos + rel);
+                if (compact_u && guidance_scale[r] != 0.0f) upos += seq_lens[r];
                 rq.row_iter_hi[n] = (uint32_t)iterations[r] << 16;
                 rq.rid[n] = (uint32_t)request_ids[r];
                 rel += seq_lens[r];
@@ -309,6 +318,8 @@ int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const voi
     }
     if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4) || (threshold_out && !aligned(threshold_out, 4)))
         return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+    if (s->flags & DS_FLAG_COMPACT_U)
+        return fail(DS_ERR_UNSUPPORTED, "ds_sample_device_params does not take the compacted u layout");
     if (!aligned(request_ids, 8) || !aligned(seq_lens, 4) || !aligned(iterations, 4) || !aligned(guidance_scale, 4) ||
         !aligned(temperature, 4))
         return fail(DS_ERR_INVALID_ARG, "per-request device arrays must be aligned to their element size");

@@ -231,6 +231,8 @@ __device__ __forceinline__ int wave_argmax(float& z, int& id) {
 // Inclusive prefix sum over lanes 0..lane: four shifted adds inside each row of
 // 16 lanes (a lane with no source lane reads 0), then each row adds the totals
 // of the rows below it, read into scalar registers.
+constexpr int kDppWaveShl1 = 0x130;   // lane i takes lane i + 1 (lane 63 reads 0)
+constexpr int kDppWaveShr1 = 0x138;   // lane i takes lane i - 1 (lane 0 reads 0)
 constexpr int kDppRowShr1 = 0x111;
 constexpr int kDppRowShr2 = 0x112;
 constexpr int kDppRowShr4 = 0x114;
@@ -267,10 +269,11 @@ struct ReqTable {
     int32_t pos0;     // first packed position covered
     int32_t npos;     // positions covered
     int32_t P;        // total packed positions of the call
+    int32_t Pu;       // positions of the u layout: P, or the guided positions when u is compacted
     int32_t offs[kMaxReqPerLaunch + 1];  // request starts, relative to pos0
     float scale[kMaxReqPerLaunch];
     float tau[kMaxReqPerLaunch];
-    float inv_tau[kMaxReqPerLaunch];
+    int32_t uoff[kMaxReqPerLaunch];  // u position of the request's first position
     uint32_t row_iter_hi[kMaxReqPerLaunch];  // iteration << 16
     uint32_t rid[kMaxReqPerLaunch];
 };
@@ -286,6 +289,10 @@ struct DevReq {
     int32_t n;                   // requests, <= kWave
     int32_t P;                   // positions of the packed layout: row stride and grid extent
 };
+
+// 1 / tau for sampled requests (correctly rounded, as the host computes it), 0
+// for greedy ones.
+__device__ __forceinline__ float inv_temperature(float tau) { return tau > 0.0f ? 1.0f / tau : 0.0f; }
 
 // What a cell takes from its request under DevReq.
 struct DevCell {
@@ -317,7 +324,7 @@ __device__ __forceinline__ bool dev_cell(const DevReq& d, bool have_u, int pl, D
     const float tau = d.temperature[r];
     o.s = (have_u && __builtin_isfinite(s)) ? s : 0.0f;
     o.tau = (tau > 0.0f && tau < __builtin_huge_valf()) ? tau : 0.0f;
-    o.inv_tau = o.tau > 0.0f ? 1.0f / o.tau : 0.0f;
+    o.inv_tau = inv_temperature(o.tau);
     o.t = (uint32_t)(pl - start);
     o.iter_hi = (uint32_t)d.iterations[r] << 16;
     o.rid = (uint32_t)d.request_ids[r];

@@ -335,7 +335,8 @@ __device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, 
 
 // Per-cell parameters of one sampled (or greedy) row.
 struct CellParams {
-    int64_t cell;   // index into the [C, P] outputs
+    int64_t cell;   // index into the [C, P] outputs; times V, into c
+    int64_t ucell;  // times V, into u (cell unless u is compacted; then V * b is a multiple of 16)
     float s, tau, inv_tau;
     NoiseKey nk;
 };
@@ -641,6 +642,12 @@ __device__ __forceinline__ RowGeom row_geom(const void* cptr, const void* uptr, 
     return G;
 }
 
+// The u pointer that puts the cell's u row where its c row is (the identity
+// unless u is compacted, when the row-to-row shift keeps the 16-byte alignment).
+__device__ __forceinline__ const void* cell_u(const void* uptr, const CellParams& cp, int V, bool bf16) {
+    return uptr ? (const void*)((const char*)uptr + (cp.ucell - cp.cell) * (int64_t)V * (bf16 ? 2 : 4)) : uptr;
+}
+
 // Kernel 1 body: stream part `part` of the row and write its partial record.
 template <bool BF16, bool SAMPLE>
 __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bool force_fallback,
@@ -650,7 +657,7 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
     const int q = part - j * w.ppc;
     const bool use_u = SAMPLE && cp.s != 0.0f;
     const bool race = SAMPLE && cp.tau != 0.0f && !force_fallback;
-    const RowGeom G = row_geom<BF16>(cptr, uptr, use_u, cp.cell, V, nch, w.ppc);
+    const RowGeom G = row_geom<BF16>(cptr, cell_u(uptr, cp, V, BF16), use_u, cp.cell, V, nch, w.ppc);
     const PartRange<BF16> pr(G, j, q);
     PartOut po = stream_part<BF16, SAMPLE, false>(G, pr, cp, use_u, race, sh);
     if (po.nan) {
@@ -754,7 +761,7 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
     // not score has a smaller key), so it is the answer as soon as it is kept.
     bool done = raced && queued <= (int64_t)k;
     float t = kNegInf;
-    const RowGeom G = row_geom<BF16>(cptr, uptr, use_u, cp.cell, V, nch, w.ppc);
+    const RowGeom G = row_geom<BF16>(cptr, cell_u(uptr, cp, V, BF16), use_u, cp.cell, V, nch, w.ppc);
     if (!done || thresholds) t = radix_select_row<BF16>(G, cp.s, use_u, k, sh);
     done = done || (raced && bz > kNegInf && bh >= t);
     if (!done) {
@@ -788,9 +795,10 @@ __device__ __forceinline__ CellParams sample_cell(const SampleArgs& a, const Req
     const int r = find_request(rq, pl);
     CellParams cp;
     cp.cell = (int64_t)row * rq.P + rq.pos0 + pl;
+    cp.ucell = (int64_t)row * rq.Pu + rq.uoff[r] + (pl - rq.offs[r]);
     cp.s = rq.scale[r];
     cp.tau = rq.tau[r];
-    cp.inv_tau = rq.inv_tau[r];
+    cp.inv_tau = inv_temperature(cp.tau);
     cp.nk.k0 = a.k0;
     cp.nk.k1 = a.k1;
     cp.nk.t = (uint32_t)(pl - rq.offs[r]);
@@ -808,6 +816,7 @@ __device__ __forceinline__ bool sample_cell_dev(const SampleArgs& a, const DevRe
     DevCell dc;
     if (!dev_cell(d, a.u != nullptr, pl, dc)) return false;
     cp.cell = lin;
+    cp.ucell = lin;
     cp.s = dc.s;
     cp.tau = dc.tau;
     cp.inv_tau = dc.inv_tau;
@@ -822,6 +831,7 @@ __device__ __forceinline__ bool sample_cell_dev(const SampleArgs& a, const DevRe
 __device__ __forceinline__ CellParams greedy_cell(const GreedyArgs& a, int64_t slot) {
     CellParams cp;
     cp.cell = a.w.cell_base + slot;
+    cp.ucell = cp.cell;
     cp.s = 0.0f;
     cp.tau = 0.0f;
     cp.inv_tau = 0.0f;

@@ -210,6 +210,32 @@ __device__ __forceinline__ int count_list_above(const Entry* list, int n, float 
     return c;
 }
 
+// u's dwords loaded in u's own dword frame, moved into c's: when the two rows
+// start at different halves of a dword, each c-frame dword takes one element
+// from this own-frame dword and one from its neighbour (the next one when c's
+// row starts on a dword boundary, `next`, else the previous one).  The
+// neighbour is the adjacent lane's (a DPP wave shift), or at the wave's edge the
+// adjacent slot's edge lane; past the first or last slot it reads 0, which only
+// reaches positions outside the row.
+template <int NS>
+__device__ __forceinline__ void realign_u(uint32_t (&uw)[NS], bool next, int lane) {
+    if (next) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {  // uw[j + 1] is still in its own frame here
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)uw[j], kDppWaveShl1, 0xF, 0xF, true);
+            const uint32_t edge = j + 1 < NS ? (uint32_t)__builtin_amdgcn_readlane((int)uw[j + 1], 0) : 0u;
+            uw[j] = __builtin_amdgcn_alignbit(lane == kWave - 1 ? edge : nb, uw[j], 16);
+        }
+    } else {
+#pragma unroll
+        for (int j = NS - 1; j >= 0; --j) {  // uw[j - 1] is still in its own frame here
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)uw[j], kDppWaveShr1, 0xF, 0xF, true);
+            const uint32_t edge = j > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)uw[j - 1], kWave - 1) : 0u;
+            uw[j] = __builtin_amdgcn_alignbit(uw[j], lane == 0 ? edge : nb, 16);
+        }
+    }
+}
+
 // Load one row's dwords through a buffer resource that covers exactly the row:
 // the hardware range check returns 0 for dwords past it, so no load is branched
 // or masked.  Slot j of lane l is dword 64 j + l.
@@ -223,7 +249,8 @@ __device__ __forceinline__ void load_slots(const void* base, int lane, int ndw, 
 
 // What a wave needs to know about its cell (all wave-uniform).
 struct CellInfo {
-    int64_t cell;       // index into the [C, P] outputs; times V, into the logits
+    int64_t cell;       // index into the [C, P] outputs; times V, into c
+    int64_t ucell;      // times V, into u (cell unless u is compacted)
     float s, tau, inv_tau;
     uint32_t t;         // position inside the request
     uint32_t row_iter;  // (row & 0xFFFF) | (iteration << 16)
@@ -236,10 +263,11 @@ __device__ __forceinline__ bool locate(const ReqTable& rq, int pl, int row, Cell
     if (pl >= rq.npos) return false;
     const int r = find_request(rq, pl);
     ci.cell = (int64_t)row * rq.P + rq.pos0 + pl;
+    ci.t = (uint32_t)(pl - rq.offs[r]);  // offs are launch-relative
+    ci.ucell = (int64_t)row * rq.Pu + rq.uoff[r] + ci.t;
     ci.s = rq.scale[r];
     ci.tau = rq.tau[r];
-    ci.inv_tau = rq.inv_tau[r];
-    ci.t = (uint32_t)(pl - rq.offs[r]);  // offs are launch-relative
+    ci.inv_tau = inv_temperature(ci.tau);
     ci.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
     ci.rid = rq.rid[r];
     return true;
@@ -250,6 +278,7 @@ __device__ __forceinline__ bool locate(const DevReq& d, bool have_u, int pl, int
     DevCell dc;
     if (!dev_cell(d, have_u, pl, dc)) return false;
     ci.cell = (int64_t)row * d.P + pl;
+    ci.ucell = ci.cell;
     ci.s = dc.s;
     ci.tau = dc.tau;
     ci.inv_tau = dc.inv_tau;
@@ -289,7 +318,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     R_t R;
     if (BF16) {
         const uintptr_t cb = (uintptr_t)a.c;
-        // dword-aligned view of c (u has the same address modulo 16)
+        // dword-aligned view of c
         const int64_t g = (int64_t)((cb & 3) >> 1) + cell * V;
         const int par = (int)(g & 1);
         const int64_t off = (g >> 1) * 4 - (int64_t)(cb & 3);  // byte offset of the row's first dword
@@ -302,8 +331,13 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
 #pragma unroll
         for (int j = 0; j < NS; ++j) cw[j] = (lane + j * kWave < ndw) ? cw[j] : 0xFF80FF80u;
         if (s != 0.0f) {
+            // u's row (its own cell: a compacted u layout moves it) in its own
+            // dword frame; the same as c's unless its start is on the other half
             uint32_t uw[NS];
-            load_slots<NS>((const char*)a.u + off, lane, ndw, uw);
+            const uintptr_t ub = (uintptr_t)a.u + (uintptr_t)(ci.ucell * V) * 2u;
+            const int upar = (int)((ub >> 1) & 1u);
+            load_slots<NS>((const char*)(ub - 2u * (uintptr_t)upar), lane, (upar + V + 1) >> 1, uw);
+            if (upar != par) realign_u<NS>(uw, par == 0, lane);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 R.h[2 * j] = guided_raw(bf16_lo(cw[j]), bf16_lo(uw[j]), s);
@@ -332,7 +366,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         for (int j = 0; j < NS; ++j) cw[j] = (lane + j * kWave < V) ? cw[j] : 0xFF800000u;
         if (s != 0.0f) {
             uint32_t uw[NS];
-            load_slots<NS>((const float*)a.u + cell * V, lane, V, uw);
+            load_slots<NS>((const float*)a.u + ci.ucell * V, lane, V, uw);
 #pragma unroll
             for (int j = 0; j < NS; ++j) R.h[j] = guided_raw(__uint_as_float(cw[j]), __uint_as_float(uw[j]), s);
         } else {
