@@ -49,8 +49,14 @@ def test_mixed_guidance_batch_all_cells():
     w = synth.mixed()
     assert np.any(w.guidance == 0) and w.u is not None
     ref = oracle.sample_workload(w)
-    rep = check_sample(w, run_sample(w), ref)
+    got = run_sample(w)
+    rep = check_sample(w, got, ref)
     assert rep.greedy > 0 and rep.sampled > 0
+    # the production call (no threshold output): unguided sampled cells narrow
+    # the top-ratio set with a histogram and race it without the threshold
+    got2 = run_sample(w, threshold=False)
+    check_sample(w, got2, ref)
+    assert np.array_equal(got[0], got2[0]) and np.array_equal(got[1], got2[1])
 
 
 @pytest.mark.parametrize("chunks", [1, 4])

@@ -32,6 +32,14 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 constexpr int kListCap = 512;
 constexpr int kListRegs = kListCap / kWave;
+// Sampled cells with at most this many ids that can win race them all; beyond
+// it, the top-ratio set is first narrowed with a histogram.
+constexpr int kRaceAll = 256;
+// Per-wave histogram of the narrowing step: kHistLow spill bins (one per lane,
+// for ids below the range) and then kHistBins bins over the range.
+constexpr int kHistLow = kWave;
+constexpr int kHistBins = 256;
+constexpr float kHistTop = (float)(kHistLow + kHistBins) - 0.5f;
 
 struct Entry {
     float h;
@@ -58,19 +66,19 @@ struct Row {
         return n;
     }
 
-    // Count the ids whose h is >= x and, if there are at most kListCap of them,
-    // write them to `list` as (h, id).  Each lane counts its own ids, a wave
-    // prefix sum places each lane's run, and the lane writes its ids there in
+    // Count the ids whose h is >= x and, if there are at most `cap` (<= kListCap)
+    // of them, write them to `list` as (h, id).  Each lane counts its own ids, a
+    // wave prefix sum places each lane's run, and the lane writes its ids there in
     // register order.  Every lane stores every slot, the ids below x to its own
     // spare entry past kListCap, so the pass has no per-slot ballot or branch.
     // Returns the count.
-    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane) const {
+    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane, int cap = kListCap) const {
         int mine = 0;
 #pragma unroll
         for (int i = 0; i < NE; ++i) mine += (h[i] >= x) ? 1 : 0;
         const int incl = wave_incl_scan(mine);
         const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        if (total <= kListCap) {
+        if (total <= cap) {
             const int spare = kListCap + lane;
             int o = incl - mine;  // < total for every id this lane writes
 #pragma unroll
@@ -82,6 +90,19 @@ struct Row {
         }
         __builtin_amdgcn_wave_barrier();
         return total;
+    }
+
+    // Add every id to a per-wave LDS histogram: bin b = trunc(clamp(fma(h,
+    // scale, off), low, kHistTop)).  The caller places the range of interest on
+    // bins [kHistLow, kHistLow + kHistBins); `low` = kHistLow - 1 - lane sends
+    // the ids below it to a bin of the lane's own, so they do not pile onto one
+    // address.
+    __device__ __forceinline__ void histogram(uint32_t* hist, float scale, float off, float low) const {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(h[i], scale, off), low, kHistTop);
+            __hip_atomic_fetch_add(&hist[(uint32_t)x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        }
     }
 };
 
@@ -113,6 +134,70 @@ __device__ __forceinline__ float min_finite(const Row<BF16, NS>& R) {
 #pragma unroll
     for (int i = 0; i < Row<BF16, NS>::NE; ++i) mn = R.h[i] > kNegInf ? __builtin_fminf(mn, R.h[i]) : mn;
     return wave_min(mn);
+}
+
+// A top set of the row that holds the top-ratio set: the smallest float c such
+// that at least k ids have h >= c, up to the resolution of a histogram of the ids
+// at or above `lo` (lo < M).  kHistBins bins span [lo, M]; the bin holding the
+// k-th largest h is found from suffix counts, and c is the exact float at which
+// the binning predicate fma(h, scale, off) >= that bin's index turns true (it is
+// monotone in h), so count(h >= c) is that bin's suffix count, returned in n.
+// Returns false when the histogram cannot resolve the range (no finite scale)
+// or fewer than k ids reach it.  The histogram lives in the wave's list memory,
+// which the caller overwrites only after this returns.
+template <bool BF16, int NS>
+__device__ bool top_set_by_histogram(const Row<BF16, NS>& R, Entry* list, int k, float lo, float M, int lane,
+                                     float& c_out, int& n_out) {
+    const float scale = (float)kHistBins * __builtin_amdgcn_rcpf(M - lo);
+    const float off = __builtin_fmaf(-lo, scale, (float)kHistLow);
+    if (!(scale > 0.0f && scale < 1e30f) || !(__builtin_fabsf(off) < 1e30f)) return false;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(list);
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    // clear the range's bins (the spill bins below it are never read)
+    reinterpret_cast<u32x4_t*>(hist + kHistLow)[lane] = u32x4_t{0u, 0u, 0u, 0u};
+    asm volatile("" ::: "memory");
+    R.histogram(hist, scale, off, (float)(kHistLow - 1 - lane));
+    asm volatile("" ::: "memory");
+    // lane l holds bins 4l .. 4l+3 of the range; suffix counts from the top
+    const u32x4_t b = reinterpret_cast<const u32x4_t*>(hist + kHistLow)[lane];
+    asm volatile("" ::: "memory");
+    const int T = (int)(b.x + b.y + b.z + b.w);
+    const int incl = wave_incl_scan(T);
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (total < k) return false;
+    const int above = total - incl;  // ids in the bins of higher lanes
+    // the lane whose bins hold the k-th largest, then the bin inside it
+    const uint64_t m = ballot(above < k && above + T >= k);
+    const int ls = (int)__builtin_ctzll(m);
+    int jl = 0, nl = above + T;
+    if (above + (int)b.w >= k) {
+        jl = 3;
+        nl = above + (int)b.w;
+    } else if (above + (int)(b.w + b.z) >= k) {
+        jl = 2;
+        nl = above + (int)(b.w + b.z);
+    } else if (above + (int)(b.w + b.z + b.y) >= k) {
+        jl = 1;
+        nl = above + (int)(b.w + b.z + b.y);
+    }
+    const int j = 4 * ls + __builtin_amdgcn_readlane(jl, ls);
+    n_out = __builtin_amdgcn_readlane(nl, ls);
+    // smallest float c with fma(c, scale, off) >= kHistLow + j
+    const float J = (float)(kHistLow + j);
+    auto in_set = [&](uint32_t key) { return __builtin_fmaf(key_value(key), scale, off) >= J; };
+    uint32_t kc = order_key((J - off) * __builtin_amdgcn_rcpf(scale) + 0.0f);
+    int steps = 0;
+    while (in_set(kc - 1u) && steps < 64) {
+        --kc;
+        ++steps;
+    }
+    while (!in_set(kc) && steps < 64) {
+        ++kc;
+        ++steps;
+    }
+    if (steps >= 64 || !in_set(kc) || in_set(kc - 1u)) return false;
+    c_out = key_value(kc);
+    return true;
 }
 
 // Exact k-th largest of a wave's LDS list, given that the list holds every id
@@ -292,7 +377,8 @@ template <bool BF16, int NS, typename Src>
 __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src& src) {
     using R_t = Row<BF16, NS>;
     constexpr int NE = R_t::NE;
-    __shared__ Entry s_list[kWavesPerBlock][kListCap + kWave];  // + one spare entry per lane
+    // + one spare entry per lane; 16-byte aligned for the histogram's vector accesses
+    __shared__ __attribute__((aligned(16))) Entry s_list[kWavesPerBlock][kListCap + kWave];
 
     // every per-cell quantity below is wave-uniform (scalar registers); the grid
     // is (positions / 4, rows) with rows beyond 65535 folded into z
@@ -453,30 +539,53 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     float bz = kNegInf, bh = kNegInf;
     int be = 0x7FFFFFFF;
     bool decided = false;  // (bz, be, bh) is the row's winner, wave-uniform
+    // Race every id of a listed top set of n ids that holds the top-ratio set
+    // (all ids with h >= floor).  The winner is then the argmax over the kept
+    // ids as soon as it is kept itself, that is when fewer than top_k ids have a
+    // larger h (those all lie above it, so all are listed).  Only when it is not
+    // is the threshold found on the list, for a second race over the kept ids.
+    auto race_listed = [&](int n, float floor) {
+        gumbel_list(list, n, prune, false, inv_tau, nk, lane, bz, be, bh);
+        const int wl = wave_argmax(bz, be);
+        bh = readlane_f(bh, wl);
+        if (count_list_above(list, n, bh, lane) < k) {
+            decided = true;
+        } else {
+            bz = kNegInf;
+            bh = kNegInf;
+            be = 0x7FFFFFFF;
+            t = list_kth(list, n, k, floor, M, lane);
+            cthr = __builtin_fmaxf(t, prune);
+        }
+    };
     // Fast path: the ids that can still win.  If at most top_k of them reach
     // `prune`, they all lie inside the top-ratio set (fewer than top_k ids are
     // larger than any of them), so the filter is satisfied without locating its
-    // exact threshold.  Otherwise they are all raced: the winner is the argmax
-    // over every id, and it is inside the set when fewer than top_k ids have a
-    // larger h (those all lie above it, so all are listed).  Only when it is not
-    // is the threshold found among them and the race rerun over the kept ids.
-    // Rows flat next to tau * (Gmax - Gmin) overflow the list and take the exact
-    // search below.
+    // exact threshold.  Up to kRaceAll of them are all raced (race_listed: the
+    // race's winner is the argmax over every id, and it stands when it is kept).
     if (!want_t) {
-        const int nb = R.count_compact(prune, list, lane);
-        if (nb <= kListCap) {
+        const int cap = min(max(k, kRaceAll), kListCap);
+        const int nb = R.count_compact(prune, list, lane, cap);
+        if (nb <= cap) {
             n_list = nb;
-            if (nb > k) {
-                gumbel_list(list, nb, prune, false, inv_tau, nk, lane, bz, be, bh);
-                const int wl = wave_argmax(bz, be);
-                bh = readlane_f(bh, wl);
-                if (count_list_above(list, nb, bh, lane) < k) {
-                    decided = true;
+            if (nb > k) race_listed(nb, prune);
+        }
+    }
+    // More ids can still win (rows flat next to tau * (Gmax - Gmin)), or the
+    // threshold is wanted: a histogram of the ids above `prune` gives a top set
+    // of a little more than top_k ids, exactly, which is listed and raced (or
+    // searched for the threshold).
+    if (n_list < 0) {
+        float c;
+        int n;
+        if (top_set_by_histogram(R, list, k, prune, M, lane, c, n) && n <= kListCap) {
+            const int nc = R.count_compact(c, list, lane);
+            if (nc <= kListCap) {
+                n_list = nc;
+                if (!want_t) {
+                    race_listed(nc, c);
                 } else {
-                    bz = kNegInf;
-                    bh = kNegInf;
-                    be = 0x7FFFFFFF;
-                    t = list_kth(list, nb, k, prune, M, lane);
+                    t = list_kth(list, nc, k, c, M, lane);
                     cthr = __builtin_fmaxf(t, prune);
                 }
             }
