@@ -88,11 +88,28 @@ def kernel_name(w, kind: str) -> str:
     if kind == "reveal":
         return "k_reveal_topk"
     if kind == "draft":
-        return "k_greedy_parts+k_greedy_merge"
+        return draft_kernel(w)
     slots = ((w.vocab + 2) // 2 if w.dtype == "bf16" else w.vocab + 63) // 64
     if slots > (16 if w.dtype == "bf16" else 32):
         return "k_sample_parts+k_sample_merge"
     return "k_sample_small" if slots <= (9 if w.dtype == "bf16" else 16) else "k_sample_small_wide"
+
+
+def draft_kernel(w) -> str:
+    """The draft path's kernels, by the library's rule: one workgroup per row when
+    the rows fill every compute unit (whole rounds, or the last partial round
+    costing at most a tenth) and chunk edges fall on 16-byte pieces; otherwise
+    the parts + merge pair."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    epp = 8 if w.dtype == "bf16" else 4
+    L = -(-w.vocab // w.vocab_chunks)
+    rounds = -(-w.n_rows // cus)
+    if (w.n_rows >= cus and w.n_rows * 10 >= rounds * cus * 9 and w.vocab % epp == 0 and L % epp == 0
+            and w.vocab_chunks <= 64):
+        return "k_greedy_rows"
+    return "k_greedy_parts+k_greedy_merge"
 
 
 def make_workload(name: str):
@@ -252,9 +269,10 @@ def describe(w, kind: str) -> dict:
 
 
 def launches_per_step(w, kind: str) -> int:
-    """Kernel launches of one call: one for the wave-per-cell kernel, a parts and a
-    merge kernel for the streaming path (every workload here fits one batch)."""
-    return 1 if kernel_name(w, kind).startswith(("k_sample_small", "k_reveal")) else 2
+    """Kernel launches of one call: one for the wave-per-cell kernel and the
+    one-workgroup-per-row draft kernel, a parts and a merge kernel for the
+    streaming path (every workload here fits one batch)."""
+    return 1 if kernel_name(w, kind).startswith(("k_sample_small", "k_reveal", "k_greedy_rows")) else 2
 
 
 def auto_steps(r: "Runner", budget_s: float = SUITE_BUDGET_S) -> tuple:

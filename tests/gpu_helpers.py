@@ -103,15 +103,16 @@ def check_sample(w, got, ref: "oracle.SampleResult", *, check_threshold: bool = 
     return rep
 
 
-def run_greedy(x: np.ndarray, vocab_chunks: int, *, triples: bool = True):
+def run_greedy(x: np.ndarray, vocab_chunks: int, *, triples: bool = True, force_fallback: bool = False):
     import torch
 
     import vocab_wise_logit_amd as ds
 
     n, V = x.shape
     dtype = "bf16" if x.dtype == np.uint16 else "f32"
-    log(f"[gpu] ds_greedy_lse rows={n} V={V} dtype={dtype} chunks={vocab_chunks}")
-    with ds.Sampler(V, dtype, max_rows=1, max_positions=max(1, n), vocab_chunks=vocab_chunks) as smp:
+    log(f"[gpu] ds_greedy_lse rows={n} V={V} dtype={dtype} chunks={vocab_chunks} fallback={force_fallback}")
+    with ds.Sampler(V, dtype, max_rows=1, max_positions=max(1, n), vocab_chunks=vocab_chunks,
+                    force_fallback=force_fallback) as smp:
         out = smp.greedy_lse(to_dev(x), triples=triples)
         torch.cuda.synchronize()
     return [t.cpu().numpy() for t in out]

@@ -283,6 +283,35 @@ def test_repeat_calls_are_bitwise_identical():
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype,V,chunks,rows", [("bf16", 2504, 64, 256), ("bf16", 4096, 1, 512),
+                                                  ("f32", 1024, 4, 256), ("bf16", 2800, 7, 300)])
+def test_greedy_one_workgroup_per_row(dtype, V, chunks, rows):
+    # Rows that fill the GPU take one workgroup per row (no merge kernel); the
+    # shapes put chunk edges on 16-byte pieces, with a short and an empty last
+    # chunk at V=2504 / 64 chunks.  Planted ties straddle chunk edges and masked
+    # ids are -inf.  The same data through the parts + merge kernels must give
+    # the same ids and chunk maxima.
+    rng = np.random.default_rng(V + chunks)
+    x = rng.standard_normal((rows, V)).astype(np.float32) * 4
+    L = -(-V // chunks)
+    for r in range(0, rows, 7):
+        e = min(V - 1, L * int(rng.integers(1, max(2, chunks))))
+        x[r, e - 1] = x[r, e] = x[r].max() + 1.0  # tie across a chunk edge
+    x[::5, 3] = -np.inf
+    x[::11, :] = np.round(x[::11, :])  # rows with many equal values
+    if dtype == "bf16":
+        x = synth.bf16_from_f32(x)
+    ref = oracle.greedy_lse(x, vocab_chunks=chunks)
+    got = run_greedy(x, chunks)
+    check_greedy(x, got, ref, f"rows {dtype} V={V} chunks={chunks} rows={rows}")
+    fb = run_greedy(x, chunks, force_fallback=True)
+    check_greedy(x, fb, ref, f"parts {dtype} V={V} chunks={chunks} rows={rows}")
+    assert np.array_equal(got[0], fb[0])
+    assert np.array_equal(got[3][:, :, 0], fb[3][:, :, 0])
+    # id words are int32 bit patterns (an empty chunk's INT32_MAX reads as a NaN float)
+    assert np.array_equal(got[3][:, :, 2].copy().view(np.int32), fb[3][:, :, 2].copy().view(np.int32))
+
+
 @pytest.mark.parametrize("V,chunks", [(1, 1), (9, 4), (1025, 7), (1025, 1024), (5000, 3)])
 def test_greedy_lse_shapes_and_chunks(V, chunks):
     rng = np.random.default_rng(V)

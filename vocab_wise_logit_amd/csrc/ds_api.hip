@@ -33,6 +33,7 @@ struct ds_sampler {
     int32_t vocab_chunks;
     uint32_t flags;
     float z0;
+    int32_t cus;  // compute units of the device
 };
 
 namespace {
@@ -154,6 +155,8 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
             delete s;
             return hip_fail(dg.err, "hipSetDevice");
         }
+        if (hipDeviceGetAttribute(&s->cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || s->cus < 1)
+            s->cus = 1;
         const hipError_t e1 = hipMalloc(&s->ws_part, sizeof(ds::PartRec) * ds::kWorkParts);
         if (e1 != hipSuccess) {
             delete s;
@@ -400,6 +403,16 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
     a.triples = triples_out;
     const bool bf16 = s->dtype == DS_DTYPE_BF16;
     a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    // Rows that fill every compute unit (whole rounds of one row per unit, or
+    // enough rounds that the last partial one costs little) take one workgroup
+    // per row and no second kernel; otherwise rows are split into parts.
+    const int64_t rounds = (n_rows + s->cus - 1) / s->cus;
+    if (!(s->flags & DS_FLAG_FORCE_FALLBACK) && n_rows >= s->cus && n_rows * 10 >= rounds * s->cus * 9 &&
+        ds::greedy_rows_fits(bf16, s->vocab, s->vocab_chunks, logits)) {
+        const hipError_t e = ds::launch_greedy_rows(bf16, a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "greedy kernel launch");
+        return DS_OK;
+    }
     a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, n_rows);
     a.w.nparts = a.w.ppc * s->vocab_chunks;
     const int64_t slots = ds::kWorkParts / a.w.nparts;

@@ -217,6 +217,27 @@ __device__ __forceinline__ int wave_min_i(int x) {
                min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
+// The same reductions inside each row of 16 lanes (every lane of a row gets its
+// row's result).
+__device__ __forceinline__ float row16_max(float x) {
+    x = __builtin_fmaxf(x, dpp_f<kDppXor1>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppXor2>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    return __builtin_fmaxf(x, dpp_f<kDppMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    return x + dpp_f<kDppMirror>(x);
+}
+__device__ __forceinline__ int row16_min_i(int x) {
+    x = min(x, dpp_i<kDppXor1>(x));
+    x = min(x, dpp_i<kDppXor2>(x));
+    x = min(x, dpp_i<kDppHalfMirror>(x));
+    return min(x, dpp_i<kDppMirror>(x));
+}
+
 // Wave argmax of (z, id): larger z wins, equal z keeps the smaller id.  Returns
 // the winning lane's (z, id) in every lane, and the winning lane index.
 __device__ __forceinline__ int wave_argmax(float& z, int& id) {

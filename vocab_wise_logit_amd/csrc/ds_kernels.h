@@ -83,6 +83,15 @@ int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells);
 
 hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st);
 
+// One workgroup per row, no workspace (the draft path when its rows fill the
+// GPU).  Needs V and ceil(V / chunks) to be multiples of the ids per 16-byte
+// piece, at most kGreedyRowMaxChunks chunks and 16-byte aligned logits.
+constexpr int kGreedyRowThreads = 1024;
+constexpr int kGreedyRowU = 4;  // 16-byte pieces per thread per group
+constexpr int kGreedyRowMaxChunks = 64;
+bool greedy_rows_fits(bool bf16, int V, int chunks, const void* x);
+hipError_t launch_greedy_rows(bool bf16, const GreedyArgs& a, hipStream_t st);
+
 // Confidence reveal: one workgroup per request, its selected cells sorted in LDS.
 constexpr int kRevealThreads = 1024;
 constexpr int kRevealCap = 16384;        // cells one request may reveal

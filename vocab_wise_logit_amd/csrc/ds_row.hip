@@ -939,6 +939,153 @@ __global__ __launch_bounds__(kWave) void k_greedy_merge(GreedyArgs a) {
     }
 }
 
+// One workgroup per row for the draft path when the rows alone fill the GPU:
+// no second kernel and no workspace.  Each thread streams its pieces of one
+// vocabulary chunk after another, four 16-byte pieces in flight per group; at
+// the end of a chunk each wave reduces its lanes' (max, exp-sum, smallest
+// argmax) and writes one record to LDS, with no barrier, so the loads of the
+// next chunk follow at once.  After the row, lane j of the first wave folds
+// chunk j's wave records into its triple ([DRAFT] "Design and invariants"), and
+// the wave folds the triples into the row.  Chunk boundaries fall on piece
+// boundaries (the host checks V and ceil(V / chunks) are multiples of the ids
+// per piece and that rows start 16-byte aligned).
+template <bool BF16>
+__global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a) {
+    constexpr int EPP = Piece<BF16>::EPP;
+    constexpr int NTR = kGreedyRowThreads;
+    constexpr int NW = NTR / kWave;
+    constexpr int UR = kGreedyRowU;
+    __shared__ float s_m[kGreedyRowMaxChunks][NW];
+    __shared__ float s_s[kGreedyRowMaxChunks][NW];
+    __shared__ int s_id[kGreedyRowMaxChunks][NW];
+    const int64_t row = blockIdx.x;
+    const int V = a.V;
+    const int nch = a.vocab_chunks;
+    const int L = (V + nch - 1) / nch;
+    const gptr<u32x4> x16 = as_global<u32x4>((const char*)a.x + row * (int64_t)V * (BF16 ? 2 : 4));
+    const int t = (int)threadIdx.x;
+    const int lane = lane_id();
+    const int wv = t >> 6;
+    const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
+    for (int j = 0; j < nch; ++j) {
+        const int lo = min(V, j * L);
+        const int hi = min(V, lo + L);
+        const gptr<u32x4> xc = x16 + lo / EPP;
+        const int nq = (hi - lo) / EPP;
+        float m = kNegInf, acc = 0.0f;
+        int mid = 0x7FFFFFFF;
+        // Whole groups load without any test, so all their loads are in flight
+        // together; the chunk's last, partial group clamps its indices and
+        // selects -inf past the end (a load under a branch would make the
+        // compiler wait for the loads before it).
+        auto group = [&](int base, auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            u32x4 raw[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int jp = base + u * NTR + t;
+                if (FULL) {
+                    raw[u] = xc[jp];
+                } else {
+                    raw[u] = xc[min(jp, nq - 1)];
+                    if (jp >= nq) raw[u] = u32x4{ninf, ninf, ninf, ninf};
+                }
+            }
+            Piece<BF16> P[UR];
+            float pm[UR];
+            float gm = kNegInf;
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                decode_piece<BF16>(raw[u], raw[u], 0.0f, false, P[u]);
+                pm[u] = P[u].h[0];
+#pragma unroll
+                for (int e = 1; e < EPP; ++e) pm[u] = __builtin_fmaxf(pm[u], P[u].h[e]);
+                gm = __builtin_fmaxf(gm, pm[u]);
+            }
+            if (gm > m) {
+                // first piece, then first id, holding the new maximum
+                int id = 0x7FFFFFFF;
+#pragma unroll
+                for (int u = UR - 1; u >= 0; --u) {
+                    if (pm[u] == gm) {
+                        int e = EPP - 1;
+#pragma unroll
+                        for (int i = EPP - 1; i >= 0; --i)
+                            if (P[u].h[i] == gm) e = i;
+                        id = lo + (base + u * NTR + t) * EPP + e;
+                    }
+                }
+                acc *= __builtin_amdgcn_exp2f((m - gm) * kLog2e);
+                m = gm;
+                mid = id;
+            }
+            const float mL = (m > kNegInf) ? m * kLog2e : 0.0f;
+#pragma unroll
+            for (int u = 0; u < UR; ++u)
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(P[u].h[e], kLog2e, -mL));
+        };
+        int base = 0;
+        for (; base + NTR * UR <= nq; base += NTR * UR) group(base, std::true_type{});
+        if (base < nq) group(base, std::false_type{});
+        // undo the rounding of m * log2(e), then the wave's share of the chunk
+        if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
+        const float wm = wave_max(m);
+        const float ws = wave_sum((m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - wm) * kLog2e) : 0.0f);
+        const int wid = wave_min_i((wm > kNegInf && m == wm) ? mid : 0x7FFFFFFF);
+        if (lane == 0) {
+            s_m[j][wv] = wm;
+            s_s[j][wv] = ws;
+            s_id[j][wv] = wid;
+        }
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    // The first wave folds the records: lane l takes wave (l & 15)'s record of
+    // chunk 4g + (l >> 4), each row of 16 lanes reduces one chunk to its triple,
+    // and the triples fold into the row (larger max wins, equal maxima keep the
+    // smaller id, sums add in probability space).
+    float M = kNegInf, S = 0.0f;
+    int id = 0x7FFFFFFF;
+    for (int g = 0; g < nch; g += 4) {
+        const int c = g + (lane >> 4);
+        const int w = lane & 15;
+        float rm = kNegInf, rs = 0.0f;
+        int ri = 0x7FFFFFFF;
+        if (c < nch) {
+            rm = s_m[c][w];
+            rs = s_s[c][w];
+            ri = s_id[c][w];
+        }
+        const float mj = row16_max(rm);
+        const float sj = row16_sum((rm > kNegInf) ? rs * __builtin_amdgcn_exp2f((rm - mj) * kLog2e) : 0.0f);
+        const int idj = row16_min_i((mj > kNegInf && rm == mj) ? ri : 0x7FFFFFFF);
+        if (a.triples && w == 0 && c < nch) {
+            float* o = a.triples + ((int64_t)c * a.n_rows + row) * 3;
+            o[0] = mj;
+            o[1] = (mj > kNegInf) ? mj + __builtin_logf(sj) : kNegInf;
+            o[2] = __int_as_float(idj);
+        }
+        // fold this group's chunks (the first lane of each row) into the row
+        const bool lead = w == 0;
+        const float gm = wave_max(lead ? mj : kNegInf);
+        const float mn = __builtin_fmaxf(M, gm);
+        const float gs = wave_sum((lead && mj > kNegInf) ? sj * __builtin_amdgcn_exp2f((mj - mn) * kLog2e) : 0.0f);
+        const int gi = wave_min_i((lead && gm > kNegInf && mj == gm) ? idj : 0x7FFFFFFF);
+        if (mn > kNegInf) {
+            S = ((M > kNegInf) ? S * __builtin_amdgcn_exp2f((M - mn) * kLog2e) : 0.0f) + gs;
+            if (gm > M || (gm == M && gi < id)) id = gi;
+            M = mn;
+        }
+    }
+    if (lane == 0) {
+        const float lse = M + __builtin_logf(S);
+        a.token[row] = id;
+        a.lse[row] = lse;
+        a.logprob[row] = M - lse;
+    }
+}
+
 }  // namespace
 
 int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells) {
@@ -978,6 +1125,23 @@ hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d
         hipLaunchKernelGGL(k_sample_parts_dev<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
         hipLaunchKernelGGL(k_sample_merge_dev<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, d);
     }
+    return hipGetLastError();
+}
+
+bool greedy_rows_fits(bool bf16, int V, int chunks, const void* x) {
+    const int epp = bf16 ? 8 : 4;
+    if (V < 1 || chunks < 1 || chunks > kGreedyRowMaxChunks) return false;
+    const int L = (V + chunks - 1) / chunks;
+    return V % epp == 0 && L % epp == 0 && ((uintptr_t)x & 15u) == 0;
+}
+
+hipError_t launch_greedy_rows(bool bf16, const GreedyArgs& a, hipStream_t st) {
+    if (a.n_rows < 1 || a.n_rows > INT32_MAX || !greedy_rows_fits(bf16, a.V, a.vocab_chunks, a.x))
+        return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(k_greedy_rows<true>, dim3((unsigned)a.n_rows), dim3(kGreedyRowThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_greedy_rows<false>, dim3((unsigned)a.n_rows), dim3(kGreedyRowThreads), 0, st, a);
     return hipGetLastError();
 }
 
