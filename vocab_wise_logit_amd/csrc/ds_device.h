@@ -82,14 +82,19 @@ struct Words4 {
     uint32_t w0, w1, w2, w3;
 };
 
+// a ^ b ^ c in one gfx950 three-input bitwise instruction (truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return (uint32_t)__builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ Words4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
                                                 uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         const uint64_t pa = (uint64_t)0xD2511F53u * x0;
         const uint64_t pb = (uint64_t)0xCD9E8D57u * x2;
-        const uint32_t y0 = (uint32_t)(pb >> 32) ^ x1 ^ k0;
-        const uint32_t y2 = (uint32_t)(pa >> 32) ^ x3 ^ k1;
+        const uint32_t y0 = xor3((uint32_t)(pb >> 32), x1, k0);
+        const uint32_t y2 = xor3((uint32_t)(pa >> 32), x3, k1);
         x1 = (uint32_t)pb;
         x3 = (uint32_t)pa;
         x0 = y0;
