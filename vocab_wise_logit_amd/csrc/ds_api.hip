@@ -258,6 +258,8 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
                 rq.offs[n] = rel;
                 rq.scale[n] = guidance_scale[r];
                 rq.tau[n] = temperature[r];
+                // IEEE division, correctly rounded like the kernels' 1.0f / tau
+                rq.inv_tau[n] = temperature[r] > 0.0f ? 1.0f / temperature[r] : 0.0f;
                 // u position of the request's first cell: its own position, or the
                 // next compacted one (requests with guidance 0 read no u)
                 rq.uoff[n] = compact_u ? (int32_t)upos : (int32_t)(pos + rel);

@@ -299,6 +299,7 @@ struct ReqTable {
     int32_t offs[kMaxReqPerLaunch + 1];  // request starts, relative to pos0
     float scale[kMaxReqPerLaunch];
     float tau[kMaxReqPerLaunch];
+    float inv_tau[kMaxReqPerLaunch];  // 1 / tau (correctly rounded), 0 for greedy requests
     int32_t uoff[kMaxReqPerLaunch];  // u position of the request's first position
     uint32_t row_iter_hi[kMaxReqPerLaunch];  // iteration << 16
     uint32_t rid[kMaxReqPerLaunch];

@@ -798,7 +798,7 @@ __device__ __forceinline__ CellParams sample_cell(const SampleArgs& a, const Req
     cp.ucell = (int64_t)row * rq.Pu + rq.uoff[r] + (pl - rq.offs[r]);
     cp.s = rq.scale[r];
     cp.tau = rq.tau[r];
-    cp.inv_tau = inv_temperature(cp.tau);
+    cp.inv_tau = rq.inv_tau[r];
     cp.nk.k0 = a.k0;
     cp.nk.k1 = a.k1;
     cp.nk.t = (uint32_t)(pl - rq.offs[r]);

@@ -46,6 +46,22 @@ struct Entry {
     int e;
 };
 
+// Register-slot counts that get an instantiation, in increasing order; a row is
+// launched with the smallest that holds it.
+constexpr int kSlotSizes[] = {2, 4, 6, 9, 12, 16, 24, 32};
+// Slots of an NS-slot instantiation that every row it is launched for fills
+// completely: those of the next smaller instantiation (which the row did not fit,
+// so its dwords reach past them: for bf16, (V + 2) / 2 > 64 * prev implies
+// V >= 128 * prev, so even a row starting on a dword boundary has
+// (V + 1) / 2 >= 64 * prev dwords; for f32 V > 64 * prev).
+template <bool BF16, int NS>
+constexpr int kFullSlots = [] {
+    int prev = 0;
+    for (int n : kSlotSizes)
+        if (n < NS) prev = n;
+    return prev;
+}();
+
 template <bool BF16, int NS>
 struct Row {
     static constexpr int NE = BF16 ? 2 * NS : NS;
@@ -352,7 +368,7 @@ __device__ __forceinline__ bool locate(const ReqTable& rq, int pl, int row, Cell
     ci.ucell = (int64_t)row * rq.Pu + rq.uoff[r] + ci.t;
     ci.s = rq.scale[r];
     ci.tau = rq.tau[r];
-    ci.inv_tau = inv_temperature(ci.tau);
+    ci.inv_tau = rq.inv_tau[r];
     ci.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
     ci.rid = rq.rid[r];
     return true;
@@ -401,7 +417,12 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     Entry* list = s_list[wv];
 
     // ---------------------------------------------------------------- load
+    // Both rows' loads are issued before any of their data is used, so a guided
+    // cell waits for one memory latency, not two.  Dwords past a row read as 0
+    // (buffer range check); only the slots from kFullSlots<NS> on can hold them.
+    constexpr int FS = kFullSlots<BF16, NS>;
     R_t R;
+    const bool use_u = s != 0.0f;
     if (BF16) {
         const uintptr_t cb = (uintptr_t)a.c;
         // dword-aligned view of c
@@ -410,19 +431,21 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         const int64_t off = (g >> 1) * 4 - (int64_t)(cb & 3);  // byte offset of the row's first dword
         const int ndw = (par + V + 1) >> 1;
         R.ebase = 2 * lane - par;
-        uint32_t cw[NS];
+        uint32_t cw[NS], uw[NS];
         load_slots<NS>((const char*)a.c + off, lane, ndw, cw);
-        // dwords past the row read as 0; c becomes -inf there, which makes h -inf
-        // whatever u reads (guided maps the NaN of -inf - -inf back to -inf)
-#pragma unroll
-        for (int j = 0; j < NS; ++j) cw[j] = (lane + j * kWave < ndw) ? cw[j] : 0xFF80FF80u;
-        if (s != 0.0f) {
+        int upar = par;
+        if (use_u) {
             // u's row (its own cell: a compacted u layout moves it) in its own
             // dword frame; the same as c's unless its start is on the other half
-            uint32_t uw[NS];
             const uintptr_t ub = (uintptr_t)a.u + (uintptr_t)(ci.ucell * V) * 2u;
-            const int upar = (int)((ub >> 1) & 1u);
+            upar = (int)((ub >> 1) & 1u);
             load_slots<NS>((const char*)(ub - 2u * (uintptr_t)upar), lane, (upar + V + 1) >> 1, uw);
+        }
+        // c becomes -inf past the row, which makes h -inf whatever u reads there
+        // (guided maps the NaN of -inf - -inf back to -inf)
+#pragma unroll
+        for (int j = FS; j < NS; ++j) cw[j] = (lane + j * kWave < ndw) ? cw[j] : 0xFF80FF80u;
+        if (use_u) {
             if (upar != par) realign_u<NS>(uw, par == 0, lane);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
@@ -436,23 +459,23 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
                 R.h[2 * j + 1] = bf16_hi(cw[j]);
             }
         }
-        // the two half-dwords that belong to the neighbouring rows
+        // the two half-dwords that belong to the neighbouring rows (the last
+        // dword lies in a slot from FS on)
         if (par && lane == 0) R.h[0] = kNegInf;
         if ((par + V) & 1) {
             const int dl = ndw - 1;
 #pragma unroll
-            for (int j = 0; j < NS; ++j)
+            for (int j = FS; j < NS; ++j)
                 if (j == (dl >> 6) && lane == (dl & 63)) R.h[2 * j + 1] = kNegInf;
         }
     } else {
         R.ebase = lane;
-        uint32_t cw[NS];
+        uint32_t cw[NS], uw[NS];
         load_slots<NS>((const float*)a.c + cell * V, lane, V, cw);
+        if (use_u) load_slots<NS>((const float*)a.u + ci.ucell * V, lane, V, uw);
 #pragma unroll
-        for (int j = 0; j < NS; ++j) cw[j] = (lane + j * kWave < V) ? cw[j] : 0xFF800000u;
-        if (s != 0.0f) {
-            uint32_t uw[NS];
-            load_slots<NS>((const float*)a.u + ci.ucell * V, lane, V, uw);
+        for (int j = FS; j < NS; ++j) cw[j] = (lane + j * kWave < V) ? cw[j] : 0xFF800000u;
+        if (use_u) {
 #pragma unroll
             for (int j = 0; j < NS; ++j) R.h[j] = guided_raw(__uint_as_float(cw[j]), __uint_as_float(uw[j]), s);
         } else {
