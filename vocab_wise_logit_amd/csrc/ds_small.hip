@@ -586,8 +586,16 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     // larger than any of them), so the filter is satisfied without locating its
     // exact threshold.  Up to kRaceAll of them are all raced (race_listed: the
     // race's winner is the argmax over every id, and it stands when it is kept).
-    if (!want_t) {
-        const int cap = min(max(k, kRaceAll), kListCap);
+    // A count of the ids above `prune` among the first four register elements of
+    // every lane (a quarter to a ninth of the row, by ballots) tells rows with
+    // far more than `cap` of them apart; those skip the full count and go
+    // straight to the histogram, which handles any row.
+    const int cap = min(max(k, kRaceAll), kListCap);
+    int sub = 0;
+#pragma unroll
+    for (int i = 0; i < (NE < 4 ? NE : 4); ++i) sub += popc(ballot(R.h[i] >= prune));
+    const bool flat = sub * NE > 6 * cap;  // about 1.5 * cap ids expected
+    if (!want_t && !flat) {
         const int nb = R.count_compact(prune, list, lane, cap);
         if (nb <= cap) {
             n_list = nb;
