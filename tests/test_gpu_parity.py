@@ -229,7 +229,37 @@ def test_heavy_ties_and_extreme_top_k():
         w.c = synth.bf16_from_f32(np.round(f * 2) / 2)
         ref = oracle.sample_workload(w)
         check_sample(w, run_sample(w), ref)
+        check_sample(w, run_sample(w, threshold=False), ref)
         check_sample(w, run_sample(w, force_fallback=True), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_flat_rows_histogram_narrowing(dtype):
+    # Rows where far more than 256 ids can still win take the histogram
+    # narrowing in the wave-per-cell kernel: guidance 0 with wide temperatures,
+    # top_k from 1 to 500, a coarse grid that piles ties into the threshold's bin
+    # (its top set can pass the list and fall back to the exact search), and rows
+    # of one repeated value at a tiny temperature, whose range the histogram
+    # cannot resolve.  Each runs with and without the threshold output.
+    V = 1025
+    cases = [(103, [0.7, 1.2, 5.0], 3.0, None), (1, [2.0], 3.0, None), (500, [1.5, 40.0], 3.0, None),
+             (103, [3.0], 2.0, 0.5), (103, [1e-30, 1e-3], 0.0, None)]
+    for k, taus, sigma, grid in cases:
+        R = len(taus)
+        w = synth.diffusion(f"flat_{dtype}_k{k}_s{sigma}", seed=k + R, vocab=V, rows=2, seq_lens=[24] * R,
+                            dtype=dtype, sigma=max(sigma, 1.0), guidance=0.0, temperature=taus, top_k=k)
+        f = oracle.bf16_to_f32(w.c) if dtype == "bf16" else w.c.copy()
+        if sigma == 0.0:
+            f[:] = 1.25  # every id ties with the maximum
+        elif grid:
+            f = np.round(f / grid) * grid
+        w.c = synth.bf16_from_f32(f) if dtype == "bf16" else f.astype(np.float32)
+        ref = oracle.sample_workload(w)
+        got = run_sample(w)
+        check_sample(w, got, ref)
+        got2 = run_sample(w, threshold=False)
+        check_sample(w, got2, ref)
+        assert np.array_equal(got[0], got2[0])
 
 
 def test_many_requests_span_several_launches():

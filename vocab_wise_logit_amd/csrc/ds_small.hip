@@ -642,7 +642,13 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         if (!(lo < M)) lo = M - sd;
         float hi = M;
         int c_hi = -1;
-        for (int tries = 0; tries < 8; ++tries) {
+        // the search below keeps count(>= hi) < k, which fails at hi = M when at
+        // least k ids tie with the maximum: then the threshold is M itself
+        if (R.count_ge(M) >= k) {
+            t = M;
+            have_t = true;
+        }
+        for (int tries = 0; tries < 8 && !have_t; ++tries) {
             const int c_lo = R.count_compact(lo, list, lane);
             if (c_lo >= k && c_lo <= kListCap) {
                 t = list_kth(list, c_lo, k, lo, M, lane);
