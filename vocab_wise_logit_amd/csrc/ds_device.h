@@ -190,13 +190,21 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
+// The maximum is taken on order keys: an unsigned max with the DPP operand fused
+// into it is one instruction per step, where a float max needs the DPP value
+// canonicalised first; the four row results combine on the scalar unit.  A NaN
+// counts as -inf, as fmaxf would ignore it.
 __device__ __forceinline__ float wave_max(float x) {
-    x = __builtin_fmaxf(x, dpp_f<kDppXor1>(x));
-    x = __builtin_fmaxf(x, dpp_f<kDppXor2>(x));
-    x = __builtin_fmaxf(x, dpp_f<kDppHalfMirror>(x));
-    x = __builtin_fmaxf(x, dpp_f<kDppMirror>(x));
-    return __builtin_fmaxf(__builtin_fmaxf(readlane_f(x, 0), readlane_f(x, 16)),
-                           __builtin_fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+    uint32_t k = order_key(__builtin_fmaxf(x, kNegInf));
+    k = max(k, (uint32_t)dpp_i<kDppXor1>((int)k));
+    k = max(k, (uint32_t)dpp_i<kDppXor2>((int)k));
+    k = max(k, (uint32_t)dpp_i<kDppHalfMirror>((int)k));
+    k = max(k, (uint32_t)dpp_i<kDppMirror>((int)k));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)k, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)k, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)k, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)k, 48);
+    return key_value(max(max(r0, r1), max(r2, r3)));
 }
 __device__ __forceinline__ float wave_min(float x) {
     x = __builtin_fminf(x, dpp_f<kDppXor1>(x));
