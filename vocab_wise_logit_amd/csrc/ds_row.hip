@@ -213,8 +213,8 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
             cw[i] = u32x4{0u, 0u, 0u, 0u};
             uw[i] = cw[i];
             if (q <= q1) {
-                cw[i] = G.c16[q];
-                if (use_u) uw[i] = G.u16[q];
+                cw[i] = stream_load(G.c16 + q);
+                if (use_u) uw[i] = stream_load(G.u16 + q);
             }
         }
 #pragma unroll
@@ -436,15 +436,15 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
         for (int uu = 0; uu < U; ++uu) {
             const int j = it * NT * U + uu * NT + (int)threadIdx.x;
             if (!edge) {
-                R.c[uu] = pc[j];
-                if (use_u) R.u[uu] = pu[j];
+                R.c[uu] = stream_load(pc + j);
+                if (use_u) R.u[uu] = stream_load(pu + j);
             } else {
                 const uint32_t ninf = BF16 ? 0xFF80FF80u : 0xFF800000u;
                 R.c[uu] = u32x4{ninf, ninf, ninf, ninf};
                 R.u[uu] = R.c[uu];
                 if (j < nqi) {
-                    R.c[uu] = pc[j];
-                    if (use_u) R.u[uu] = pu[j];
+                    R.c[uu] = stream_load(pc + j);
+                    if (use_u) R.u[uu] = stream_load(pu + j);
                 }
             }
         }
@@ -985,9 +985,9 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
             for (int u = 0; u < UR; ++u) {
                 const int jp = base + u * NTR + t;
                 if (FULL) {
-                    raw[u] = xc[jp];
+                    raw[u] = stream_load(xc + jp);
                 } else {
-                    raw[u] = xc[min(jp, nq - 1)];
+                    raw[u] = stream_load(xc + min(jp, nq - 1));
                     if (jp >= nq) raw[u] = u32x4{ninf, ninf, ninf, ninf};
                 }
             }

@@ -345,7 +345,8 @@ __device__ __forceinline__ void load_slots(const void* base, int lane, int ndw, 
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, ndw * 4, kBufferRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (lane + j * kWave) * 4, 0, 0);
+    for (int j = 0; j < NS; ++j)
+        w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (lane + j * kWave) * 4, 0, kBufferNontemporal);
 }
 
 // What a wave needs to know about its cell (all wave-uniform).
