@@ -973,7 +973,11 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
         const gptr<u32x4> xc = x16 + lo / EPP;
         const int nq = (hi - lo) / EPP;
         float m = kNegInf, acc = 0.0f;
-        int mid = 0x7FFFFFFF;
+        // the first piece holding the thread's maximum: its index and raw
+        // dwords, searched for the first id only once the chunk is done (the
+        // maximum rises in most groups of random rows, in some lane of every wave)
+        int mq = 0;
+        u32x4 mraw = u32x4{ninf, ninf, ninf, ninf};
         // Whole groups load without any test, so all their loads are in flight
         // together; the chunk's last, partial group clamps its indices and
         // selects -inf past the end (a load under a branch would make the
@@ -1003,21 +1007,20 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
                 gm = __builtin_fmaxf(gm, pm[u]);
             }
             if (gm > m) {
-                // first piece, then first id, holding the new maximum
-                int id = 0x7FFFFFFF;
+                // first piece holding the new maximum (ids grow with u)
+                int pu = UR - 1;
+                u32x4 r = raw[UR - 1];
 #pragma unroll
-                for (int u = UR - 1; u >= 0; --u) {
+                for (int u = UR - 2; u >= 0; --u) {
                     if (pm[u] == gm) {
-                        int e = EPP - 1;
-#pragma unroll
-                        for (int i = EPP - 1; i >= 0; --i)
-                            if (P[u].h[i] == gm) e = i;
-                        id = lo + (base + u * NTR + t) * EPP + e;
+                        pu = u;
+                        r = raw[u];
                     }
                 }
+                mq = base + pu * NTR + t;
+                mraw = r;
                 acc *= __builtin_amdgcn_exp2f((m - gm) * kLog2e);
                 m = gm;
-                mid = id;
             }
             const float mL = (m > kNegInf) ? m * kLog2e : 0.0f;
 #pragma unroll
@@ -1032,7 +1035,18 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
         if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
         const float wm = wave_max(m);
         const float ws = wave_sum((m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - wm) * kLog2e) : 0.0f);
-        const int wid = wave_min_i((wm > kNegInf && m == wm) ? mid : 0x7FFFFFFF);
+        // the first id of the maximum's piece, in the lanes that hold the wave's maximum
+        int mid = 0x7FFFFFFF;
+        if (wm > kNegInf && m == wm) {
+            Piece<BF16> P;
+            decode_piece<BF16>(mraw, mraw, 0.0f, false, P);
+            int e = EPP - 1;
+#pragma unroll
+            for (int i = EPP - 1; i >= 0; --i)
+                if (P.h[i] == m) e = i;
+            mid = lo + mq * EPP + e;
+        }
+        const int wid = wave_min_i(mid);
         if (lane == 0) {
             s_m[j][wv] = wm;
             s_s[j][wv] = ws;
