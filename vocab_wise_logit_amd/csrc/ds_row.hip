@@ -51,15 +51,17 @@ struct WaveRec {
     int pad;
 };
 
-// Cross-wave reduction slots.
-struct Red {
-    float f[NWAVES];
-    float f2[NWAVES];
-    int i[NWAVES];
-    WaveRec w[NWAVES];
+// Cross-wave reduction slots of a block of NW_ waves.
+template <int NW_>
+struct RedT {
+    float f[NW_];
+    float f2[NW_];
+    int i[NW_];
+    WaveRec w[NW_];
     uint32_t bcast_u;
     int bcast_i;
 };
+using Red = RedT<NWAVES>;
 
 // A sampled part's Gumbel race queues, per wave: pieces holding an id at or
 // above the bound (their decoded h and first id), and ids at or above the bound.
@@ -81,21 +83,35 @@ struct PartLDS {
 constexpr int kDigitShift[3] = {21, 10, 0};
 constexpr int kDigitBits[3] = {11, 11, 10};
 constexpr int kHistBins = 2048;
-constexpr int kKeyCap = 8192;
+
+// The merge runs in one of two shapes.  When the call asks for no threshold, a
+// row's merge almost always only folds its part records, so the kernel is
+// latency-bound: small blocks with little LDS let every row of a launch run at
+// once.  When every row needs the exact select, larger blocks keep more keys of
+// the threshold's first-digit bin in LDS, which saves passes over the row.
+constexpr int kMergeStage = 64;    // part records staged in LDS at a time
+constexpr int kMergeThreadsFast = 256;
+constexpr int kKeyCapFast = 2048;
+constexpr int kMergeThreadsExact = 512;
+constexpr int kKeyCapExact = 8192;
 
 // The merge's staged part records (or the threshold select's keys) and histogram.
+template <int MT_, int KCAP>
 struct MergeLDS {
+    static constexpr int kThreads = MT_;
+    static constexpr int kKeyCap = KCAP;
     union {
-        PartRec rec[NT];
-        uint32_t keys[kKeyCap];
+        PartRec rec[kMergeStage];
+        uint32_t keys[KCAP];
     } u;
     uint32_t hist[kHistBins];
     int nkeys;
-    Red r;
+    RedT<MT_ / kWave> r;
 };
 
 // Block argmax of (z, id, h): larger z, then smaller id.
-__device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Red& r) {
+template <int NW_>
+__device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, RedT<NW_>& r) {
     const int wl = wave_argmax(z, id);
     hv = readlane_f(hv, wl);
     const int w = threadIdx.x >> 6;
@@ -110,7 +126,7 @@ __device__ __forceinline__ void block_argmax3(float& z, int& id, float& hv, Red&
     id = r.i[0];
     hv = r.f2[0];
 #pragma unroll
-    for (int i = 1; i < NWAVES; ++i) {
+    for (int i = 1; i < NW_; ++i) {
         const bool take = (r.f[i] > z) || (r.f[i] == z && r.i[i] < id);
         z = take ? r.f[i] : z;
         id = take ? r.i[i] : id;
@@ -199,17 +215,17 @@ struct PartRange {
 // Visit every id of the row: f(v, h).  Used by the exact multi-pass path; four
 // pieces per thread are loaded before any is decoded, so that a single
 // workgroup keeps enough loads in flight to stream its row.
-template <bool BF16, typename F>
+template <bool BF16, int BT, typename F>
 __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_u, F&& f) {
     constexpr int EPP = Piece<BF16>::EPP;
     constexpr int UF = 4;
     const int64_t q0 = G.gbase / EPP;
     const int64_t q1 = (G.gbase + G.V - 1) / EPP;
-    for (int64_t qb = q0 + threadIdx.x; qb <= q1; qb += (int64_t)NT * UF) {
+    for (int64_t qb = q0 + threadIdx.x; qb <= q1; qb += (int64_t)BT * UF) {
         u32x4 cw[UF], uw[UF];
 #pragma unroll
         for (int i = 0; i < UF; ++i) {
-            const int64_t q = qb + (int64_t)i * NT;
+            const int64_t q = qb + (int64_t)i * BT;
             cw[i] = u32x4{0u, 0u, 0u, 0u};
             uw[i] = cw[i];
             if (q <= q1) {
@@ -219,7 +235,7 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
         }
 #pragma unroll
         for (int i = 0; i < UF; ++i) {
-            const int64_t q = qb + (int64_t)i * NT;
+            const int64_t q = qb + (int64_t)i * BT;
             if (q > q1) break;
             Piece<BF16> P;
             decode_piece<BF16>(cw[i], uw[i], s, use_u, P);
@@ -233,10 +249,11 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
 
 // The digit (histogram bin) holding the kk-th largest key among those counted
 // in sh.hist[0, nbins), with 1 <= kk <= their number; kk becomes the rank inside
-// that bin.  Thread j owns bins nbins-1-j*b .. nbins-b-j*b (b = nbins / NT), so a
-// block prefix sum over the threads counts the keys in higher bins.
-__device__ uint32_t find_digit(MergeLDS& sh, int nbins, int& kk) {
-    const int bpt = nbins / NT;
+// that bin.  Thread j owns bins nbins-1-j*b .. nbins-b-j*b (b = nbins / threads),
+// so a block prefix sum over the threads counts the keys in higher bins.
+template <typename SH>
+__device__ uint32_t find_digit(SH& sh, int nbins, int& kk) {
+    const int bpt = nbins / SH::kThreads;
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
     int own = 0;
@@ -289,22 +306,23 @@ __device__ __forceinline__ int wave_append(bool pred, int* counter) {
 // keys in the chosen bin into LDS, where the last two digits are selected.  If
 // that bin holds more than kKeyCap keys, the last digits take a pass over the
 // row each instead.
-template <bool BF16>
-__device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, MergeLDS& sh) {
+template <bool BF16, typename SH>
+__device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, SH& sh) {
+    constexpr int BT = SH::kThreads;
     uint32_t prefix = 0, pmask = 0;
     int kk = k;
     auto hist_pass = [&](int dg, bool from_lds, int n) {
         const int shift = kDigitShift[dg];
         const uint32_t dmask = (1u << kDigitBits[dg]) - 1u;
-        for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
+        for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
         __syncthreads();
         if (from_lds) {
-            for (int i = threadIdx.x; i < n; i += NT) {
+            for (int i = threadIdx.x; i < n; i += BT) {
                 const uint32_t key = sh.u.keys[i];
                 if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
             }
         } else {
-            for_each_id<BF16>(G, s, use_u, [&](int, float h) {
+            for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
                 const uint32_t key = order_key(h + 0.0f);
                 if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
             });
@@ -318,14 +336,14 @@ __device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, 
     // keep the keys that share the first digit with the answer
     if (threadIdx.x == 0) sh.nkeys = 0;
     __syncthreads();
-    for_each_id<BF16>(G, s, use_u, [&](int, float h) {
+    for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
         const uint32_t key = order_key(h + 0.0f);
         const int at = wave_append((key & pmask) == prefix, &sh.nkeys);
-        if (at >= 0 && at < kKeyCap) sh.u.keys[at] = key;
+        if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = key;
     });
     __syncthreads();
     const int n = sh.nkeys;
-    const bool fit = n <= kKeyCap;
+    const bool fit = n <= SH::kKeyCap;
     hist_pass(1, fit, n);
     hist_pass(2, fit, n);
     return key_value(prefix);
@@ -680,11 +698,11 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
 // Kernel 2 body: merge the row's partial records ([DRAFT]: larger max wins,
 // equal maxima keep the smaller id, sums add in probability space), then finish
 // the greedy or sampled decision.
-template <bool BF16, bool SAMPLE>
+template <bool BF16, bool SAMPLE, int MT_, int KCAP>
 __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, int top_k, bool force_fallback,
                            const RowWork& w, const CellParams& cp, int64_t slot, int* tokens, float* logprobs,
                            float* lse_out, float* thresholds, float* triples, int64_t n_rows) {
-    __shared__ MergeLDS sh;
+    __shared__ MergeLDS<MT_, KCAP> sh;
     const bool use_u = SAMPLE && cp.s != 0.0f;
     const bool sampled = SAMPLE && cp.tau != 0.0f;
     const PartRec* recs = w.part + slot * w.nparts;
@@ -695,11 +713,11 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
     int be = 0x7FFFFFFF;
     int64_t queued = 0;
     bool raced = sampled && !force_fallback;
-    // records in chunk-major order, staged through LDS NT at a time
+    // records in chunk-major order, staged through LDS kMergeStage at a time
     float mj = kNegInf, sj = 0.0f;
     int idj = 0x7FFFFFFF;
-    for (int t0 = 0; t0 < w.nparts; t0 += NT) {
-        const int n = min(NT, w.nparts - t0);
+    for (int t0 = 0; t0 < w.nparts; t0 += kMergeStage) {
+        const int n = min(kMergeStage, w.nparts - t0);
         __syncthreads();
         if ((int)threadIdx.x < n) sh.u.rec[threadIdx.x] = recs[t0 + threadIdx.x];
         __syncthreads();
@@ -770,7 +788,7 @@ __device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, i
         bz = kNegInf;
         be = 0x7FFFFFFF;
         bh = kNegInf;
-        for_each_id<BF16>(G, cp.s, use_u, [&](int v, float hv) {
+        for_each_id<BF16, MT_>(G, cp.s, use_u, [&](int v, float hv) {
             if (!(hv >= cthr)) return;
             const float z = __builtin_fmaf(hv, cp.inv_tau, gumbel_from_word(noise_word(cp.nk, (uint32_t)v)));
             if (z > bz || (z == bz && v < be)) {
@@ -850,11 +868,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void
     part_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot), slot,
                           part);
 }
-template <bool BF16>
-__global__ __launch_bounds__(NT) void k_sample_merge(SampleArgs a, ReqTable rq) {
+template <bool BF16, int MT_, int KCAP>
+__global__ __launch_bounds__(MT_) void k_sample_merge(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x;
-    merge_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
-                           sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr, a.thresholds, nullptr, 0);
+    merge_body<BF16, true, MT_, KCAP>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
+                                      sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr, a.thresholds,
+                                      nullptr, 0);
 }
 // The same two kernels with the per-request parameters in device memory.
 template <bool BF16>
@@ -865,13 +884,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void
     if (!sample_cell_dev(a, d, slot, cp)) return;
     part_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part);
 }
-template <bool BF16>
-__global__ __launch_bounds__(NT) void k_sample_merge_dev(SampleArgs a, DevReq d) {
+template <bool BF16, int MT_, int KCAP>
+__global__ __launch_bounds__(MT_) void k_sample_merge_dev(SampleArgs a, DevReq d) {
     const int64_t slot = blockIdx.x;
     CellParams cp;
     if (!sample_cell_dev(a, d, slot, cp)) return;
-    merge_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w, cp, slot, a.tokens,
-                           a.logprobs, nullptr, a.thresholds, nullptr, 0);
+    merge_body<BF16, true, MT_, KCAP>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w, cp, slot,
+                                      a.tokens, a.logprobs, nullptr, a.thresholds, nullptr, 0);
 }
 template <bool BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_greedy_parts(GreedyArgs a) {
@@ -1118,12 +1137,24 @@ int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells) {
 hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
     const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
     if (parts == 0) return hipSuccess;
+    const dim3 mg((unsigned)a.w.ncells);
+    const bool exact = a.thresholds != nullptr || a.force_fallback != 0;  // every row selects its threshold
     if (bf16) {
         hipLaunchKernelGGL(k_sample_parts<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
-        hipLaunchKernelGGL(k_sample_merge<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, rq);
+        if (exact)
+            hipLaunchKernelGGL((k_sample_merge<true, kMergeThreadsExact, kKeyCapExact>), mg, dim3(kMergeThreadsExact),
+                               0, st, a, rq);
+        else
+            hipLaunchKernelGGL((k_sample_merge<true, kMergeThreadsFast, kKeyCapFast>), mg, dim3(kMergeThreadsFast), 0,
+                               st, a, rq);
     } else {
         hipLaunchKernelGGL(k_sample_parts<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
-        hipLaunchKernelGGL(k_sample_merge<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, rq);
+        if (exact)
+            hipLaunchKernelGGL((k_sample_merge<false, kMergeThreadsExact, kKeyCapExact>), mg,
+                               dim3(kMergeThreadsExact), 0, st, a, rq);
+        else
+            hipLaunchKernelGGL((k_sample_merge<false, kMergeThreadsFast, kKeyCapFast>), mg, dim3(kMergeThreadsFast),
+                               0, st, a, rq);
     }
     return hipGetLastError();
 }
@@ -1132,12 +1163,24 @@ hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d
     const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
     if (parts == 0) return hipSuccess;
     if (d.n < 1 || d.n > kWave || d.P < 1) return hipErrorInvalidValue;
+    const dim3 mg((unsigned)a.w.ncells);
+    const bool exact = a.thresholds != nullptr || a.force_fallback != 0;  // every row selects its threshold
     if (bf16) {
         hipLaunchKernelGGL(k_sample_parts_dev<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
-        hipLaunchKernelGGL(k_sample_merge_dev<true>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, d);
+        if (exact)
+            hipLaunchKernelGGL((k_sample_merge_dev<true, kMergeThreadsExact, kKeyCapExact>), mg,
+                               dim3(kMergeThreadsExact), 0, st, a, d);
+        else
+            hipLaunchKernelGGL((k_sample_merge_dev<true, kMergeThreadsFast, kKeyCapFast>), mg,
+                               dim3(kMergeThreadsFast), 0, st, a, d);
     } else {
         hipLaunchKernelGGL(k_sample_parts_dev<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
-        hipLaunchKernelGGL(k_sample_merge_dev<false>, dim3((unsigned)a.w.ncells), dim3(NT), 0, st, a, d);
+        if (exact)
+            hipLaunchKernelGGL((k_sample_merge_dev<false, kMergeThreadsExact, kKeyCapExact>), mg,
+                               dim3(kMergeThreadsExact), 0, st, a, d);
+        else
+            hipLaunchKernelGGL((k_sample_merge_dev<false, kMergeThreadsFast, kKeyCapFast>), mg,
+                               dim3(kMergeThreadsFast), 0, st, a, d);
     }
     return hipGetLastError();
 }
