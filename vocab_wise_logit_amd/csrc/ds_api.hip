@@ -274,6 +274,10 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         rq.n = n;
         rq.offs[n] = rel;
         rq.npos = rel;
+        // u can be loaded before the request lookup when every request reads it
+        // at its own position
+        rq.all_guided = compact_u ? 0 : 1;
+        for (int32_t i = 0; i < n; ++i) rq.all_guided &= rq.scale[i] != 0.0f ? 1 : 0;
         if (small) {
             const hipError_t e = ds::launch_sample_small(bf16, a, rq, st);
             if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");

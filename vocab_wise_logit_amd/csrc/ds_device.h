@@ -311,6 +311,7 @@ struct ReqTable {
     int32_t npos;     // positions covered
     int32_t P;        // total packed positions of the call
     int32_t Pu;       // positions of the u layout: P, or the guided positions when u is compacted
+    int32_t all_guided;  // every request of the launch reads u at its own position (no compaction)
     int32_t offs[kMaxReqPerLaunch + 1];  // request starts, relative to pos0
     float scale[kMaxReqPerLaunch];
     float tau[kMaxReqPerLaunch];

@@ -362,7 +362,7 @@ struct CellInfo {
 // The cell at launch-relative position pl of `row`, from the kernel-argument
 // table; false past the launch's positions.
 __device__ __forceinline__ bool locate(const ReqTable& rq, int pl, int row, CellInfo& ci) {
-    if (pl >= rq.npos) return false;
+    if (pl >= rq.npos) return false;  // (the kernel checks first)
     const int r = find_request(rq, pl);
     ci.cell = (int64_t)row * rq.P + rq.pos0 + pl;
     ci.t = (uint32_t)(pl - rq.offs[r]);  // offs are launch-relative
@@ -404,17 +404,21 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     const int pl = (int)blockIdx.x * kWavesPerBlock + wv;
     const int row = (int)(blockIdx.z * gridDim.y + blockIdx.y);
     if (row >= a.rows) return;  // whole wave leaves together
-    CellInfo ci;
-    bool here;
-    if constexpr (std::is_same<Src, DevReq>::value)
-        here = locate(src, a.u != nullptr, pl, row, ci);
-    else
-        here = locate(src, pl, row, ci);
-    if (!here) return;  // past the positions in use: the whole wave leaves
-    const int64_t cell = ci.cell;
+    constexpr bool kTable = !std::is_same<Src, DevReq>::value;
+    // With the table, a cell's rows are known before its request is: c's loads,
+    // and u's when every request of the launch reads u at its own position, go
+    // out before the request lookup.
+    bool early_u = false;
+    int64_t cell;
+    if constexpr (kTable) {
+        if (pl >= src.npos) return;  // past the launch's positions: the whole wave leaves
+        cell = (int64_t)row * src.P + src.pos0 + pl;
+        early_u = src.all_guided != 0;
+    } else {
+        if (pl >= src.P) return;  // past the fixed layout (the grid rounds up to whole blocks)
+        cell = (int64_t)row * src.P + pl;
+    }
     const int V = a.V;
-    const float s = ci.s;
-    const float tau = ci.tau;
     Entry* list = s_list[wv];
 
     // ---------------------------------------------------------------- load
@@ -422,26 +426,47 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     // cell waits for one memory latency, not two.  Dwords past a row read as 0
     // (buffer range check); only the slots from kFullSlots<NS> on can hold them.
     constexpr int FS = kFullSlots<BF16, NS>;
-    R_t R;
-    const bool use_u = s != 0.0f;
+    uint32_t cw[NS], uw[NS];
+    // bf16: the row in c's dword frame (its first id in the high half when par)
+    int par = 0, ndw = V;
     if (BF16) {
         const uintptr_t cb = (uintptr_t)a.c;
-        // dword-aligned view of c
         const int64_t g = (int64_t)((cb & 3) >> 1) + cell * V;
-        const int par = (int)(g & 1);
+        par = (int)(g & 1);
         const int64_t off = (g >> 1) * 4 - (int64_t)(cb & 3);  // byte offset of the row's first dword
-        const int ndw = (par + V + 1) >> 1;
-        R.ebase = 2 * lane - par;
-        uint32_t cw[NS], uw[NS];
+        ndw = (par + V + 1) >> 1;
         load_slots<NS>((const char*)a.c + off, lane, ndw, cw);
-        int upar = par;
-        if (use_u) {
-            // u's row (its own cell: a compacted u layout moves it) in its own
-            // dword frame; the same as c's unless its start is on the other half
-            const uintptr_t ub = (uintptr_t)a.u + (uintptr_t)(ci.ucell * V) * 2u;
+    } else {
+        load_slots<NS>((const float*)a.c + cell * V, lane, V, cw);
+    }
+    // u's row (its own cell: a compacted u layout moves it), in its own dword frame
+    // for bf16: the same as c's unless its start is on the other half
+    int upar = par;
+    auto load_u = [&](int64_t ucell) {
+        if (BF16) {
+            const uintptr_t ub = (uintptr_t)a.u + (uintptr_t)(ucell * V) * 2u;
             upar = (int)((ub >> 1) & 1u);
             load_slots<NS>((const char*)(ub - 2u * (uintptr_t)upar), lane, (upar + V + 1) >> 1, uw);
+        } else {
+            load_slots<NS>((const float*)a.u + ucell * V, lane, V, uw);
         }
+    };
+    if (early_u) load_u(cell);
+    CellInfo ci;
+    bool here;
+    if constexpr (kTable)
+        here = locate(src, pl, row, ci);
+    else
+        here = locate(src, a.u != nullptr, pl, row, ci);
+    if (!here) return;  // padding position of the fixed layout: the whole wave leaves
+    const float s = ci.s;
+    const float tau = ci.tau;
+    const bool use_u = s != 0.0f;
+    if (use_u && !early_u) load_u(ci.ucell);
+
+    R_t R;
+    if (BF16) {
+        R.ebase = 2 * lane - par;
         // c becomes -inf past the row, which makes h -inf whatever u reads there
         // (guided maps the NaN of -inf - -inf back to -inf)
 #pragma unroll
@@ -471,9 +496,6 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         }
     } else {
         R.ebase = lane;
-        uint32_t cw[NS], uw[NS];
-        load_slots<NS>((const float*)a.c + cell * V, lane, V, cw);
-        if (use_u) load_slots<NS>((const float*)a.u + ci.ucell * V, lane, V, uw);
 #pragma unroll
         for (int j = FS; j < NS; ++j) cw[j] = (lane + j * kWave < V) ? cw[j] : 0xFF800000u;
         if (use_u) {
