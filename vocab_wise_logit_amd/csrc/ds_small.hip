@@ -2,21 +2,25 @@
 //
 // Each 64-lane wave owns one cell (row, position) of the packed [C, P, V] logits
 // and holds the whole guided row h[0..V) in VGPRs (dword slots of two bf16 or one
-// f32 per lane).  Everything after the load is register / LDS work:
+// f32 per lane).  The row's loads (c, and u for guided cells) go out before any
+// of their data is used; everything after them is register / LDS work:
 //   1. h = CFG combine ([ISSUE] comment on the API shape; [PR] "What does this PR
 //      do?": guidance 0 never reads u), row max, log-sum-exp;
 //   2. greedy cells (temperature 0): token = smallest-id argmax, logprob =
 //      max - LSE;
-//   3. sampled cells: the exact top_k-th largest h ([ISSUE] top-ratio filter),
-//      found by counting ids above pivots; the ids above the final pivot are
-//      compacted into a per-wave LDS list (per-lane counts and a wave prefix
-//      sum), so refinement runs on a few registers instead of the whole row;
-//   4. Gumbel-max ([ISSUE]) over the kept ids that can still win: an id whose
+//   3. sampled cells, Gumbel-max ([ISSUE]) over the top-ratio set: an id whose
 //      h/tau + max-noise is below the argmax's h/tau + min-noise never wins, so
-//      only ids with h >= max(t, M - tau * (Gmax - Gmin)) draw Philox noise.
-//      When more than top_k ids can win, all of them are raced before any
-//      threshold is located: the winner stands if fewer than top_k ids have a
-//      larger h, and step 3 runs only when it does not.
+//      only ids with h >= M - tau * (Gmax - Gmin) are candidates.  They are
+//      compacted into a per-wave LDS list (per-lane counts and a wave prefix sum)
+//      and raced, 64 Philox draws at a time.  If at most top_k ids are
+//      candidates they all lie inside the top-ratio set; otherwise the winner
+//      stands when fewer than top_k ids have a larger h.
+//   4. rows with many candidates (flat rows) first narrow them: a per-wave LDS
+//      histogram over [M - tau * (Gmax - Gmin), M] yields the exact float edge
+//      of a top set holding the top-ratio set with a few ids to spare, which is
+//      listed and raced as in 3.  The exact top_k-th largest h ([ISSUE]
+//      top-ratio filter) is located on that list only when the race's winner is
+//      not kept or the caller asks for the threshold.
 // Ties: smallest id for the greedy argmax and for exact Gumbel ties ([DRAFT]
 // "Design and invariants" rule, applied to every decision).
 #include <stdint.h>
