@@ -205,6 +205,11 @@ int ds_sample_device_params(ds_sampler *s, const int64_t *request_ids, const voi
  *                float word (reinterpret, never convert); an empty chunk is
  *                (-inf, -inf, INT32_MAX).
  *   stream       hipStream_t.
+ * Launch shape (results do not depend on it): when the rows fill every compute
+ * unit in whole rounds, V and ceil(V / vocab_chunks) are multiples of the ids
+ * in 16 bytes and logits is 16-byte aligned, one workgroup reduces each row in a
+ * single kernel; otherwise parts of rows are reduced into the handle's
+ * workspace and merged by a second kernel.
  */
 int ds_greedy_lse(ds_sampler *s, const void *logits, int64_t n_rows, int32_t *token_out,
                   float *lse_out, float *logprob_out, float *triples_out, void *stream);
