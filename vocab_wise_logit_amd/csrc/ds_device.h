@@ -259,14 +259,19 @@ __device__ __forceinline__ int row16_min_i(int x) {
 }
 
 // Wave argmax of (z, id): larger z wins, equal z keeps the smaller id.  Returns
-// the winning lane's (z, id) in every lane, and the winning lane index.
+// the winning lane's (z, id) in every lane, and the winning lane index.  The
+// id reduction runs only when several lanes hold the maximum.
 __device__ __forceinline__ int wave_argmax(float& z, int& id) {
     const float zm = wave_max(z);
-    const int im = wave_min_i(z == zm ? id : 0x7FFFFFFF);
-    const uint64_t m = __ballot(z == zm && id == im);
+    uint64_t m = __ballot(z == zm);
+    if (__popcll(m) > 1) {
+        const int im = wave_min_i(z == zm ? id : 0x7FFFFFFF);
+        m = __ballot(z == zm && id == im);
+    }
+    const int l = (int)__builtin_ctzll(m);
     z = zm;
-    id = im;
-    return (int)__builtin_ctzll(m);
+    id = __builtin_amdgcn_readlane(id, l);
+    return l;
 }
 
 // Inclusive prefix sum over lanes 0..lane: four shifted adds inside each row of

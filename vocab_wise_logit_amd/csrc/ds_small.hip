@@ -86,30 +86,24 @@ struct Row {
         return n;
     }
 
-    // Count the ids whose h is >= x and, if there are at most `cap` (<= kListCap)
-    // of them, write them to `list` as (h, id).  Each lane counts its own ids, a
-    // wave prefix sum places each lane's run, and the lane writes its ids there in
-    // register order.  Every lane stores every slot, the ids below x to its own
-    // spare entry past kListCap, so the pass has no per-slot ballot or branch.
-    // Returns the count.
-    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane, int cap = kListCap) const {
-        int mine = 0;
+    // Count the ids whose h is >= x and list them in `list` as (h, id), slot by
+    // slot: a ballot per register slot gives each lane holding such an id its
+    // place (the slot's earlier lanes, after the earlier slots' ids).  Once more
+    // than `cap` (<= kListCap) ids are found the remaining slots are only
+    // counted, so a slot is written only when the count before it is <= cap and
+    // the list's kWave spare entries past kListCap hold its last ids.  Returns
+    // the count; the list is complete when it is <= cap.
+    __device__ __forceinline__ int count_compact(float x, Entry* list, int cap = kListCap) const {
+        int base = 0;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) mine += (h[i] >= x) ? 1 : 0;
-        const int incl = wave_incl_scan(mine);
-        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        if (total <= cap) {
-            const int spare = kListCap + lane;
-            int o = incl - mine;  // < total for every id this lane writes
-#pragma unroll
-            for (int i = 0; i < NE; ++i) {
-                const bool p = h[i] >= x;
-                list[p ? o : spare] = Entry{h[i], id_of(i)};
-                o += p ? 1 : 0;
-            }
+        for (int i = 0; i < NE; ++i) {
+            const bool p = h[i] >= x;
+            const uint64_t m = ballot(p);
+            if (base <= cap && p) list[base + lanes_below(m)] = Entry{h[i], id_of(i)};
+            base += popc(m);
         }
         __builtin_amdgcn_wave_barrier();
-        return total;
+        return base;
     }
 
     // Add every id to a per-wave LDS histogram: bin b = trunc(clamp(fma(h,
@@ -623,7 +617,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     for (int i = 0; i < (NE < 4 ? NE : 4); ++i) sub += popc(ballot(R.h[i] >= prune));
     const bool flat = sub * NE > 6 * cap;  // about 1.5 * cap ids expected
     if (!want_t && !flat) {
-        const int nb = R.count_compact(prune, list, lane, cap);
+        const int nb = R.count_compact(prune, list, cap);
         if (nb <= cap) {
             n_list = nb;
             if (nb > k) race_listed(nb, prune);
@@ -637,7 +631,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         float c;
         int n;
         if (top_set_by_histogram(R, list, k, prune, M, lane, c, n) && n <= kListCap) {
-            const int nc = R.count_compact(c, list, lane);
+            const int nc = R.count_compact(c, list);
             if (nc <= kListCap) {
                 n_list = nc;
                 if (!want_t) {
@@ -676,7 +670,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
             have_t = true;
         }
         for (int tries = 0; tries < 8 && !have_t; ++tries) {
-            const int c_lo = R.count_compact(lo, list, lane);
+            const int c_lo = R.count_compact(lo, list);
             if (c_lo >= k && c_lo <= kListCap) {
                 t = list_kth(list, c_lo, k, lo, M, lane);
                 n_list = c_lo;
