@@ -65,10 +65,13 @@ class Sampler:
         self._h = ds_sample_create(device, vocab, DS_DTYPE_BF16 if dtype == "bf16" else DS_DTYPE_F32,
                                    max_rows, max_positions, max_requests, top_k, vocab_chunks, flags)
         self._stage = RequestStage(max_requests)
+        # held by the object: at interpreter exit the module's globals may be gone
+        # before a sampler that is still alive is collected
+        self._destroy = ds_sample_destroy
 
     def close(self) -> None:
         if getattr(self, "_h", None):
-            ds_sample_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     def __del__(self):
