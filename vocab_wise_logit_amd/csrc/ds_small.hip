@@ -88,18 +88,21 @@ struct Row {
 
     // Count the ids whose h is >= x and list them in `list` as (h, id), slot by
     // slot: a ballot per register slot gives each lane holding such an id its
-    // place (the slot's earlier lanes, after the earlier slots' ids).  Once more
-    // than `cap` (<= kListCap) ids are found the remaining slots are only
-    // counted, so a slot is written only when the count before it is <= cap and
-    // the list's kWave spare entries past kListCap hold its last ids.  Returns
-    // the count; the list is complete when it is <= cap.
-    __device__ __forceinline__ int count_compact(float x, Entry* list, int cap = kListCap) const {
+    // place (the slot's earlier lanes, after the earlier slots' ids).  Every lane
+    // stores every slot, the ids below x to its own spare entry past kListCap, so
+    // the pass has no branch.  Places start from min(count so far, kListCap), so
+    // every store stays inside the list and its kWave spare entries.  Returns
+    // the count; the list is complete when it is <= kListCap.
+    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane) const {
         int base = 0;
+        Entry* const spare = list + kListCap + lane;
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
             const bool p = h[i] >= x;
             const uint64_t m = ballot(p);
-            if (base <= cap && p) list[base + lanes_below(m)] = Entry{h[i], id_of(i)};
+            // (before slot kListCap / kWave the count cannot pass kListCap)
+            Entry* const at = list + (i * kWave <= kListCap ? base : min(base, kListCap)) + lanes_below(m);
+            *(p ? at : spare) = Entry{h[i], id_of(i)};
             base += popc(m);
         }
         __builtin_amdgcn_wave_barrier();
@@ -344,7 +347,7 @@ __device__ __forceinline__ void load_slots(const void* base, int lane, int ndw, 
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, ndw * 4, kBufferRsrcWord3);
 #pragma unroll
     for (int j = 0; j < NS; ++j)
-        w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (lane + j * kWave) * 4, 0, kBufferNontemporal);
+        w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, j * kWave * 4, kBufferNontemporal);
 }
 
 // What a wave needs to know about its cell (all wave-uniform).
@@ -527,7 +530,9 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     }
     // exact residual of the rounded M*log2(e) shifts every exponent equally
     const float err = __builtin_fmaf(M, kLog2e, -mL);
-    const float lse = M + (log2f(S) - err) * kLn2;
+    // S >= 1 - 2^-23 (the maximum's own term), so the hardware log2 needs no
+    // denormal scaling
+    const float lse = M + (__builtin_amdgcn_logf(S) - err) * kLn2;
 
     if (tau == 0.0f) {
         // Only greedy cells need the argmax of h (sampled cells take the Gumbel
@@ -617,7 +622,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     for (int i = 0; i < (NE < 4 ? NE : 4); ++i) sub += popc(ballot(R.h[i] >= prune));
     const bool flat = sub * NE > 6 * cap;  // about 1.5 * cap ids expected
     if (!want_t && !flat) {
-        const int nb = R.count_compact(prune, list, cap);
+        const int nb = R.count_compact(prune, list, lane);
         if (nb <= cap) {
             n_list = nb;
             if (nb > k) race_listed(nb, prune);
@@ -631,7 +636,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         float c;
         int n;
         if (top_set_by_histogram(R, list, k, prune, M, lane, c, n) && n <= kListCap) {
-            const int nc = R.count_compact(c, list);
+            const int nc = R.count_compact(c, list, lane);
             if (nc <= kListCap) {
                 n_list = nc;
                 if (!want_t) {
@@ -670,7 +675,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
             have_t = true;
         }
         for (int tries = 0; tries < 8 && !have_t; ++tries) {
-            const int c_lo = R.count_compact(lo, list);
+            const int c_lo = R.count_compact(lo, list, lane);
             if (c_lo >= k && c_lo <= kListCap) {
                 t = list_kth(list, c_lo, k, lo, M, lane);
                 n_list = c_lo;
