@@ -256,16 +256,18 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         while (r < num_requests && n < ds::kMaxReqPerLaunch) {
             if (seq_lens[r] > 0) {
                 rq.offs[n] = rel;
-                rq.scale[n] = guidance_scale[r];
-                rq.tau[n] = temperature[r];
+                ds::ReqParams& q = rq.req[n];
+                q.start = rel;
+                q.scale = guidance_scale[r];
+                q.tau = temperature[r];
                 // IEEE division, correctly rounded like the kernels' 1.0f / tau
-                rq.inv_tau[n] = temperature[r] > 0.0f ? 1.0f / temperature[r] : 0.0f;
+                q.inv_tau = temperature[r] > 0.0f ? 1.0f / temperature[r] : 0.0f;
                 // u position of the request's first cell: its own position, or the
                 // next compacted one (requests with guidance 0 read no u)
-                rq.uoff[n] = compact_u ? (int32_t)upos : (int32_t)(pos + rel);
+                q.uoff = compact_u ? (int32_t)upos : (int32_t)(pos + rel);
                 if (compact_u && guidance_scale[r] != 0.0f) upos += seq_lens[r];
-                rq.row_iter_hi[n] = (uint32_t)iterations[r] << 16;
-                rq.rid[n] = (uint32_t)request_ids[r];
+                q.row_iter_hi = (uint32_t)iterations[r] << 16;
+                q.rid = (uint32_t)request_ids[r];
                 rel += seq_lens[r];
                 ++n;
             }
@@ -277,7 +279,7 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         // u can be loaded before the request lookup when every request reads it
         // at its own position
         rq.all_guided = compact_u ? 0 : 1;
-        for (int32_t i = 0; i < n; ++i) rq.all_guided &= rq.scale[i] != 0.0f ? 1 : 0;
+        for (int32_t i = 0; i < n; ++i) rq.all_guided &= rq.req[i].scale != 0.0f ? 1 : 0;
         if (small) {
             const hipError_t e = ds::launch_sample_small(bf16, a, rq, st);
             if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");

@@ -310,6 +310,18 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // broadcast to every position of the request).
 constexpr int kMaxReqPerLaunch = 64;
 
+// One request's parameters, read by a cell's wave with a single scalar load.
+struct ReqParams {
+    int32_t start;        // first position, relative to the launch's pos0
+    float scale;          // guidance
+    float tau;
+    float inv_tau;        // 1 / tau (correctly rounded), 0 for greedy requests
+    int32_t uoff;         // u position of the request's first position
+    uint32_t row_iter_hi; // iteration << 16
+    uint32_t rid;         // low 32 bits of the request id
+    int32_t pad;
+};
+
 struct ReqTable {
     int32_t n;        // requests in this launch
     int32_t pos0;     // first packed position covered
@@ -317,13 +329,9 @@ struct ReqTable {
     int32_t P;        // total packed positions of the call
     int32_t Pu;       // positions of the u layout: P, or the guided positions when u is compacted
     int32_t all_guided;  // every request of the launch reads u at its own position (no compaction)
-    int32_t offs[kMaxReqPerLaunch + 1];  // request starts, relative to pos0
-    float scale[kMaxReqPerLaunch];
-    float tau[kMaxReqPerLaunch];
-    float inv_tau[kMaxReqPerLaunch];  // 1 / tau (correctly rounded), 0 for greedy requests
-    int32_t uoff[kMaxReqPerLaunch];  // u position of the request's first position
-    uint32_t row_iter_hi[kMaxReqPerLaunch];  // iteration << 16
-    uint32_t rid[kMaxReqPerLaunch];
+    int32_t offs[kMaxReqPerLaunch + 1];  // request starts, relative to pos0 (searched by position)
+    int32_t pad[2];
+    ReqParams req[kMaxReqPerLaunch];
 };
 
 // Per-request parameters read from device memory when the launch runs (the
@@ -377,6 +385,24 @@ __device__ __forceinline__ bool dev_cell(const DevReq& d, bool have_u, int pl, D
     o.iter_hi = (uint32_t)d.iterations[r] << 16;
     o.rid = (uint32_t)d.request_ids[r];
     return true;
+}
+
+// Request r's parameters as one 32-byte scalar load (a field-by-field read is
+// split by the compiler into loads at each field's first use, each waiting
+// for its own memory latency).
+__device__ __forceinline__ ReqParams req_params(const ReqTable& rq, int r) {
+    typedef int32_t i32x8 __attribute__((ext_vector_type(8), aligned(4)));
+    const i32x8 v = *reinterpret_cast<const i32x8*>(&rq.req[r]);
+    ReqParams q;
+    q.start = v[0];
+    q.scale = __int_as_float(v[1]);
+    q.tau = __int_as_float(v[2]);
+    q.inv_tau = __int_as_float(v[3]);
+    q.uoff = v[4];
+    q.row_iter_hi = (uint32_t)v[5];
+    q.rid = (uint32_t)v[6];
+    q.pad = 0;
+    return q;
 }
 
 // The request owning launch-relative position pl: the last r with offs[r] <= pl.

@@ -810,18 +810,18 @@ __device__ __forceinline__ CellParams sample_cell(const SampleArgs& a, const Req
     const int64_t lin = a.w.cell_base + slot;  // launch-relative cell
     const int row = (int)(lin / rq.npos);
     const int pl = (int)(lin - (int64_t)row * rq.npos);
-    const int r = find_request(rq, pl);
+    const ReqParams q = req_params(rq, find_request(rq, pl));
     CellParams cp;
     cp.cell = (int64_t)row * rq.P + rq.pos0 + pl;
-    cp.ucell = (int64_t)row * rq.Pu + rq.uoff[r] + (pl - rq.offs[r]);
-    cp.s = rq.scale[r];
-    cp.tau = rq.tau[r];
-    cp.inv_tau = rq.inv_tau[r];
+    cp.ucell = (int64_t)row * rq.Pu + q.uoff + (pl - q.start);
+    cp.s = q.scale;
+    cp.tau = q.tau;
+    cp.inv_tau = q.inv_tau;
     cp.nk.k0 = a.k0;
     cp.nk.k1 = a.k1;
-    cp.nk.t = (uint32_t)(pl - rq.offs[r]);
-    cp.nk.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
-    cp.nk.rid = rq.rid[r];
+    cp.nk.t = (uint32_t)(pl - q.start);
+    cp.nk.row_iter = ((uint32_t)row & 0xFFFFu) | q.row_iter_hi;
+    cp.nk.rid = q.rid;
     return cp;
 }
 

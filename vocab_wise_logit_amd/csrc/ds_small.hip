@@ -364,15 +364,15 @@ struct CellInfo {
 // table; false past the launch's positions.
 __device__ __forceinline__ bool locate(const ReqTable& rq, int pl, int row, CellInfo& ci) {
     if (pl >= rq.npos) return false;  // (the kernel checks first)
-    const int r = find_request(rq, pl);
+    const ReqParams q = req_params(rq, find_request(rq, pl));
     ci.cell = (int64_t)row * rq.P + rq.pos0 + pl;
-    ci.t = (uint32_t)(pl - rq.offs[r]);  // offs are launch-relative
-    ci.ucell = (int64_t)row * rq.Pu + rq.uoff[r] + ci.t;
-    ci.s = rq.scale[r];
-    ci.tau = rq.tau[r];
-    ci.inv_tau = rq.inv_tau[r];
-    ci.row_iter = ((uint32_t)row & 0xFFFFu) | rq.row_iter_hi[r];
-    ci.rid = rq.rid[r];
+    ci.t = (uint32_t)(pl - q.start);  // starts are launch-relative
+    ci.ucell = (int64_t)row * rq.Pu + q.uoff + ci.t;
+    ci.s = q.scale;
+    ci.tau = q.tau;
+    ci.inv_tau = q.inv_tau;
+    ci.row_iter = ((uint32_t)row & 0xFFFFu) | q.row_iter_hi;
+    ci.rid = q.rid;
     return true;
 }
 
