@@ -72,6 +72,12 @@ def _setup(lib):
     lib.dso_reveal_topk.argtypes = [P, C.c_int32, C.c_int64, P, P, C.c_int32, P, P]
     lib.dso_greedy_lse.argtypes = [C.c_int, C.c_int32, P, P, C.c_int64, C.c_int32, P, P, P, P,
                                    P, P]
+    lib.dso_f32_to_bf16.restype = C.c_uint16
+    lib.dso_f32_to_bf16.argtypes = [C.c_float]
+    lib.dso_penalized.restype = C.c_float
+    lib.dso_penalized.argtypes = [C.c_float, C.c_float]
+    lib.dso_repetition_penalty.restype = C.c_int
+    lib.dso_repetition_penalty.argtypes = [C.c_int, C.c_int32, P, P, P, C.c_int64]
     return lib
 
 
@@ -255,6 +261,36 @@ def greedy_lse(x: np.ndarray, vocab_chunks: int = 1, rows: Optional[np.ndarray] 
         raise ValueError(_err(lib))
     return GreedyResult(rows=rows, token=token, lse=lse_, logprob=lp, triples=trip,
                         dense_token=dtok, dense_lse=dlse)
+
+
+def f32_to_bf16(x: np.ndarray, lib=None) -> np.ndarray:
+    """binary32 values to bf16 bit patterns, round to nearest even."""
+    lib = lib or _load()
+    x = np.asarray(x, dtype=np.float32).reshape(-1)
+    return np.array([lib.dso_f32_to_bf16(float(v)) for v in x], dtype=np.uint16)
+
+
+def penalized(x: float, theta: float, lib=None) -> float:
+    lib = lib or _load()
+    return float(np.float32(lib.dso_penalized(float(x), float(theta))))
+
+
+def repetition_penalty(logits: np.ndarray, seen: np.ndarray, theta, lib=None) -> np.ndarray:
+    """The repetition penalty over [n_rows, V] logits (float32 or bf16 bits) and
+    [n_rows, ceil(V / 32)] uint32 seen masks; returns a penalised copy."""
+    lib = lib or _load()
+    out = np.array(logits, copy=True, order="C")
+    dt = _dtype_code(out)
+    V = int(out.shape[-1])
+    n = out.size // V
+    seen = np.ascontiguousarray(seen, dtype=np.uint32)
+    th = np.ascontiguousarray(np.broadcast_to(np.asarray(theta, np.float32), (n,)))
+    if seen.shape != (n, (V + 31) // 32):
+        raise ValueError("seen mask must be [n_rows, ceil(V / 32)]")
+    rc = lib.dso_repetition_penalty(dt, V, _ptr(out), _ptr(seen), _ptr(th), n)
+    if rc:
+        raise ValueError(_err(lib))
+    return out
 
 
 def reveal_topk(scores: np.ndarray, seq_lens, reveal_counts, lib=None):

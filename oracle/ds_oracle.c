@@ -42,6 +42,12 @@
  *     (v >> 2, t, (row & 0xFFFF) | (iteration << 16), (uint32)request_id), word
  *     v & 3; U = ((x >> 9) * 2 + 1) * 2^-24; G = -log(-log U); the token
  *     maximises h / tau + G over the kept ids, smallest id on exact ties.
+ *   - Autoregressive mode ([ISSUE]: the existing sampler draws one token per
+ *     request and applies a repetition penalty over seen-token masks; the pages
+ *     give no formula): a seen id's logit x becomes x / theta when x > 0 and
+ *     x * theta otherwise, in binary32, stored back in the logits' own type
+ *     (bf16 by round-to-nearest-even); the token is then drawn like a cell with
+ *     guidance 0, with the top-ratio filter chosen by the caller's top_k.
  *   - Confidence reveal ([ISSUE], the top-k over the flattened [C, T] scores):
  *     per request, the reveal_count largest scores of its [C, T] block flattened
  *     row-major, best first, the smaller flattened index first on equal scores.
@@ -374,6 +380,56 @@ int dso_sample(int dtype, int32_t V, int32_t top_k, const void *c, const void *u
     free(work);
     free(hd);
     return rc;
+}
+
+/* ------------------------------------------------ autoregressive mode */
+
+/* binary32 -> bf16 rounded to nearest, ties to the even pattern.  The two
+ * candidates are the bf16 values on either side (the upper half of the pattern,
+ * and that plus one unit in the last place, away from zero); the nearer one is
+ * taken, distances measured exactly in binary64.  Past the largest finite bf16
+ * the next pattern is infinity, whose distance is that of 2^128 (an unbounded
+ * exponent), so only values from the largest finite plus half a unit round to
+ * it.  Infinities map to themselves; NaN is not an input. */
+uint16_t dso_f32_to_bf16(float f) {
+    uint32_t b = bits_from_f32(f);
+    if ((b & 0x7FFFFFFFu) >= 0x7F800000u) return (uint16_t)(b >> 16);
+    uint32_t lo = b & 0xFFFF0000u, hi = lo + 0x10000u;
+    double vlo = (double)f32_from_bits(lo);
+    double vhi = ((hi & 0x7FFFFFFFu) == 0x7F800000u) ? copysign(ldexp(1.0, 128), (double)f)
+                                                        : (double)f32_from_bits(hi);
+    double dlo = fabs((double)f - vlo), dhi = fabs(vhi - (double)f);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return ((lo >> 16) & 1u) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);
+}
+
+/* [ISSUE] repetition penalty of the autoregressive sampler (reading: the
+ * multiplicative penalty, see the header). */
+float dso_penalized(float x, float theta) { return x > 0.0f ? x / theta : x * theta; }
+
+/* In place over n_rows rows of V logits: every id whose bit is set in the row's
+ * seen mask (bit v & 31 of word v >> 5, ceil(V / 32) words per row; bits past V
+ * ignored) takes the penalised value of its row's theta (finite, > 0). */
+int dso_repetition_penalty(int dtype, int32_t V, void *logits, const uint32_t *seen,
+                           const float *theta, int64_t n_rows) {
+    if (V < 1 || n_rows < 0) return fail("bad sizes");
+    int64_t W = ((int64_t)V + 31) / 32;
+    for (int64_t i = 0; i < n_rows; i++) {
+        if (!(theta[i] > 0.0f) || isinf(theta[i])) return fail("bad penalty");
+        for (int32_t v = 0; v < V; v++) {
+            if (!((seen[i * W + (v >> 5)] >> (v & 31)) & 1u)) continue;
+            int64_t at = i * (int64_t)V + v;
+            float x = load_elem(logits, dtype, at);
+            if (isnan(x) || x == INFINITY) return fail("unsupported non-finite logit");
+            float y = dso_penalized(x, theta[i]);
+            if (dtype == DSO_BF16)
+                ((uint16_t *)logits)[at] = dso_f32_to_bf16(y);
+            else
+                ((float *)logits)[at] = y;
+        }
+    }
+    return 0;
 }
 
 /* ---------------------------------------------------- draft greedy path */

@@ -56,6 +56,13 @@ MUTANTS = {
     "reveal_flatten_transposed": ("buf[c * T + t].f = c * T + t;", "buf[c * T + t].f = t * C + c;"),
     "reveal_count_short": ("for (int32_t j = 0; j < reveal[r]; j++) {",
                            "for (int32_t j = 0; j + 1 < reveal[r]; j++) {"),
+    "penalty_divides_negatives": ("return x > 0.0f ? x / theta : x * theta;", "return x / theta;"),
+    "penalty_bit_index": (">> (v & 31)) & 1u", ">> (v & 15)) & 1u"),
+    "penalty_word_index": ("seen[i * W + (v >> 5)]", "seen[i * W + (v >> 6)]"),
+    "bf16_ties_away": ("return ((lo >> 16) & 1u) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);",
+                       "return (uint16_t)(hi >> 16);"),
+    "bf16_truncates": ("if (dlo < dhi) return (uint16_t)(lo >> 16);",
+                       "if (dlo <= dhi + 1e300) return (uint16_t)(lo >> 16);"),
 }
 
 
@@ -192,8 +199,37 @@ def check_reveal(lib):
     assert oracle.reveal_topk(s2, [3], [1], lib=lib)[0].tolist() == [2]
 
 
+def check_penalty(lib):
+    import torch
+
+    # binary32 -> bf16 against torch's conversion, on values around every kind of
+    # rounding decision (below, at and above the tie, both signs)
+    rng = np.random.default_rng(8)
+    hi = rng.integers(0, 0x7F7F, 3000).astype(np.uint32)
+    lows = np.array([0x0000, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    bits = ((hi[:, None] << 16) | lows[None, :]).reshape(-1)
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    f = bits.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16(f, lib=lib), want)
+    # the penalty on hand-computed values: ids 0, 1, 2, 4, 5, 6, 8, 40, 58 and 65
+    # seen
+    x = np.zeros((1, 70), np.float32)
+    x[0, :9] = [2.0, -2.0, 0.0, 3.0, -np.inf, 1.5, -0.75, 5.0, 7.0]
+    x[0, 40], x[0, 41], x[0, 58], x[0, 65] = -1.25, 9.0, 4.0, 6.0
+    seen = np.zeros((1, 3), np.uint32)
+    seen[0, 0] = 0b101110111
+    seen[0, 1] = (1 << 8) | (1 << 26)
+    seen[0, 2] = (1 << 1) | 0xFFFFFF80  # bits past id 69 are ignored
+    out = oracle.repetition_penalty(x, seen, 2.0, lib=lib)
+    want = x.copy()
+    want[0, :9] = [1.0, -4.0, 0.0, 3.0, -np.inf, 0.75, -1.5, 5.0, 3.5]
+    want[0, 40], want[0, 58], want[0, 65] = -2.5, 2.0, 3.0
+    assert np.array_equal(out, want)
+
+
 CHECKS = [check_guided, check_bf16, check_logprobs, check_philox, check_gumbel,
-          check_threshold, check_greedy, check_sampling, check_draft, check_reveal]
+          check_threshold, check_greedy, check_sampling, check_draft, check_reveal, check_penalty]
 
 
 def _failures(lib):

@@ -588,3 +588,68 @@ def test_reveal_rejects_bad_counts_and_nan():
     s[0, 1] = np.nan
     with pytest.raises(ValueError):
         oracle.reveal_topk(s, [3], [1])
+
+
+# ------------------------------------------- autoregressive mode (penalty)
+
+def test_bf16_rounding_matches_torch_on_every_pattern_and_tie():
+    import torch
+
+    # every finite upper half with the lower halves just below, at and just above
+    # the rounding tie, both signs
+    hi = np.arange(0, 0x7F80, dtype=np.uint32)
+    lows = np.array([0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    bits = ((hi[:, None] << 16) | lows[None, :]).reshape(-1)
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    f = bits.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.f32_to_bf16(f)
+    assert np.array_equal(got, want)
+    # exact bf16 values and infinities map to themselves
+    exact = (hi << 16).view(np.float32)
+    assert np.array_equal(oracle.f32_to_bf16(exact), hi.astype(np.uint16))
+    assert oracle.f32_to_bf16(np.array([np.inf, -np.inf], np.float32)).tolist() == [0x7F80, 0xFF80]
+
+
+def test_repetition_penalty_identities_and_closed_forms():
+    rng = np.random.default_rng(21)
+    V = 1000
+    x = synth.bf16_from_f32((rng.normal(size=(5, V)) * 4).astype(np.float32))
+    W = (V + 31) // 32
+    seen = rng.integers(0, 2**32, (5, W), dtype=np.uint64).astype(np.uint32)
+    # theta = 1 and an empty mask leave the row bit for bit
+    assert np.array_equal(oracle.repetition_penalty(x, seen, 1.0), x)
+    assert np.array_equal(oracle.repetition_penalty(x, np.zeros_like(seen), 1.7), x)
+    # theta = 2 is exact in binary32 and bf16 (a power of two): seen positive
+    # logits halve, seen negative ones double, unseen ones stay
+    out = oracle.repetition_penalty(x, seen, 2.0)
+    xf, of = oracle.bf16_to_f32(x), oracle.bf16_to_f32(out)
+    bit = ((seen[:, np.arange(V) >> 5] >> (np.arange(V) & 31)) & 1).astype(bool)
+    want = np.where(bit, np.where(xf > 0, xf / 2, xf * 2), xf)
+    assert np.array_equal(of, want.astype(np.float32))
+    # a general theta: one binary32 rounding, then one bf16 rounding (checked with
+    # exact rational arithmetic on a few values)
+    th = np.float32(1.3)
+    out = oracle.repetition_penalty(x[:1], seen[:1], th)
+    for v in np.flatnonzero(bit[0])[:40]:
+        xv = Fraction(float(xf[0, v]))
+        q = xv / Fraction(float(th)) if xv > 0 else xv * Fraction(float(th))
+        a = np.float32(float(q))
+        cands = [np.nextafter(a, np.float32(-np.inf)), a, np.nextafter(a, np.float32(np.inf))]
+        f32 = min(cands, key=lambda y: (abs(Fraction(float(y)) - q), int(np.array(y).view(np.uint32)) & 1))
+        assert oracle.bf16_to_f32(out[:1, v:v + 1])[0, 0] == oracle.bf16_to_f32(oracle.f32_to_bf16(f32))[0]
+    # float32 logits are penalised without a second rounding
+    xf32 = (rng.normal(size=(2, 70)) * 3).astype(np.float32)
+    s2 = np.full((2, 3), 0xFFFFFFFF, np.uint32)
+    o2 = oracle.repetition_penalty(xf32, s2, th)
+    assert np.array_equal(o2, np.where(xf32 > 0, xf32 / th, xf32 * th).astype(np.float32))
+
+
+def test_repetition_penalty_rejects_bad_theta_and_shapes():
+    x = np.zeros((2, 40), np.float32)
+    seen = np.zeros((2, 2), np.uint32)
+    for bad in (0.0, -1.0, np.inf, np.nan):
+        with pytest.raises(ValueError):
+            oracle.repetition_penalty(x, seen, bad)
+    with pytest.raises(ValueError):
+        oracle.repetition_penalty(x, np.zeros((2, 1), np.uint32), 1.5)
