@@ -243,6 +243,32 @@ int ds_reveal_topk(ds_sampler *s, const float *scores, int32_t num_rows, const i
                    const int32_t *reveal_counts, int32_t num_requests, int32_t *index_out,
                    float *score_out, void *stream);
 
+/*
+ * ds_repetition_penalty -- the repetition penalty of the autoregressive mode
+ * ([ISSUE]: the existing sampler draws one token per request and applies a
+ * repetition penalty over seen-token masks; the pages give no formula).  Reading:
+ * every seen id's logit x becomes x / theta when x > 0 and x * theta otherwise,
+ * computed in binary32 and written back in place in the handle's dtype (bf16
+ * rounded to nearest even).  An autoregressive step is this call followed by
+ * ds_sample over the same rows as one position per request (guidance 0, u NULL),
+ * with the top-ratio filter given by the handle's top_k (V keeps every id).
+ *
+ *   logits       device [n_rows, V] of the handle's dtype, modified in place at
+ *                the seen ids only; values finite or -inf (NaN unsupported).
+ *   n_rows       0 .. max_rows * max_positions (0 is a no-op).
+ *   seen_mask    device uint32 [n_rows, ceil(V / 32)], 4-byte aligned: id v of
+ *                row i is seen when bit (v & 31) of word i * ceil(V / 32) + (v >> 5)
+ *                is set; bits past V are ignored.
+ *   penalty      device float [n_rows], 4-byte aligned: theta of each row; a row
+ *                whose theta is not finite and > 0 is left unchanged (theta = 1
+ *                changes nothing either).
+ *   stream       hipStream_t.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY or DS_ERR_HIP.  Rows whose
+ * mask words overlap in memory with another row's logits race.
+ */
+int ds_repetition_penalty(ds_sampler *s, void *logits, int64_t n_rows, const uint32_t *seen_mask,
+                          const float *penalty, void *stream);
+
 /* Release a handle and its device scratch.  NULL is a no-op.  The caller must
  * make sure no call on the handle is still pending on a stream. */
 void ds_sample_destroy(ds_sampler *s);

@@ -293,6 +293,18 @@ def repetition_penalty(logits: np.ndarray, seen: np.ndarray, theta, lib=None) ->
     return out
 
 
+def ar_step(w, lib=None):
+    """Oracle of one autoregressive step (a ``synth.ARWorkload``): the repetition
+    penalty, then every row sampled as one position of its request with guidance
+    0.  Returns (penalised logits, SampleResult over the R cells)."""
+    pen = repetition_penalty(w.logits, w.seen, w.penalty, lib=lib)
+    R = pen.shape[0]
+    res = sample(c=pen.reshape(1, R, w.vocab), u=None, seq_lens=np.ones(R, np.int32),
+                 request_ids=w.request_ids, iterations=w.iterations, guidance=np.zeros(R, np.float32),
+                 temperature=w.temperature, rows=1, seed=w.seed, top_k=w.top_k, lib=lib)
+    return pen, res
+
+
 def reveal_topk(scores: np.ndarray, seq_lens, reveal_counts, lib=None):
     """Per request, the reveal_counts[r] best cells of its [C, T_r] block of the
     packed [C, P] scores: (flattened indices c * T_r + t, scores), concatenated

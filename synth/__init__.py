@@ -7,6 +7,7 @@ exactly these arrays.
 """
 
 from .workloads import (  # noqa: F401
+    ARWorkload,
     DiffusionWorkload,
     DraftWorkload,
     RevealWorkload,
@@ -19,4 +20,5 @@ from .workloads import (  # noqa: F401
     stress,
     tiny,
     WORKLOADS,
+    ar,
 )

@@ -329,6 +329,81 @@ def reveal(n_requests: int = 8, rows: int = 8, seed: int = 5, lo: int = 80, hi: 
     return RevealWorkload(name=name, scores=vals, seq_lens=seq_lens, reveal_counts=counts)
 
 
+@dataclass
+class ARWorkload:
+    """Inputs of one autoregressive step: logits ``[R, vocab]`` (one row per
+    request), seen-token masks ``[R, ceil(vocab / 32)]`` (bit v & 31 of word
+    v >> 5), and per-request penalty, temperature, iteration and id."""
+    name: str
+    dtype: str
+    vocab: int
+    logits: np.ndarray
+    seen: np.ndarray          # uint32 [R, W]
+    penalty: np.ndarray       # float32 [R]
+    temperature: np.ndarray   # float32 [R]
+    iterations: np.ndarray    # int32 [R]
+    request_ids: np.ndarray   # int64 [R]
+    top_k: int
+    seed: int
+
+    @property
+    def rows(self) -> int:
+        return int(self.logits.shape[0])
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def n_seen(self) -> int:
+        V = self.vocab
+        ids = np.arange(V)
+        bits = (self.seen[:, ids >> 5] >> (ids & 31).astype(np.uint32)) & np.uint32(1)
+        return int(bits.sum())
+
+    def algorithmic_bytes(self) -> int:
+        """Masks read once, each seen logit read and written, the logits read once
+        by the sampler, and token plus logprob (8 bytes) per request."""
+        return int(self.seen.size * 4 + 2 * self.n_seen() * self.elem_bytes
+                   + self.rows * self.vocab * self.elem_bytes + self.rows * 8)
+
+
+def ar(n_requests: int = 256, vocab: int = 248320, seed: int = 6, dtype: str = "bf16",
+       sigma: float = 4.0, seen_lo: int = 256, seen_hi: int = 1280, top_share: float = 0.25,
+       penalty: float = 1.1, temperatures=(0.0, 0.7, 1.0), top_k: Optional[int] = None,
+       name: str = "ar") -> ARWorkload:
+    """Autoregressive step: R rows of N(0, sigma) logits; each request has seen
+    between seen_lo and seen_hi distinct tokens (the pages' serving setting of 256
+    input and up to 1024 output tokens), a top_share of them drawn from the row's
+    50 largest logits (repeated tokens are likely ones) and the rest uniform;
+    penalty theta for every request; temperatures cycled over the requests;
+    top_k = vocab (no top-ratio filter) unless given."""
+    root = np.random.SeedSequence([seed, 13])
+    s_x, s_seen = root.spawn(2)
+    x = _normal_f32(s_x, n_requests * vocab, sigma).reshape(n_requests, vocab)
+    g = np.random.Generator(np.random.PCG64(s_seen))
+    W = (vocab + 31) // 32
+    seen = np.zeros((n_requests, W), dtype=np.uint32)
+    for r in range(n_requests):
+        n = int(g.integers(min(seen_lo, vocab), min(seen_hi, vocab) + 1))
+        n_top = min(int(round(top_share * n)), 50, vocab)
+        top = np.argpartition(-x[r], n_top - 1)[:n_top] if n_top > 0 else np.zeros(0, np.int64)
+        picked = set(int(v) for v in g.choice(top, n_top, replace=False)) if n_top else set()
+        rest = g.choice(vocab, n, replace=False)
+        for v in rest:
+            if len(picked) >= n:
+                break
+            picked.add(int(v))
+        ids = np.fromiter(picked, dtype=np.int64)
+        np.bitwise_or.at(seen[r], ids >> 5, (np.uint32(1) << (ids & 31).astype(np.uint32)))
+    logits = bf16_from_f32(x) if dtype == "bf16" else x
+    temps = np.array([temperatures[r % len(temperatures)] for r in range(n_requests)], np.float32)
+    return ARWorkload(name=name, dtype=dtype, vocab=vocab, logits=logits, seen=seen,
+                      penalty=np.full(n_requests, penalty, np.float32), temperature=temps,
+                      iterations=np.full(n_requests, 7, np.int32),
+                      request_ids=(2000 + np.arange(n_requests)).astype(np.int64),
+                      top_k=vocab if top_k is None else top_k, seed=42)
+
+
 WORKLOADS: Dict[str, Callable[[], object]] = {
     "tiny_greedy": lambda: tiny(0.0),
     "tiny_sampled": lambda: tiny(0.9),
@@ -337,4 +412,5 @@ WORKLOADS: Dict[str, Callable[[], object]] = {
     "draft": draft,
     "stress": stress,
     "reveal": reveal,
+    "ar": ar,
 }

@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     RequestStage,
     ds_greedy_lse,
     ds_last_error,
+    ds_repetition_penalty,
     ds_reveal_topk,
     ds_sample,
     ds_sample_create,
@@ -139,6 +140,27 @@ class Sampler:
             tok, lse, lp, tri = out
         ds_greedy_lse(self._h, logits, n, tok, lse, lp, tri, stream)
         return (tok, lse, lp, tri) if triples else (tok, lse, lp)
+
+    def repetition_penalty(self, logits, seen_mask, penalty, stream=None):
+        """In place over logits [n_rows, V]: every id set in the row's seen_mask
+        (int32 [n_rows, ceil(V / 32)] holding the uint32 words) takes x / theta
+        when x > 0, else x * theta, with theta = penalty[row] (float32 device
+        tensor).  Returns logits."""
+        ds_repetition_penalty(self._h, logits, int(logits.shape[0]), seen_mask, penalty, stream)
+        return logits
+
+    def sample_ar(self, request_ids: Sequence[int], logits, seen_mask, penalty, iterations: Sequence[int],
+                  temperature: Sequence[float], seed: int = 0, out=None, stream=None):
+        """Autoregressive step, one token per request: the repetition penalty in
+        place on logits [R, V], then each row sampled as one position of its
+        request (guidance 0) with the handle's top_k.  Returns (tokens int32 [R],
+        logprobs float32 [R])."""
+        R = int(logits.shape[0])
+        self.repetition_penalty(logits, seen_mask, penalty, stream)
+        o = None if out is None else (out[0].view(1, R), out[1].view(1, R), None)
+        tok, lp = self.sample(request_ids, logits.view(1, R, logits.shape[1]), None, [1] * R, iterations,
+                              [0.0] * R, temperature, seed=seed, out=o, stream=stream)
+        return tok.view(R), lp.view(R)
 
     def reveal_topk(self, scores, seq_lens: Sequence[int], reveal_counts: Sequence[int], out=None,
                     stream=None):

@@ -1,7 +1,7 @@
 """ctypes binding of libdssample.so: argument marshalling only.
 
 Functions carry the C entry points' names (ds_sample_create, ds_sample,
-ds_sample_device_params, ds_greedy_lse, ds_reveal_topk, ds_sample_destroy,
+ds_sample_device_params, ds_greedy_lse, ds_reveal_topk, ds_repetition_penalty, ds_sample_destroy,
 ds_last_error, ds_version).  Device buffers are
 torch tensors on a HIP device (torch supplies memory and streams); per-request
 arrays are host sequences.  Every computation happens in the HIP library; when the
@@ -23,7 +23,7 @@ DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY
 DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK, DS_FLAG_COMPACT_U = 0, 1, 2
 
 EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_greedy_lse", "ds_reveal_topk",
-            "ds_sample_destroy", "ds_last_error", "ds_version")
+            "ds_repetition_penalty", "ds_sample_destroy", "ds_last_error", "ds_version")
 
 _lib = None
 
@@ -40,6 +40,12 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m vocab_wise_logit_amd.build`")
+        # torch ships its own HIP runtime and loads it into the global symbol
+        # scope; loaded after it, the library's HIP calls bind to that same
+        # runtime, so its streams and memory are the library's.  Loaded first, the
+        # library would start the system HIP runtime, and torch's own could then
+        # not open the device.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         P, I32, I64, U32, U64 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_uint64
         L.ds_sample_create.restype = C.c_int
@@ -52,6 +58,8 @@ def lib():
         L.ds_greedy_lse.argtypes = [P, P, I64, P, P, P, P, P]
         L.ds_reveal_topk.restype = C.c_int
         L.ds_reveal_topk.argtypes = [P, P, I32, P, P, I32, P, P, P]
+        L.ds_repetition_penalty.restype = C.c_int
+        L.ds_repetition_penalty.argtypes = [P, P, I64, P, P, P]
         L.ds_sample_destroy.restype = None
         L.ds_sample_destroy.argtypes = [P]
         L.ds_last_error.restype = C.c_char_p
@@ -239,6 +247,14 @@ def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_
                                _dev_ptr(logprob_out, "logprob_out", torch.float32),
                                _dev_ptr(triples_out, "triples_out", torch.float32),
                                _stream_ptr(stream, logits)))
+
+
+def ds_repetition_penalty(handle: int, logits, n_rows: int, seen_mask, penalty, stream=None) -> None:
+    """seen_mask: int32 tensor holding the uint32 mask words bit for bit."""
+    torch = _t()
+    _check(lib().ds_repetition_penalty(handle, _dev_ptr(logits, "logits"), n_rows,
+                                       _dev_ptr(seen_mask, "seen_mask", torch.int32),
+                                       _dev_ptr(penalty, "penalty", torch.float32), _stream_ptr(stream, logits)))
 
 
 def ds_reveal_topk(handle: int, scores, num_rows: int, seq_lens: Sequence[int],

@@ -434,6 +434,35 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
 }
 
 
+int ds_repetition_penalty(ds_sampler* s, void* logits, int64_t n_rows, const uint32_t* seen_mask,
+                          const float* penalty, void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    if (n_rows < 0) return fail(DS_ERR_INVALID_ARG, "n_rows must be >= 0");
+    if (n_rows > (int64_t)s->max_rows * s->max_positions)
+        return fail(DS_ERR_CAPACITY, "n_rows %lld exceeds max_rows * max_positions", (long long)n_rows);
+    if (n_rows == 0) return DS_OK;
+    if (!logits || !seen_mask || !penalty)
+        return fail(DS_ERR_INVALID_ARG, "logits, seen_mask and penalty must be non-NULL");
+    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(logits, es)) return fail(DS_ERR_INVALID_ARG, "logits is not %d-byte aligned", (int)es);
+    if (!aligned(seen_mask, 4) || !aligned(penalty, 4))
+        return fail(DS_ERR_INVALID_ARG, "seen_mask and penalty must be 4-byte aligned");
+
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    ds::PenaltyArgs a;
+    a.logits = logits;
+    a.seen = seen_mask;
+    a.penalty = penalty;
+    a.n_rows = n_rows;
+    a.V = s->vocab;
+    a.W = (s->vocab + 31) / 32;
+    const hipError_t e = ds::launch_repetition_penalty(s->dtype == DS_DTYPE_BF16, a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "penalty kernel launch");
+    return DS_OK;
+}
+
 int ds_reveal_topk(ds_sampler* s, const float* scores, int32_t num_rows, const int32_t* seq_lens,
                    const int32_t* reveal_counts, int32_t num_requests, int32_t* index_out, float* score_out,
                    void* stream) {

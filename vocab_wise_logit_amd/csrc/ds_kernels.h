@@ -92,6 +92,19 @@ constexpr int kGreedyRowMaxChunks = 64;
 bool greedy_rows_fits(bool bf16, int V, int chunks, const void* x);
 hipError_t launch_greedy_rows(bool bf16, const GreedyArgs& a, hipStream_t st);
 
+// Repetition penalty of the autoregressive mode, in place: one thread per
+// seen-mask word.
+constexpr int kPenaltyThreads = 256;
+struct PenaltyArgs {
+    void* logits;           // [n_rows, V], modified in place
+    const uint32_t* seen;   // [n_rows, W]
+    const float* penalty;   // [n_rows]
+    int64_t n_rows;
+    int32_t V;
+    int32_t W;              // ceil(V / 32)
+};
+hipError_t launch_repetition_penalty(bool bf16, const PenaltyArgs& a, hipStream_t st);
+
 // Confidence reveal: one workgroup per request, its selected cells sorted in LDS.
 constexpr int kRevealThreads = 1024;
 constexpr int kRevealCap = 16384;        // cells one request may reveal
