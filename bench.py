@@ -43,12 +43,13 @@ KERNEL_SOURCES = {
     "small": ("ds_small.hip", "ds_device.h", "ds_kernels.h"),
     "row": ("ds_row.hip", "ds_device.h", "ds_kernels.h"),
     "reveal": ("ds_reveal.hip", "ds_device.h", "ds_kernels.h"),
+    "ar": ("ds_penalty.hip", "ds_row.hip", "ds_device.h", "ds_kernels.h"),
 }
 
 
 def kernel_family(workload: str) -> str:
-    if workload == "reveal":
-        return "reveal"
+    if workload in ("reveal", "ar"):
+        return workload
     return "small" if workload in ("tiny", "omnivoice", "mixed") else "row"
 
 
@@ -87,12 +88,20 @@ def to_dev(arr: np.ndarray):
 def kernel_name(w, kind: str) -> str:
     if kind == "reveal":
         return "k_reveal_topk"
+    if kind == "ar":
+        dev = [k.replace("_wide", "") + "_dev" + ("_wide" if k.endswith("_wide") else "")
+               for k in sampler_kernels(w.vocab, w.dtype).split("+")]
+        return "+".join(["k_repetition_penalty"] + dev)
     if kind == "draft":
         return draft_kernel(w)
-    slots = ((w.vocab + 2) // 2 if w.dtype == "bf16" else w.vocab + 63) // 64
-    if slots > (16 if w.dtype == "bf16" else 32):
+    return sampler_kernels(w.vocab, w.dtype)
+
+
+def sampler_kernels(vocab: int, dtype: str) -> str:
+    slots = ((vocab + 2) // 2 if dtype == "bf16" else vocab + 63) // 64
+    if slots > (16 if dtype == "bf16" else 32):
         return "k_sample_parts+k_sample_merge"
-    return "k_sample_small" if slots <= (9 if w.dtype == "bf16" else 16) else "k_sample_small_wide"
+    return "k_sample_small" if slots <= (9 if dtype == "bf16" else 16) else "k_sample_small_wide"
 
 
 def draft_kernel(w) -> str:
@@ -134,7 +143,24 @@ class Runner:
         import vocab_wise_logit_amd as ds
 
         self.w, self.kind, self.mode = w, kind, mode
-        if kind == "reveal":
+        if kind == "ar":
+            # the penalty works in place, so each buffer set is penalised again on
+            # every pass over it (same seen ids, same work per step)
+            x = to_dev(w.logits)
+            per_set = x.numel() * x.element_size()
+            self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
+            self.x = [x] + [x.clone() for _ in range(self.n_sets - 1)]
+            self.seen = torch.from_numpy(np.ascontiguousarray(w.seen).view(np.int32)).cuda()
+            self.pen = torch.from_numpy(np.ascontiguousarray(w.penalty)).cuda()
+            R = w.rows
+            self.smp = ds.Sampler(w.vocab, w.dtype, max_rows=1, max_positions=R, max_requests=R, top_k=w.top_k)
+            self.out = (torch.empty(R, dtype=torch.int32, device="cuda"),
+                        torch.empty(R, dtype=torch.float32, device="cuda"))
+            self.prm = (torch.tensor(np.asarray(w.request_ids, np.int64), device="cuda"),
+                        torch.tensor(np.asarray(w.iterations, np.int32), device="cuda"),
+                        torch.tensor(np.asarray(w.temperature, np.float32), device="cuda"))
+            self.cells = R
+        elif kind == "reveal":
             x = torch.from_numpy(np.ascontiguousarray(w.scores)).cuda()
             per_set = x.numel() * x.element_size()
             self.n_sets = max(1, min(64, math.ceil(ROTATE_BYTES / per_set)))
@@ -206,7 +232,10 @@ class Runner:
     def step(self, i: int) -> None:
         s = i % self.n_sets
         w = self.w
-        if self.kind == "reveal":
+        if self.kind == "ar":
+            self.smp.sample_ar(self.prm[0], self.x[s], self.seen, self.pen, self.prm[1], self.prm[2],
+                               seed=w.seed, out=self.out)
+        elif self.kind == "reveal":
             self.smp.reveal_topk(self.x[s], w.seq_lens, w.reveal_counts, out=self.out)
         elif self.kind == "draft":
             self.smp.greedy_lse(self.x[s], out=self.out)
@@ -255,6 +284,10 @@ def time_runner(r: Runner, steps: int, warmup: int):
 
 
 def describe(w, kind: str) -> dict:
+    if kind == "ar":
+        return {"workload": "ar_step", "requests": w.rows, "vocab": w.vocab, "input_dtype": w.dtype,
+                "top_k": w.top_k, "seen_ids": w.n_seen(), "penalty": float(w.penalty[0]),
+                "temperatures": sorted(set(float(t) for t in w.temperature))}
     if kind == "reveal":
         return {"workload": "confidence_reveal", "requests": int(len(w.seq_lens)), "rows": w.rows,
                 "positions": w.positions, "revealed": int(w.reveal_counts.sum())}
@@ -271,7 +304,11 @@ def describe(w, kind: str) -> dict:
 def launches_per_step(w, kind: str) -> int:
     """Kernel launches of one call: one for the wave-per-cell kernel and the
     one-workgroup-per-row draft kernel, a parts and a merge kernel for the
-    streaming path (every workload here fits one batch)."""
+    streaming path (every sampling workload here fits one batch).  The
+    autoregressive step is the penalty kernel and then the sampler over all its
+    requests at once."""
+    if kind == "ar":
+        return 1 + (1 if sampler_kernels(w.vocab, w.dtype).startswith("k_sample_small") else 2)
     return 1 if kernel_name(w, kind).startswith(("k_sample_small", "k_reveal", "k_greedy_rows")) else 2
 
 
@@ -296,7 +333,7 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     """Times one workload; steps=None sizes the run with auto_steps."""
     import torch
 
-    kind = name if name in ("draft", "reveal") else "sample"
+    kind = name if name in ("draft", "reveal", "ar") else "sample"
     w = make_workload(name)
     r = Runner(w, kind, threshold, mode)
     if steps is None:
@@ -307,7 +344,8 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     torch.cuda.empty_cache()
     alg = w.algorithmic_bytes()
     # positions: cells sampled, draft rows reduced, or cells ranked by the reveal
-    cells = {"draft": lambda: w.n_rows, "reveal": lambda: w.rows * w.positions}.get(kind, lambda: w.cells)()
+    cells = {"draft": lambda: w.n_rows, "reveal": lambda: w.rows * w.positions,
+             "ar": lambda: w.rows}.get(kind, lambda: w.cells)()
     # every workload here has <= 64 requests, so one step is one launch of the
     # wave-per-cell kernel (its back-to-back time per step is that kernel's
     # average duration on its stream) or one parts + merge pair
@@ -398,7 +436,7 @@ def main() -> int:
     if not args.no_suite:
         # every workload, then the two sampled shapes again with the threshold
         # output requested (it needs the exact k-th largest h of every row)
-        runs = [(n, False) for n in ("tiny", "omnivoice", "mixed", "draft", "stress", "reveal")]
+        runs = [(n, False) for n in ("tiny", "omnivoice", "mixed", "draft", "stress", "reveal", "ar")]
         runs += [("omnivoice", True), ("stress", True)]
         runs = [(n, thr, "eager") for n, thr in runs]
         # the fixed-shape entry point with device-resident parameters, called and replayed

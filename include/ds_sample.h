@@ -250,8 +250,9 @@ int ds_reveal_topk(ds_sampler *s, const float *scores, int32_t num_rows, const i
  * every seen id's logit x becomes x / theta when x > 0 and x * theta otherwise,
  * computed in binary32 and written back in place in the handle's dtype (bf16
  * rounded to nearest even).  An autoregressive step is this call followed by
- * ds_sample over the same rows as one position per request (guidance 0, u NULL),
- * with the top-ratio filter given by the handle's top_k (V keeps every id).
+ * sampling the same rows as one position per request (guidance 0, no u),
+ * with the top-ratio filter given by the handle's top_k (V keeps every id);
+ * ds_sample_ar runs both in one call.
  *
  *   logits       device [n_rows, V] of the handle's dtype, modified in place at
  *                the seen ids only; values finite or -inf (NaN unsupported).
@@ -268,6 +269,37 @@ int ds_reveal_topk(ds_sampler *s, const float *scores, int32_t num_rows, const i
  */
 int ds_repetition_penalty(ds_sampler *s, void *logits, int64_t n_rows, const uint32_t *seen_mask,
                           const float *penalty, void *stream);
+
+/*
+ * ds_sample_ar -- one autoregressive step: one token per request ([ISSUE]: the
+ * existing sampler draws one token per request and applies a repetition penalty
+ * over seen-token masks).  The repetition penalty (as ds_repetition_penalty, in
+ * place) and then, in one launch, every row sampled as the only position of its
+ * request: guidance 0, the request's temperature (0 = greedy), the handle's
+ * top_k, Gumbel noise keyed by (seed, request id, iteration, row 0, position 0,
+ * id) exactly as ds_sample keys a request with one position, and the
+ * full-vocabulary log-probability of the penalised row.
+ *
+ *   request_ids   device int64 [R], 8-byte aligned.
+ *   logits        device [R, V] of the handle's dtype; penalised in place.
+ *   seen_mask     device uint32 [R, ceil(V / 32)] as in ds_repetition_penalty,
+ *                 or NULL together with penalty for no penalty.
+ *   penalty       device float [R] as in ds_repetition_penalty, or NULL.
+ *   iterations    device int32 [R]; keys the noise.
+ *   temperature   device float [R]; a value that is not finite and > 0 samples
+ *                 greedily.
+ *   num_requests  R, 1 .. min(max_requests, max_positions).
+ *   seed          keys the noise.
+ *   tokens_out    device int32 [R]; logprobs_out device float [R].
+ *   stream        hipStream_t.
+ * Returns DS_OK, DS_ERR_INVALID_ARG, DS_ERR_CAPACITY or DS_ERR_HIP.  The
+ * parameters are read when the call runs, so a captured call follows updates to
+ * the device arrays between replays.
+ */
+int ds_sample_ar(ds_sampler *s, const int64_t *request_ids, void *logits, const uint32_t *seen_mask,
+                 const float *penalty, const int32_t *iterations, const float *temperature,
+                 int32_t num_requests, uint64_t seed, int32_t *tokens_out, float *logprobs_out,
+                 void *stream);
 
 /* Release a handle and its device scratch.  NULL is a no-op.  The caller must
  * make sure no call on the handle is still pending on a stream. */

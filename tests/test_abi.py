@@ -72,6 +72,8 @@ def test_calls_on_a_null_handle_fail_cleanly():
     assert rc == ds.DS_ERR_INVALID_ARG and "sampler is NULL" in ds.ds_last_error()
     rc = L.ds_repetition_penalty(None, None, 1, None, None, None)
     assert rc == ds.DS_ERR_INVALID_ARG and "sampler is NULL" in ds.ds_last_error()
+    rc = L.ds_sample_ar(None, None, None, None, None, None, None, 1, 0, None, None, None)
+    assert rc == ds.DS_ERR_INVALID_ARG and "sampler is NULL" in ds.ds_last_error()
     h = C.c_void_p()
     assert L.ds_sample_create(None, 0, 10, 0, 1, 1, 1, 0, 1, 0) == ds.DS_ERR_INVALID_ARG
     assert L.ds_sample_create(C.byref(h), 0, -1, 0, 1, 1, 1, 0, 1, 0) == ds.DS_ERR_INVALID_ARG

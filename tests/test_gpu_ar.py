@@ -20,6 +20,9 @@ CASES = [
     ("row_bf16", 9, 40961, "bf16", (100, 2000), (0.0, 0.8), None),
     ("small_f32", 13, 777, "f32", (1, 100), (0.0, 1.3), None),
     ("row_f32_ragged", 5, 3001, "f32", (10, 300), (0.6,), None),
+    # more requests than one wave's table: every request is its own position
+    ("many_small_bf16", 150, 1025, "bf16", (5, 100), (0.0, 0.9), None),
+    ("many_row_bf16", 90, 8192, "bf16", (50, 500), (0.0, 1.0), None),
 ]
 
 
@@ -104,3 +107,22 @@ def test_library_loaded_before_torch_uses_one_runtime():
     log("[gpu] fresh process: sampler before torch")
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
     assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]
+
+
+def test_ar_step_without_penalty_equals_ds_sample_rows():
+    """With no mask and no penalty the step is ds_sample over requests of one
+    position each (the noise is keyed the same way)."""
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    R, V = 70, 1025
+    w = synth.ar(n_requests=R, vocab=V, seed=77, seen_lo=1, seen_hi=2, temperatures=(0.0, 0.8, 1.1))
+    with ds.Sampler(V, "bf16", max_rows=1, max_positions=R, max_requests=R, top_k=w.top_k) as smp:
+        x = to_dev(w.logits)
+        tok, lp = smp.sample_ar(w.request_ids, x, None, None, w.iterations, w.temperature, seed=w.seed)
+        t2, l2 = smp.sample(w.request_ids, x.view(1, R, V), None, [1] * R, w.iterations, [0.0] * R,
+                            w.temperature, seed=w.seed)
+        torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), t2.view(-1).cpu().numpy())
+    assert np.array_equal(lp.cpu().numpy().view(np.uint32), l2.view(-1).cpu().numpy().view(np.uint32))

@@ -10,6 +10,8 @@ from __future__ import annotations
 
 from typing import Optional, Sequence
 
+import numpy as np
+
 from ._binding import (  # noqa: F401
     DS_DTYPE_BF16,
     DS_DTYPE_F32,
@@ -30,6 +32,7 @@ from ._binding import (  # noqa: F401
     ds_last_error,
     ds_repetition_penalty,
     ds_reveal_topk,
+    ds_sample_ar,
     ds_sample,
     ds_sample_create,
     ds_sample_destroy,
@@ -149,18 +152,29 @@ class Sampler:
         ds_repetition_penalty(self._h, logits, int(logits.shape[0]), seen_mask, penalty, stream)
         return logits
 
-    def sample_ar(self, request_ids: Sequence[int], logits, seen_mask, penalty, iterations: Sequence[int],
-                  temperature: Sequence[float], seed: int = 0, out=None, stream=None):
-        """Autoregressive step, one token per request: the repetition penalty in
-        place on logits [R, V], then each row sampled as one position of its
-        request (guidance 0) with the handle's top_k.  Returns (tokens int32 [R],
-        logprobs float32 [R])."""
-        R = int(logits.shape[0])
-        self.repetition_penalty(logits, seen_mask, penalty, stream)
-        o = None if out is None else (out[0].view(1, R), out[1].view(1, R), None)
-        tok, lp = self.sample(request_ids, logits.view(1, R, logits.shape[1]), None, [1] * R, iterations,
-                              [0.0] * R, temperature, seed=seed, out=o, stream=stream)
-        return tok.view(R), lp.view(R)
+    def sample_ar(self, request_ids, logits, seen_mask, penalty, iterations, temperature, seed: int = 0,
+                  out=None, stream=None):
+        """Autoregressive step, one token per request, in one call: the
+        repetition penalty in place on logits [R, V] (seen_mask and penalty may
+        both be None), then each row sampled as the only position of its request
+        (guidance 0) with the handle's top_k.  request_ids (int64), iterations
+        (int32) and temperature (float32) are [R] device tensors; host sequences
+        are copied to the device first.  Returns (tokens int32 [R], logprobs
+        float32 [R])."""
+        import torch
+
+        R, dev = int(logits.shape[0]), logits.device
+
+        def on_dev(x, dt):
+            return x if isinstance(x, torch.Tensor) else torch.tensor(np.asarray(x), dtype=dt, device=dev)
+
+        rid = on_dev(request_ids, torch.int64)
+        it = on_dev(iterations, torch.int32)
+        tp = on_dev(temperature, torch.float32)
+        if out is None:
+            out = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.float32, device=dev))
+        ds_sample_ar(self._h, rid, logits, seen_mask, penalty, it, tp, seed, out[0], out[1], stream)
+        return out
 
     def reveal_topk(self, scores, seq_lens: Sequence[int], reveal_counts: Sequence[int], out=None,
                     stream=None):

@@ -1,7 +1,8 @@
 """ctypes binding of libdssample.so: argument marshalling only.
 
 Functions carry the C entry points' names (ds_sample_create, ds_sample,
-ds_sample_device_params, ds_greedy_lse, ds_reveal_topk, ds_repetition_penalty, ds_sample_destroy,
+ds_sample_device_params, ds_greedy_lse, ds_reveal_topk, ds_repetition_penalty, ds_sample_ar,
+ds_sample_destroy,
 ds_last_error, ds_version).  Device buffers are
 torch tensors on a HIP device (torch supplies memory and streams); per-request
 arrays are host sequences.  Every computation happens in the HIP library; when the
@@ -23,7 +24,7 @@ DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY
 DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK, DS_FLAG_COMPACT_U = 0, 1, 2
 
 EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_greedy_lse", "ds_reveal_topk",
-            "ds_repetition_penalty", "ds_sample_destroy", "ds_last_error", "ds_version")
+            "ds_repetition_penalty", "ds_sample_ar", "ds_sample_destroy", "ds_last_error", "ds_version")
 
 _lib = None
 
@@ -60,6 +61,8 @@ def lib():
         L.ds_reveal_topk.argtypes = [P, P, I32, P, P, I32, P, P, P]
         L.ds_repetition_penalty.restype = C.c_int
         L.ds_repetition_penalty.argtypes = [P, P, I64, P, P, P]
+        L.ds_sample_ar.restype = C.c_int
+        L.ds_sample_ar.argtypes = [P, P, P, P, P, P, P, I32, U64, P, P, P]
         L.ds_sample_destroy.restype = None
         L.ds_sample_destroy.argtypes = [P]
         L.ds_last_error.restype = C.c_char_p
@@ -255,6 +258,20 @@ def ds_repetition_penalty(handle: int, logits, n_rows: int, seen_mask, penalty, 
     _check(lib().ds_repetition_penalty(handle, _dev_ptr(logits, "logits"), n_rows,
                                        _dev_ptr(seen_mask, "seen_mask", torch.int32),
                                        _dev_ptr(penalty, "penalty", torch.float32), _stream_ptr(stream, logits)))
+
+
+def ds_sample_ar(handle: int, request_ids, logits, seen_mask, penalty, iterations, temperature, seed: int,
+                 tokens_out, logprobs_out, stream=None) -> None:
+    """Per-request arrays are device tensors (int64, int32, float32); seen_mask
+    and penalty may both be None (no penalty)."""
+    torch = _t()
+    n = int(logits.shape[0])
+    _check(lib().ds_sample_ar(handle, _dev_ptr(request_ids, "request_ids", torch.int64), _dev_ptr(logits, "logits"),
+                              _dev_ptr(seen_mask, "seen_mask", torch.int32), _dev_ptr(penalty, "penalty", torch.float32),
+                              _dev_ptr(iterations, "iterations", torch.int32),
+                              _dev_ptr(temperature, "temperature", torch.float32), n, seed & 0xFFFFFFFFFFFFFFFF,
+                              _dev_ptr(tokens_out, "tokens_out", torch.int32),
+                              _dev_ptr(logprobs_out, "logprobs_out", torch.float32), _stream_ptr(stream, logits)))
 
 
 def ds_reveal_topk(handle: int, scores, num_rows: int, seq_lens: Sequence[int],

@@ -98,6 +98,33 @@ bool use_small_kernel(const ds_sampler* s) { return !(s->flags & DS_FLAG_FORCE_F
 constexpr int32_t kDevParamsMaxRequests = ds::kWave;
 constexpr int64_t kDevParamsMaxPositions = int64_t(1) << 24;
 
+// The device-parameter kernels over every cell of the fixed [num_rows, d.P]
+// layout: the wave-per-cell kernel, or the streaming pair in batches that fit
+// the workspace (padding cells leave at once).
+int launch_dev_params(ds_sampler* s, ds::SampleArgs& a, const ds::DevReq& d, int32_t num_rows,
+                             hipStream_t st) {
+    const bool bf16 = s->dtype == DS_DTYPE_BF16;
+    const int64_t positions = d.P;
+    if (use_small_kernel(s)) {
+        const hipError_t e = ds::launch_sample_small_dev(bf16, a, d, st);
+        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+        return DS_OK;
+    }
+    // the streaming kernels over every cell of the fixed layout, in batches that
+    // fit the workspace; padding cells leave at once
+    const int64_t cells = (int64_t)num_rows * positions;
+    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
+    a.w.nparts = a.w.ppc * s->vocab_chunks;
+    const int64_t slots = ds::kWorkParts / a.w.nparts;
+    for (int64_t c0 = 0; c0 < cells; c0 += slots) {
+        a.w.cell_base = c0;
+        a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
+        const hipError_t e = ds::launch_sample_row_dev(bf16, a, d, st);
+        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
+    }
+    return DS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,26 +387,8 @@ int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const voi
     d.temperature = temperature;
     d.n = num_requests;
     d.P = (int32_t)positions;
-    const bool bf16 = s->dtype == DS_DTYPE_BF16;
-    hipStream_t st = (hipStream_t)stream;
-    if (use_small_kernel(s)) {
-        const hipError_t e = ds::launch_sample_small_dev(bf16, a, d, st);
-        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
-        return DS_OK;
-    }
-    // the streaming kernels over every cell of the fixed layout, in batches that
-    // fit the workspace; padding cells leave at once
-    const int64_t cells = (int64_t)num_rows * positions;
-    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
-    a.w.nparts = a.w.ppc * s->vocab_chunks;
-    const int64_t slots = ds::kWorkParts / a.w.nparts;
-    for (int64_t c0 = 0; c0 < cells; c0 += slots) {
-        a.w.cell_base = c0;
-        a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
-        const hipError_t e = ds::launch_sample_row_dev(bf16, a, d, st);
-        if (e != hipSuccess) return hip_fail(e, "sampler kernel launch");
-    }
-    return DS_OK;
+    d.one_per_request = 0;
+    return launch_dev_params(s, a, d, num_rows, (hipStream_t)stream);
 }
 
 int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* token_out, float* lse_out,
@@ -461,6 +470,60 @@ int ds_repetition_penalty(ds_sampler* s, void* logits, int64_t n_rows, const uin
     const hipError_t e = ds::launch_repetition_penalty(s->dtype == DS_DTYPE_BF16, a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "penalty kernel launch");
     return DS_OK;
+}
+
+int ds_sample_ar(ds_sampler* s, const int64_t* request_ids, void* logits, const uint32_t* seen_mask,
+                 const float* penalty, const int32_t* iterations, const float* temperature, int32_t num_requests,
+                 uint64_t seed, int32_t* tokens_out, float* logprobs_out, void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    if (num_requests < 1 || num_requests > s->max_requests || num_requests > s->max_positions ||
+        num_requests > kDevParamsMaxPositions)
+        return fail(DS_ERR_CAPACITY, "num_requests %d outside [1, min(max_requests, max_positions)]", num_requests);
+    if (!request_ids || !iterations || !temperature)
+        return fail(DS_ERR_INVALID_ARG, "a per-request device array is NULL");
+    if (!logits || !tokens_out || !logprobs_out)
+        return fail(DS_ERR_INVALID_ARG, "logits, tokens_out and logprobs_out must be non-NULL");
+    if (!aligned(request_ids, 8) || !aligned(iterations, 4) || !aligned(temperature, 4))
+        return fail(DS_ERR_INVALID_ARG, "per-request device arrays must be aligned to their element size");
+    if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4))
+        return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+    // the penalty validates logits, seen_mask and penalty, and runs first on the stream
+    if (seen_mask || penalty) {
+        const int rc = ds_repetition_penalty(s, logits, num_requests, seen_mask, penalty, stream);
+        if (rc != DS_OK) return rc;
+    } else {
+        const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+        if (!aligned(logits, es)) return fail(DS_ERR_INVALID_ARG, "logits is not %d-byte aligned", (int)es);
+    }
+
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    ds::SampleArgs a;
+    a.c = logits;
+    a.u = nullptr;
+    a.V = s->vocab;
+    a.rows = 1;
+    a.top_k = s->top_k;
+    a.vocab_chunks = s->vocab_chunks;
+    a.k0 = (uint32_t)seed;
+    a.k1 = (uint32_t)(seed >> 32);
+    a.z0 = s->z0;
+    a.force_fallback = (s->flags & DS_FLAG_FORCE_FALLBACK) ? 1 : 0;
+    a.tokens = tokens_out;
+    a.logprobs = logprobs_out;
+    a.thresholds = nullptr;
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    ds::DevReq d;
+    d.request_ids = request_ids;
+    d.seq_lens = nullptr;
+    d.iterations = iterations;
+    d.guidance = temperature;  // read only when u is present, which it is not
+    d.temperature = temperature;
+    d.n = num_requests;
+    d.P = num_requests;
+    d.one_per_request = 1;
+    return launch_dev_params(s, a, d, 1, (hipStream_t)stream);
 }
 
 int ds_reveal_topk(ds_sampler* s, const float* scores, int32_t num_rows, const int32_t* seq_lens,

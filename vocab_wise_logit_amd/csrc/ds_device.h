@@ -342,8 +342,9 @@ struct DevReq {
     const int32_t* iterations;   // [n]
     const float* guidance;       // [n]
     const float* temperature;    // [n]
-    int32_t n;                   // requests, <= kWave
+    int32_t n;                   // requests (<= kWave unless one_per_request)
     int32_t P;                   // positions of the packed layout: row stride and grid extent
+    int32_t one_per_request;     // position r is request r's only position (seq_lens unread)
 };
 
 // 1 / tau for sampled requests (correctly rounded, as the host computes it), 0
@@ -366,16 +367,24 @@ struct DevCell {
 // is absent, counts as 0; a temperature that is not a positive finite number
 // samples greedily.
 __device__ __forceinline__ bool dev_cell(const DevReq& d, bool have_u, int pl, DevCell& o) {
-    const int lane = lane_id();
-    int T = 0;
-    if (lane < d.n) T = min(max(d.seq_lens[lane], 0), d.P);
-    const int incl = wave_incl_scan(T);
-    const int used = min(__builtin_amdgcn_readlane(incl, kWave - 1), d.P);
-    if (pl >= used) return false;
-    // the first request whose inclusive end passes pl (r < d.n, since pl is
-    // below the sum of the lengths)
-    const int r = popc(ballot(incl <= pl));
-    const int start = __builtin_amdgcn_readlane(incl - T, r);
+    int r, start;
+    if (d.one_per_request) {
+        // one position per request (the autoregressive step): no lengths to scan
+        if (pl >= d.n) return false;
+        r = pl;
+        start = pl;
+    } else {
+        const int lane = lane_id();
+        int T = 0;
+        if (lane < d.n) T = min(max(d.seq_lens[lane], 0), d.P);
+        const int incl = wave_incl_scan(T);
+        const int used = min(__builtin_amdgcn_readlane(incl, kWave - 1), d.P);
+        if (pl >= used) return false;
+        // the first request whose inclusive end passes pl (r < d.n, since pl is
+        // below the sum of the lengths)
+        r = popc(ballot(incl <= pl));
+        start = __builtin_amdgcn_readlane(incl - T, r);
+    }
     const float s = d.guidance[r];
     const float tau = d.temperature[r];
     o.s = (have_u && __builtin_isfinite(s)) ? s : 0.0f;

@@ -1162,7 +1162,7 @@ hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq,
 hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st) {
     const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
     if (parts == 0) return hipSuccess;
-    if (d.n < 1 || d.n > kWave || d.P < 1) return hipErrorInvalidValue;
+    if (d.n < 1 || (d.n > kWave && !d.one_per_request) || d.P < 1) return hipErrorInvalidValue;
     const dim3 mg((unsigned)a.w.ncells);
     const bool exact = a.thresholds != nullptr || a.force_fallback != 0;  // every row selects its threshold
     if (bf16) {

@@ -842,7 +842,8 @@ hipError_t launch_sample_small(bool bf16, const SampleArgs& a, const ReqTable& r
 
 hipError_t launch_sample_small_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st) {
     const int ns = small_slots_needed(bf16, a.V);
-    if (ns > (bf16 ? kSmallMaxSlotsBf16 : kSmallMaxSlotsF32) || d.n < 1 || d.n > kWave || d.P < 1)
+    if (ns > (bf16 ? kSmallMaxSlotsBf16 : kSmallMaxSlotsF32) || d.n < 1 || (d.n > kWave && !d.one_per_request) ||
+        d.P < 1)
         return hipErrorInvalidValue;
     return bf16 ? dispatch<true>(ns, a, d, st) : dispatch<false>(ns, a, d, st);
 }
