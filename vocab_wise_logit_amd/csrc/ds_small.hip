@@ -86,27 +86,30 @@ struct Row {
         return n;
     }
 
-    // Count the ids whose h is >= x and list them in `list` as (h, id), slot by
-    // slot: a ballot per register slot gives each lane holding such an id its
-    // place (the slot's earlier lanes, after the earlier slots' ids).  Every lane
-    // stores every slot, the ids below x to its own spare entry past kListCap, so
-    // the pass has no branch.  Places start from min(count so far, kListCap), so
-    // every store stays inside the list and its kWave spare entries.  Returns
-    // the count; the list is complete when it is <= kListCap.
-    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane) const {
-        int base = 0;
-        Entry* const spare = list + kListCap + lane;
+    // Count the ids whose h is >= x and, if there are at most `cap` (<= kListCap)
+    // of them, write them to `list` as (h, id).  Each lane counts its own ids, a
+    // wave prefix sum places each lane's run, and the lane writes its ids there in
+    // register order.  Every lane stores every slot, the ids below x to its own
+    // spare entry past kListCap, so the pass has no per-slot ballot or branch.
+    // Returns the count.
+    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane, int cap = kListCap) const {
+        int mine = 0;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const bool p = h[i] >= x;
-            const uint64_t m = ballot(p);
-            // (before slot kListCap / kWave the count cannot pass kListCap)
-            Entry* const at = list + (i * kWave <= kListCap ? base : min(base, kListCap)) + lanes_below(m);
-            *(p ? at : spare) = Entry{h[i], id_of(i)};
-            base += popc(m);
+        for (int i = 0; i < NE; ++i) mine += (h[i] >= x) ? 1 : 0;
+        const int incl = wave_incl_scan(mine);
+        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (total <= cap) {
+            const int spare = kListCap + lane;
+            int o = incl - mine;  // < total for every id this lane writes
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                const bool p = h[i] >= x;
+                list[p ? o : spare] = Entry{h[i], id_of(i)};
+                o += p ? 1 : 0;
+            }
         }
         __builtin_amdgcn_wave_barrier();
-        return base;
+        return total;
     }
 
     // Add every id to a per-wave LDS histogram: bin b = trunc(clamp(fma(h,
@@ -622,7 +625,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     for (int i = 0; i < (NE < 4 ? NE : 4); ++i) sub += popc(ballot(R.h[i] >= prune));
     const bool flat = sub * NE > 6 * cap;  // about 1.5 * cap ids expected
     if (!want_t && !flat) {
-        const int nb = R.count_compact(prune, list, lane);
+        const int nb = R.count_compact(prune, list, lane, cap);
         if (nb <= cap) {
             n_list = nb;
             if (nb > k) race_listed(nb, prune);
