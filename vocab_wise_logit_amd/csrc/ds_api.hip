@@ -518,7 +518,7 @@ int ds_sample_ar(ds_sampler* s, const int64_t* request_ids, void* logits, const 
     d.request_ids = request_ids;
     d.seq_lens = nullptr;
     d.iterations = iterations;
-    d.guidance = temperature;  // read only when u is present, which it is not
+    d.guidance = nullptr;  // no u: every guidance scale is 0
     d.temperature = temperature;
     d.n = num_requests;
     d.P = num_requests;

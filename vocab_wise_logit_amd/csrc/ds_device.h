@@ -340,7 +340,7 @@ struct DevReq {
     const int64_t* request_ids;  // [n]
     const int32_t* seq_lens;     // [n]
     const int32_t* iterations;   // [n]
-    const float* guidance;       // [n]
+    const float* guidance;       // [n], read only when u is present
     const float* temperature;    // [n]
     int32_t n;                   // requests (<= kWave unless one_per_request)
     int32_t P;                   // positions of the packed layout: row stride and grid extent
@@ -385,9 +385,14 @@ __device__ __forceinline__ bool dev_cell(const DevReq& d, bool have_u, int pl, D
         r = popc(ballot(incl <= pl));
         start = __builtin_amdgcn_readlane(incl - T, r);
     }
-    const float s = d.guidance[r];
+    // guidance is read only where u is: without u every scale is 0
+    float s = 0.0f;
+    if (have_u) {
+        s = d.guidance[r];
+        if (!__builtin_isfinite(s)) s = 0.0f;
+    }
     const float tau = d.temperature[r];
-    o.s = (have_u && __builtin_isfinite(s)) ? s : 0.0f;
+    o.s = s;
     o.tau = (tau > 0.0f && tau < __builtin_huge_valf()) ? tau : 0.0f;
     o.inv_tau = inv_temperature(o.tau);
     o.t = (uint32_t)(pl - start);
