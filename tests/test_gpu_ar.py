@@ -126,3 +126,48 @@ def test_ar_step_without_penalty_equals_ds_sample_rows():
         torch.cuda.synchronize()
     assert np.array_equal(tok.cpu().numpy(), t2.view(-1).cpu().numpy())
     assert np.array_equal(lp.cpu().numpy().view(np.uint32), l2.view(-1).cpu().numpy().view(np.uint32))
+
+
+def test_ar_step_replayed_from_a_graph_follows_device_parameters():
+    """A captured autoregressive step reads its parameters when it runs: replays
+    after the iterations and temperatures change match fresh eager calls."""
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    R, V = 96, 4096
+    w = synth.ar(n_requests=R, vocab=V, seed=55, seen_lo=20, seen_hi=300, temperatures=(0.0, 0.8, 1.0))
+    log(f"[gpu] ar graph: R={R} V={V}")
+    with ds.Sampler(V, "bf16", max_rows=1, max_positions=R, max_requests=R, top_k=w.top_k) as smp:
+        x0 = to_dev(w.logits)
+        x = x0.clone()
+        seen = torch.from_numpy(w.seen.view(np.int32)).cuda()
+        pen = torch.from_numpy(w.penalty).cuda()
+        rid = torch.tensor(w.request_ids, device="cuda")
+        it = torch.tensor(w.iterations, device="cuda")
+        tp = torch.tensor(w.temperature, device="cuda")
+        out = (torch.empty(R, dtype=torch.int32, device="cuda"), torch.empty(R, dtype=torch.float32, device="cuda"))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            smp.sample_ar(rid, x, seen, pen, it, tp, seed=w.seed, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        x.copy_(x0)
+        with torch.cuda.graph(g):
+            smp.sample_ar(rid, x, seen, pen, it, tp, seed=w.seed, out=out)
+        for step in range(4):
+            it.fill_(step + 3)
+            tp.copy_(torch.tensor(np.roll(w.temperature, step), device="cuda"))
+            x.copy_(x0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = (out[0].cpu().numpy().copy(), out[1].cpu().numpy().copy())
+            xe = x0.clone()
+            ref = smp.sample_ar(rid, xe, seen, pen, it, tp, seed=w.seed)
+            torch.cuda.synchronize()
+            assert np.array_equal(got[0], ref[0].cpu().numpy()), f"replay {step}: tokens differ"
+            assert np.array_equal(got[1].view(np.uint32), ref[1].cpu().numpy().view(np.uint32))
+            assert torch.equal(x, xe), f"replay {step}: penalised logits differ"
