@@ -106,6 +106,7 @@ struct MergeLDS {
     } u;
     uint32_t hist[kHistBins];
     int nkeys;
+    int nabove;
     RedT<MT_ / kWave> r;
 };
 
@@ -247,6 +248,29 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
     }
 }
 
+// Visit the ids of every `every`-th run of 64 pieces of the row: f(v, h).  One
+// piece per lane; the sample's runs are spread over the whole row.
+template <bool BF16, int BT, typename F>
+__device__ __forceinline__ void for_each_sampled_id(const RowGeom& G, float s, bool use_u, int every, F&& f) {
+    constexpr int EPP = Piece<BF16>::EPP;
+    const int64_t q0 = G.gbase / EPP;
+    const int64_t q1 = (G.gbase + G.V - 1) / EPP;
+    const int64_t runs = (q1 - q0) / kWave + 1;
+    for (int64_t r = (int64_t)(threadIdx.x / kWave) * every; r < runs; r += (int64_t)(BT / kWave) * every) {
+        const int64_t q = q0 + r * kWave + lane_id();
+        if (q <= q1) {
+            const u32x4 cw = stream_load(G.c16 + q);
+            const u32x4 uw = use_u ? stream_load(G.u16 + q) : cw;
+            Piece<BF16> P;
+            decode_piece<BF16>(cw, uw, s, use_u, P);
+            const int64_t v0 = q * EPP - G.gbase;
+#pragma unroll
+            for (int e = 0; e < EPP; ++e)
+                if (v0 + e >= 0 && v0 + e < G.V) f((int)(v0 + e), P.h[e]);
+        }
+    }
+}
+
 // The digit (histogram bin) holding the kk-th largest key among those counted
 // in sh.hist[0, nbins), with 1 <= kk <= their number; kk becomes the rank inside
 // that bin.  Thread j owns bins nbins-1-j*b .. nbins-b-j*b (b = nbins / threads),
@@ -301,14 +325,23 @@ __device__ __forceinline__ int wave_append(bool pred, int* counter) {
     return pred ? base + lanes_below(m) : -1;
 }
 
-// Exact top_k-th largest h of the row (an LDS radix select on order keys).  One
-// pass over the row histograms the first 11-bit digit; a second collects the
-// keys in the chosen bin into LDS, where the last two digits are selected.  If
-// that bin holds more than kKeyCap keys, the last digits take a pass over the
-// row each instead.
+// Exact top_k-th largest h of the row (an LDS radix select on order keys).
+//
+// On long rows a sample comes first: the keys of every `every`-th run of 64
+// pieces (at most kKeyCap of them) go to LDS, and two selects there bracket the
+// answer between the sample's order statistics around rank k * n / V, three
+// standard deviations out each way.  One pass over the row then counts the keys
+// above the bracket and collects those inside it; when the k-th largest falls
+// inside and the bracket fits in LDS, it is selected there exactly.  Otherwise
+// (an unlucky sample, or too many keys in the bracket) the full path runs: one
+// pass histograms the first 11-bit digit, a second collects the keys in the
+// chosen bin into LDS, where the last two digits are selected, and if that bin
+// holds more than kKeyCap keys the last digits take a pass over the row each.
+// The result is exact either way; the sample only saves a pass.
 template <bool BF16, typename SH>
-__device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, SH& sh) {
+__device__ __forceinline__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, SH& sh) {
     constexpr int BT = SH::kThreads;
+    constexpr int EPP = Piece<BF16>::EPP;
     uint32_t prefix = 0, pmask = 0;
     int kk = k;
     auto hist_pass = [&](int dg, bool from_lds, int n) {
@@ -332,6 +365,70 @@ __device__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, 
         prefix |= d << shift;
         pmask |= dmask << shift;
     };
+    // the rank-th largest of the n keys in LDS (1 <= rank <= n)
+    auto lds_kth = [&](int n, int rank) {
+        prefix = 0;
+        pmask = 0;
+        kk = rank;
+        hist_pass(0, true, n);
+        hist_pass(1, true, n);
+        hist_pass(2, true, n);
+        return prefix;
+    };
+
+    // ---- sampled bracket
+    const int64_t runs = ((G.gbase + G.V - 1) / EPP - G.gbase / EPP) / kWave + 1;
+    constexpr int kRunIds = kWave * EPP;
+    constexpr int kSampleRuns = SH::kKeyCap / kRunIds - 1;  // ceil(runs / every) <= runs / every + 1
+    const int every = kSampleRuns > 0 ? (int)((runs + kSampleRuns - 1) / kSampleRuns) : 0;
+    // the bracket's expected width in row ids, 2 m / f with f the sampled share,
+    // must leave room in LDS (checked again on the sample actually drawn)
+    const float f_exp = (float)(((runs + every - 1) / max(every, 1)) * kRunIds) / (float)G.V;
+    const float m_exp = 3.0f * __builtin_sqrtf((float)k * f_exp) + 4.0f;
+    if (every >= 4 && 2.0f * m_exp < 0.7f * (float)SH::kKeyCap * f_exp) {
+        if (threadIdx.x == 0) sh.nkeys = 0;
+        __syncthreads();
+        for_each_sampled_id<BF16, BT>(G, s, use_u, every, [&](int, float h) {
+            const int at = wave_append(true, &sh.nkeys);
+            if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = order_key(h + 0.0f);
+        });
+        __syncthreads();
+        const int ns = min(sh.nkeys, SH::kKeyCap);
+        // expected sample rank of the answer and a margin of three standard deviations
+        const float f = (float)ns / (float)G.V;
+        const float r = (float)k * f;
+        const float m = 3.0f * __builtin_sqrtf(r) + 4.0f;
+        // the bracket's expected width in row ids must leave room in LDS
+        if (ns > 0 && 2.0f * m < 0.7f * (float)SH::kKeyCap * f) {
+            const int r_hi = (int)__builtin_floorf(r - m);
+            const int r_lo = (int)__builtin_ceilf(r + m);
+            const uint32_t key_hi = r_hi >= 1 ? lds_kth(ns, r_hi) : 0xFFFFFFFFu;
+            const uint32_t key_lo = r_lo <= ns ? lds_kth(ns, r_lo) : 0u;
+            if (threadIdx.x == 0) {
+                sh.nkeys = 0;
+                sh.nabove = 0;
+            }
+            __syncthreads();
+            int above = 0;
+            for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
+                const uint32_t key = order_key(h + 0.0f);
+                above += key > key_hi ? 1 : 0;
+                const int at = wave_append(key >= key_lo && key <= key_hi, &sh.nkeys);
+                if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = key;
+            });
+            if (above) atomicAdd(&sh.nabove, above);
+            __syncthreads();
+            const int n = sh.nkeys;
+            const int A = sh.nabove;
+            __syncthreads();
+            if (n <= SH::kKeyCap && A < k && k <= A + n) return key_value(lds_kth(n, k - A));
+        }
+        prefix = 0;
+        pmask = 0;
+        kk = k;
+    }
+
+    // ---- full path
     hist_pass(0, false, 0);
     // keep the keys that share the first digit with the answer
     if (threadIdx.x == 0) sh.nkeys = 0;
@@ -699,7 +796,7 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
 // equal maxima keep the smaller id, sums add in probability space), then finish
 // the greedy or sampled decision.
 template <bool BF16, bool SAMPLE, int MT_, int KCAP>
-__device__ void merge_body(const void* cptr, const void* uptr, int V, int nch, int top_k, bool force_fallback,
+__device__ __forceinline__ void merge_body(const void* cptr, const void* uptr, int V, int nch, int top_k, bool force_fallback,
                            const RowWork& w, const CellParams& cp, int64_t slot, int* tokens, float* logprobs,
                            float* lse_out, float* thresholds, float* triples, int64_t n_rows) {
     __shared__ MergeLDS<MT_, KCAP> sh;
