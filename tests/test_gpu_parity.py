@@ -198,6 +198,22 @@ def test_row_kernel_threshold_bin_overflow():
     check_sample(w, run_sample(w, force_fallback=True), ref)
 
 
+def test_row_kernel_threshold_sample_misses_a_hidden_cluster():
+    # the long-row select brackets the threshold from a sample of runs of 512
+    # ids; here the largest ids sit in runs the sample skips (ids 512..2047), so
+    # the bracket lies below the answer and the exact two-pass select must take
+    # over; the second position, without the cluster, takes the bracket
+    V = 30000
+    w = synth.diffusion("hidden_cluster", seed=44, vocab=V, rows=1, seq_lens=[2], sigma=1.0, guidance=0.0,
+                        temperature=1.0, top_k=1000)
+    x = oracle.bf16_to_f32(w.c)
+    x[0, 0, 512:2048] += np.float32(10.0)
+    w.c = synth.bf16_from_f32(x)
+    ref = oracle.sample_workload(w)
+    for thr in (False, True):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+
+
 def test_row_kernel_many_parts_per_row():
     # 4 positions x 4 chunks: each chunk is cut into several parts, each running
     # its own race
