@@ -171,3 +171,20 @@ def test_ar_step_replayed_from_a_graph_follows_device_parameters():
             assert np.array_equal(got[0], ref[0].cpu().numpy()), f"replay {step}: tokens differ"
             assert np.array_equal(got[1].view(np.uint32), ref[1].cpu().numpy().view(np.uint32))
             assert torch.equal(x, xe), f"replay {step}: penalised logits differ"
+
+
+def test_sampler_left_open_at_exit_is_released_cleanly():
+    """A sampler still alive when the interpreter exits is destroyed without an
+    error, though the binding's module globals may already be gone."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import vocab_wise_logit_amd as ds\n"
+            "s = ds.Sampler(1025, 'bf16', max_rows=1, max_positions=4, max_requests=1)\n"
+            "print('ok', flush=True)\n")
+    log("[gpu] fresh process: sampler alive at exit")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]
+    assert "Exception ignored" not in r.stderr and "Traceback" not in r.stderr, r.stderr[-2000:]

@@ -69,9 +69,10 @@ class Sampler:
         self._h = ds_sample_create(device, vocab, DS_DTYPE_BF16 if dtype == "bf16" else DS_DTYPE_F32,
                                    max_rows, max_positions, max_requests, top_k, vocab_chunks, flags)
         self._stage = RequestStage(max_requests)
-        # held by the object: at interpreter exit the module's globals may be gone
-        # before a sampler that is still alive is collected
-        self._destroy = ds_sample_destroy
+        # the C function itself, held by the object: at interpreter exit the
+        # modules' globals (this binding's included) may be gone before a
+        # sampler that is still alive is collected
+        self._destroy = lib().ds_sample_destroy
 
     def close(self) -> None:
         if getattr(self, "_h", None):
