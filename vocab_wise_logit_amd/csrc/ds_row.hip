@@ -409,12 +409,16 @@ __device__ __forceinline__ float radix_select_row(const RowGeom& G, float s, boo
                 sh.nabove = 0;
             }
             __syncthreads();
+            // compared as floats (the key order is the order of h + 0, and h is
+            // never NaN here); only the collected ids need their key
+            // (the open ends, keys 0xFFFFFFFF and 0, decode to NaN: they become +-inf)
+            const float f_hi = key_hi == 0xFFFFFFFFu ? __builtin_inff() : key_value(key_hi);
+            const float f_lo = key_lo == 0u ? -__builtin_inff() : key_value(key_lo);
             int above = 0;
             for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
-                const uint32_t key = order_key(h + 0.0f);
-                above += key > key_hi ? 1 : 0;
-                const int at = wave_append(key >= key_lo && key <= key_hi, &sh.nkeys);
-                if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = key;
+                above += h > f_hi ? 1 : 0;
+                const int at = wave_append(h >= f_lo && h <= f_hi, &sh.nkeys);
+                if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = order_key(h + 0.0f);
             });
             if (above) atomicAdd(&sh.nabove, above);
             __syncthreads();
