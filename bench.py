@@ -346,9 +346,11 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     # positions: cells sampled, draft rows reduced, or cells ranked by the reveal
     cells = {"draft": lambda: w.n_rows, "reveal": lambda: w.rows * w.positions,
              "ar": lambda: w.rows}.get(kind, lambda: w.cells)()
-    # every workload here has <= 64 requests, so one step is one launch of the
-    # wave-per-cell kernel (its back-to-back time per step is that kernel's
-    # average duration on its stream) or one parts + merge pair
+    # one step is one launch of the wave-per-cell kernel (every sampling workload
+    # here has <= 64 requests, one request table), so its back-to-back time per
+    # step is that kernel's average duration on its stream; or one parts + merge
+    # pair; or, for the autoregressive step, the penalty kernel and one sampler
+    # launch over all its requests (launches_per_step)
     achieved = alg / (ms_step * 1e-3) / 1e9
     cfg = describe(w, kind)
     if threshold:
