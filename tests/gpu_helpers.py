@@ -8,7 +8,11 @@ Bar (fixed before any kernel was written):
     fp32 inputs against the oracle's double precision);
   - sampled token ids: exact, except cells where the oracle's best and second-best
     perturbed scores differ by less than 1e-5 relative (near ties, where fp32 and
-    double may legitimately order them differently); those are counted.
+    double may legitimately order them differently).  Those are counted, bounded
+    (by default at most max(2, 1e-3 * sampled cells) per workload; a test whose
+    scores sit far from zero by construction states its own bound), reported in
+    the session summary, and a near-tie cell whose token differs must still have
+    drawn a kept id whose oracle score lies within the band of the best score.
 """
 
 from __future__ import annotations
@@ -21,6 +25,15 @@ import numpy as np
 import oracle
 
 LP_TOL = 1e-4
+NEAR_TIE_BAND = 1e-5
+
+# (workload, sampled cells, oracle near ties, near ties with a different token);
+# printed by the terminal summary of tests/conftest.py
+NEAR_TIE_TALLY: list = []
+
+
+def default_near_tie_bound(sampled: int) -> float:
+    return max(2.0, 1e-3 * sampled)
 
 
 def to_dev(arr: np.ndarray):
@@ -73,13 +86,60 @@ class Report:
     max_lp_err: float
 
 
-def check_sample(w, got, ref: "oracle.SampleResult", *, check_threshold: bool = True) -> Report:
+def _cell_request(w, cell: int):
+    """(row, request index, position inside the request) of a packed cell."""
+    P = max(1, w.positions)
+    row, p = divmod(int(cell), P)
+    offs = np.concatenate([[0], np.cumsum(w.seq_lens)])
+    r = int(np.searchsorted(offs, p, side="right") - 1)
+    return row, r, p - int(offs[r])
+
+
+def _oracle_h(w, cell: int, v: int) -> float:
+    """The oracle's guided logit of id v in one cell."""
+    row, r, _ = _cell_request(w, cell)
+    P = max(1, w.positions)
+    p = int(cell) % P
+    s = float(w.guidance[r])
+    conv = oracle.bf16_to_f32 if w.dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+    c = float(conv(np.asarray([w.c[row, p, v]]))[0])
+    u = float(conv(np.asarray([w.u[row, p, v]]))[0]) if s != 0.0 else 0.0
+    return oracle.guided_logit(c, u, s)
+
+
+def _oracle_z(w, cell: int, v: int, h: float) -> float:
+    row, r, t = _cell_request(w, cell)
+    word = oracle.noise_word(int(w.seed), int(w.request_ids[r]), int(w.iterations[r]), row, t, int(v))
+    return float(np.float32(h)) / float(np.float32(w.temperature[r])) + oracle.gumbel(word)
+
+
+def check_near_tie_choice(w, cell: int, gpu_tok: int, ref_tok: int, threshold: float) -> None:
+    """A near-tie cell whose GPU token differs from the oracle's: the GPU's id must
+    be kept (h at or above the oracle's threshold) and its oracle score must lie
+    within the band of the oracle's best score."""
+    hg = _oracle_h(w, cell, gpu_tok)
+    assert 0 <= gpu_tok < w.vocab and oracle.order_key(hg) >= oracle.order_key(threshold), \
+        f"cell {cell}: near-tie token {gpu_tok} is not kept"
+    z1 = _oracle_z(w, cell, ref_tok, _oracle_h(w, cell, ref_tok))
+    zg = _oracle_z(w, cell, gpu_tok, hg)
+    assert z1 - zg < NEAR_TIE_BAND * max(1.0, abs(z1)), \
+        f"cell {cell}: token {gpu_tok} scores {zg}, outside the band of the best {z1} (id {ref_tok})"
+
+
+def check_sample(w, got, ref: "oracle.SampleResult", *, check_threshold: bool = True,
+                 max_near_ties=None) -> Report:
     cells = ref.cells
     tok = got[0][cells]
     lp = got[1][cells]
     tau = cell_temperature(w, cells)
     greedy = tau == 0
     near = ref.near_tie.astype(bool) & ~greedy
+    sampled = int((~greedy).sum())
+    bound = default_near_tie_bound(sampled) if max_near_ties is None else max_near_ties
+    assert near.sum() <= bound, (f"{w.name}: {int(near.sum())} oracle near ties among {sampled} sampled cells "
+                                 f"exceeds the bound {bound}")
+    for i in np.nonzero(near & (tok != ref.tokens))[0]:
+        check_near_tie_choice(w, int(cells[i]), int(tok[i]), int(ref.tokens[i]), float(ref.thresholds[i]))
     bad_greedy = np.nonzero(greedy & (tok != ref.tokens))[0]
     assert bad_greedy.size == 0, f"greedy token mismatch at cells {cells[bad_greedy[:10]]}"
     bad = np.nonzero(~greedy & ~near & (tok != ref.tokens))[0]
@@ -96,9 +156,10 @@ def check_sample(w, got, ref: "oracle.SampleResult", *, check_threshold: bool = 
         o = ref.thresholds[~greedy].view(np.uint32)
         badt = np.nonzero(g != o)[0]
         assert badt.size == 0, f"threshold mismatch at cells {cells[~greedy][badt[:10]]}"
-    rep = Report(cells=int(cells.size), greedy=int(greedy.sum()), sampled=int((~greedy).sum()),
+    rep = Report(cells=int(cells.size), greedy=int(greedy.sum()), sampled=sampled,
                  near_ties=int(near.sum()), near_tie_mismatch=int((near & (tok != ref.tokens)).sum()),
                  max_lp_err=max_err)
+    NEAR_TIE_TALLY.append((w.name, rep.sampled, rep.near_ties, rep.near_tie_mismatch))
     log(f"[check] {w.name}: {rep}")
     return rep
 

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import LP_TOL, log, to_dev
+from gpu_helpers import (LP_TOL, NEAR_TIE_TALLY, check_near_tie_choice, default_near_tie_bound, log,
+                         to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +25,18 @@ CASES = [
     ("many_small_bf16", 150, 1025, "bf16", (5, 100), (0.0, 0.9), None),
     ("many_row_bf16", 90, 8192, "bf16", (50, 500), (0.0, 1.0), None),
 ]
+
+
+def ar_as_diffusion(w, penalised):
+    """The step's sampling half as the diffusion call it equals: one position per
+    request, guidance 0, the penalised logits as c."""
+    R = penalised.shape[0]
+    return synth.DiffusionWorkload(name=f"{w.name}_as_cells", dtype=w.dtype, vocab=w.vocab, rows=1,
+                                   seq_lens=np.ones(R, np.int32), request_ids=np.asarray(w.request_ids, np.int64),
+                                   iterations=np.asarray(w.iterations, np.int32),
+                                   guidance=np.zeros(R, np.float32),
+                                   temperature=np.asarray(w.temperature, np.float32),
+                                   c=penalised.reshape(1, R, w.vocab), u=None, top_k=w.top_k, seed=w.seed)
 
 
 def _run(w, smp):
@@ -54,9 +67,16 @@ def test_ar_step_matches_oracle(case):
     assert np.array_equal(xo, pen), "penalised logits differ from the oracle"
     greedy = w.temperature == 0
     near = ref.near_tie.astype(bool) & ~greedy
+    sampled = int((~greedy).sum())
+    assert near.sum() <= default_near_tie_bound(sampled), f"{int(near.sum())} near ties in {sampled} sampled rows"
     assert np.array_equal(tok[greedy], ref.tokens[greedy])
     bad = np.nonzero(~greedy & ~near & (tok != ref.tokens))[0]
     assert bad.size == 0, f"sampled token mismatch at requests {bad[:10]}"
+    # a near-tie row that drew another id drew a kept one within the band
+    aw = ar_as_diffusion(w, pen)
+    for i in np.nonzero(near & (tok != ref.tokens))[0]:
+        check_near_tie_choice(aw, int(i), int(tok[i]), int(ref.tokens[i]), float(ref.thresholds[i]))
+    NEAR_TIE_TALLY.append((f"ar_{name}", sampled, int(near.sum()), int((near & (tok != ref.tokens)).sum())))
     same = tok == ref.tokens
     assert np.max(np.abs(lp[same].astype(np.float64) - ref.logprobs[same])) <= LP_TOL
     log(f"[check] ar {name}: greedy={int(greedy.sum())} sampled={int((~greedy).sum())} near_ties={int(near.sum())}")

@@ -271,10 +271,15 @@ def test_flat_rows_histogram_narrowing(dtype):
             f = np.round(f / grid) * grid
         w.c = synth.bf16_from_f32(f) if dtype == "bf16" else f.astype(np.float32)
         ref = oracle.sample_workload(w)
+        # constant rows at temperatures of 1e-30 and 1e-3 score |z1| >= 1250, so
+        # the relative band (>= 1.25e-2) holds every kept id's noise difference
+        # at tau = 1e-30 (scores are h / tau to within 1e-29 relative) and most of
+        # them at 1e-3: every sampled cell may be a near tie there
+        bound = w.cells if sigma == 0.0 else None
         got = run_sample(w)
-        check_sample(w, got, ref)
+        check_sample(w, got, ref, max_near_ties=bound)
         got2 = run_sample(w, threshold=False)
-        check_sample(w, got2, ref)
+        check_sample(w, got2, ref, max_near_ties=bound)
         assert np.array_equal(got[0], got2[0])
 
 

@@ -20,6 +20,7 @@ import pytest
 import scipy.special
 import scipy.stats
 
+import near_tie_pin
 import oracle
 from oracle.build_oracle import SRC, build
 
@@ -63,6 +64,13 @@ MUTANTS = {
                        "return (uint16_t)(hi >> 16);"),
     "bf16_truncates": ("if (dlo < dhi) return (uint16_t)(lo >> 16);",
                        "if (dlo <= dhi + 1e300) return (uint16_t)(lo >> 16);"),
+    # the near-tie classification that excuses sampled cells from token equality
+    "near_tie_always": ("*near_tie = (z1 - z2) < 1e-5 * scale;", "*near_tie = 1;"),
+    "near_tie_never": ("*near_tie = (z1 - z2) < 1e-5 * scale;", "*near_tie = 0;"),
+    "near_tie_wide_band": ("*near_tie = (z1 - z2) < 1e-5 * scale;", "*near_tie = (z1 - z2) < 1e-1 * scale;"),
+    "near_tie_absolute_band": ("double scale = fabs(z1) > 1.0 ? fabs(z1) : 1.0;", "double scale = 1.0;"),
+    "z2_not_demoted": ("if (best >= 0) z2 = z1;", "if (best >= 0) z2 = z2;"),
+    "z2_later_ids_ignored": ("} else if (z > z2) {", "} else if (0 && z > z2) {"),
 }
 
 
@@ -228,8 +236,13 @@ def check_penalty(lib):
     assert np.array_equal(out, want)
 
 
+def check_near_tie(lib):
+    near_tie_pin.check(lib=lib, noise_lib=oracle._load())
+
+
 CHECKS = [check_guided, check_bf16, check_logprobs, check_philox, check_gumbel,
-          check_threshold, check_greedy, check_sampling, check_draft, check_reveal, check_penalty]
+          check_threshold, check_greedy, check_sampling, check_draft, check_reveal, check_penalty,
+          check_near_tie]
 
 
 def _failures(lib):

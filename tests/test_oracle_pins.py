@@ -23,6 +23,7 @@ import pytest
 import scipy.special
 import scipy.stats
 
+import near_tie_pin
 import oracle
 import synth
 
@@ -406,6 +407,17 @@ def test_changing_iteration_or_seed_changes_draws_and_repeats_are_identical():
     w.seed = 43
     d = oracle.sample_workload(w)
     assert np.mean(a.tokens != d.tokens) > 0.1
+
+
+def test_near_tie_flag_and_gap_recomputed_from_pinned_noise():
+    # The flag that excuses a sampled cell from token equality, recomputed in
+    # Python double from the pinned noise word and Gumbel map: about 1200 random
+    # cells plus races built to land just inside and just outside the band, with
+    # scores near 1, 100 and 1000 (where the band is relative).
+    checked, near, (inside, outside) = near_tie_pin.check()
+    assert checked >= 1200
+    assert inside >= 6 and outside >= 6
+    assert near >= inside
 
 
 def test_unread_u_rows_may_hold_nan():
