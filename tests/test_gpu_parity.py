@@ -495,13 +495,31 @@ def test_invalid_calls_are_rejected_before_launch():
             dict(num_rows=3),
         ]
         for bad in cases:
+            args = dict(request_ids=w.request_ids, u_logits=u, seq_lens=w.seq_lens,
+                        iterations=w.iterations, guidance_scale=w.guidance,
+                        temperature=w.temperature, num_rows=2)
+            args.update(bad)
+            log(f"[gpu] invalid call {bad}")
+            # straight to the C entry point (the binding refuses some of these
+            # itself, by the tensors' shapes): the library must reject each one
+            # before anything is enqueued
+            host = [np.ascontiguousarray(args[k], dt) for k, dt in
+                    (("request_ids", np.int64), ("seq_lens", np.int32), ("iterations", np.int32),
+                     ("guidance_scale", np.float32), ("temperature", np.float32))]
+            up = args["u_logits"].data_ptr() if args["u_logits"] is not None else None
+            rc = ds.lib().ds_sample(smp._h, host[0].ctypes.data, c.data_ptr(), up, host[1].ctypes.data,
+                                    host[2].ctypes.data, host[3].ctypes.data, host[4].ctypes.data,
+                                    host[0].size, args["num_rows"], 1, tok.data_ptr(), lp.data_ptr(), None,
+                                    torch.cuda.current_stream().cuda_stream)
+            assert rc != ds.DS_OK, bad
+        # the binding refuses the tensors that do not match the call's sizes
+        for bad in (dict(seq_lens=[17]), dict(num_rows=3)):
             args = dict(request_ids=w.request_ids, c_logits=c, u_logits=u, seq_lens=w.seq_lens,
                         iterations=w.iterations, guidance_scale=w.guidance,
                         temperature=w.temperature, num_rows=2, seed=1, tokens_out=tok,
                         logprobs_out=lp)
             args.update(bad)
-            log(f"[gpu] invalid call {bad}")
-            with pytest.raises(ds.DSError):
+            with pytest.raises(ValueError):
                 ds.ds_sample(smp._h, **args)
         torch.cuda.synchronize()
         assert int((tok == -7).sum()) == tok.numel()  # nothing was written

@@ -28,6 +28,13 @@ EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_gree
 
 _lib = None
 
+# What each live handle was created for, keyed by its address: (vocab, dtype,
+# vocab_chunks, flags).  The calls below check the shapes and element types of the
+# tensors they are given against it before calling into the library, which
+# trusts the sizes it derives from its arguments (a short or mistyped tensor would
+# otherwise be read or written past its end).
+_HANDLES: dict = {}
+
 
 class DSError(RuntimeError):
     def __init__(self, code: int, msg: str):
@@ -105,6 +112,46 @@ def _dev_ptr(t, what: str, dtype=None) -> Optional[int]:
     return t.data_ptr()
 
 
+def _info(handle: int):
+    info = _HANDLES.get(handle)
+    if info is None:
+        raise ValueError("unknown or destroyed sampler handle")
+    return info
+
+
+def _logit_dtype(code: int):
+    torch = _t()
+    return torch.bfloat16 if code == DS_DTYPE_BF16 else torch.float32
+
+
+def _need_shape(t, what: str, shape: tuple) -> None:
+    """t must be a torch tensor of exactly `shape`."""
+    torch = _t()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor on a HIP device")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _need_logits(t, what: str, shape: tuple, code: int) -> None:
+    _need_shape(t, what, shape)
+    if t.dtype != _logit_dtype(code):
+        raise TypeError(f"{what} must have dtype {_logit_dtype(code)} like the sampler (got {t.dtype})")
+
+
+def _need_numel(t, what: str, n: int, dtype) -> None:
+    """t (if given) must hold at least n elements of dtype."""
+    if t is None:
+        return
+    torch = _t()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor on a HIP device")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must have dtype {dtype} (got {t.dtype})")
+    if t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements; the call writes or reads {n}")
+
+
 def _host(a, dtype) -> np.ndarray:
     if type(a) is np.ndarray and a.dtype == dtype and a.flags.c_contiguous:
         return a
@@ -136,10 +183,12 @@ def ds_sample_create(device: int, vocab: int, dtype: int, max_rows: int, max_pos
     h = C.c_void_p()
     _check(lib().ds_sample_create(C.byref(h), device, vocab, dtype, max_rows, max_positions,
                                   max_requests, top_k, vocab_chunks, flags))
+    _HANDLES[h.value] = (int(vocab), int(dtype), int(vocab_chunks), int(flags))
     return h.value
 
 
 def ds_sample_destroy(handle: int) -> None:
+    _HANDLES.pop(handle, None)
     lib().ds_sample_destroy(handle)
 
 
@@ -195,9 +244,11 @@ def ds_sample(handle: int, request_ids: Sequence[int], c_logits, u_logits, seq_l
               temperature: Sequence[float], num_rows: int, seed: int, tokens_out, logprobs_out,
               threshold_out=None, stream=None, stage: Optional[RequestStage] = None) -> None:
     torch = _t()
+    V, code, _, flags = _info(handle)
     n = stage.fill(request_ids, seq_lens, iterations, guidance_scale, temperature) if stage is not None else -1
     if n > 0:
         prid, psl, pit, pgs, ptp = stage.ptrs
+        sl, gs = stage.sl[:n], stage.gs[:n]
     else:
         rid = _host(request_ids, np.int64)
         sl = _host(seq_lens, np.int32)
@@ -208,6 +259,14 @@ def ds_sample(handle: int, request_ids: Sequence[int], c_logits, u_logits, seq_l
         if not (sl.size == it.size == gs.size == tp.size == n):
             raise ValueError("per-request arrays must all have num_requests entries")
         prid, psl, pit, pgs, ptp = (a.ctypes.data for a in (rid, sl, it, gs, tp))
+    P = int(sl.sum())
+    _need_logits(c_logits, "c_logits", (num_rows, P, V), code)
+    if u_logits is not None:
+        Pu = int(sl[gs != 0].sum()) if flags & DS_FLAG_COMPACT_U else P
+        _need_logits(u_logits, "u_logits", (num_rows, Pu, V), code)
+    _need_numel(tokens_out, "tokens_out", num_rows * P, torch.int32)
+    _need_numel(logprobs_out, "logprobs_out", num_rows * P, torch.float32)
+    _need_numel(threshold_out, "threshold_out", num_rows * P, torch.float32)
     cp = _dev_ptr(c_logits, "c_logits")
     up = _dev_ptr(u_logits, "u_logits")
     _check(lib().ds_sample(handle, prid, cp, up, psl, pit, pgs, ptp, n, num_rows, seed & (2**64 - 1),
@@ -224,6 +283,7 @@ def ds_sample_device_params(handle: int, request_ids, c_logits, u_logits, seq_le
     ids, int32 lengths and iterations, float32 guidance and temperature); the
     packed layout's positions are c_logits.shape[1]."""
     torch = _t()
+    V, code, _, _ = _info(handle)
     if not isinstance(request_ids, torch.Tensor):
         raise TypeError("request_ids must be a device tensor")
     n = int(request_ids.numel())
@@ -231,6 +291,15 @@ def ds_sample_device_params(handle: int, request_ids, c_logits, u_logits, seq_le
                     (temperature, "temperature")):
         if not isinstance(t, torch.Tensor) or int(t.numel()) != n:
             raise ValueError(f"{what} must be a device tensor with as many entries as request_ids")
+    if not isinstance(c_logits, torch.Tensor) or c_logits.dim() != 3:
+        raise ValueError("c_logits must be a [num_rows, positions, V] tensor")
+    positions = int(c_logits.shape[1])
+    _need_logits(c_logits, "c_logits", (num_rows, positions, V), code)
+    if u_logits is not None:
+        _need_logits(u_logits, "u_logits", (num_rows, positions, V), code)
+    _need_numel(tokens_out, "tokens_out", num_rows * positions, torch.int32)
+    _need_numel(logprobs_out, "logprobs_out", num_rows * positions, torch.float32)
+    _need_numel(threshold_out, "threshold_out", num_rows * positions, torch.float32)
     _check(lib().ds_sample_device_params(
         handle, _dev_ptr(request_ids, "request_ids", torch.int64), _dev_ptr(c_logits, "c_logits"),
         _dev_ptr(u_logits, "u_logits"), _dev_ptr(seq_lens, "seq_lens", torch.int32),
@@ -244,6 +313,14 @@ def ds_sample_device_params(handle: int, request_ids, c_logits, u_logits, seq_le
 def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_out,
                   triples_out=None, stream=None) -> None:
     torch = _t()
+    V, code, chunks, _ = _info(handle)
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2 or logits.shape[0] < n_rows:
+        raise ValueError(f"logits must be a [n_rows, V] tensor with at least {n_rows} rows")
+    _need_logits(logits, "logits", (int(logits.shape[0]), V), code)
+    _need_numel(token_out, "token_out", n_rows, torch.int32)
+    _need_numel(lse_out, "lse_out", n_rows, torch.float32)
+    _need_numel(logprob_out, "logprob_out", n_rows, torch.float32)
+    _need_numel(triples_out, "triples_out", chunks * n_rows * 3, torch.float32)
     _check(lib().ds_greedy_lse(handle, _dev_ptr(logits, "logits"), n_rows,
                                _dev_ptr(token_out, "token_out", torch.int32),
                                _dev_ptr(lse_out, "lse_out", torch.float32),
@@ -255,6 +332,12 @@ def ds_greedy_lse(handle: int, logits, n_rows: int, token_out, lse_out, logprob_
 def ds_repetition_penalty(handle: int, logits, n_rows: int, seen_mask, penalty, stream=None) -> None:
     """seen_mask: int32 tensor holding the uint32 mask words bit for bit."""
     torch = _t()
+    V, code, _, _ = _info(handle)
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2 or logits.shape[0] < n_rows:
+        raise ValueError(f"logits must be a [n_rows, V] tensor with at least {n_rows} rows")
+    _need_logits(logits, "logits", (int(logits.shape[0]), V), code)
+    _need_numel(seen_mask, "seen_mask", n_rows * ((V + 31) // 32), torch.int32)
+    _need_numel(penalty, "penalty", n_rows, torch.float32)
     _check(lib().ds_repetition_penalty(handle, _dev_ptr(logits, "logits"), n_rows,
                                        _dev_ptr(seen_mask, "seen_mask", torch.int32),
                                        _dev_ptr(penalty, "penalty", torch.float32), _stream_ptr(stream, logits)))
@@ -265,7 +348,20 @@ def ds_sample_ar(handle: int, request_ids, logits, seen_mask, penalty, iteration
     """Per-request arrays are device tensors (int64, int32, float32); seen_mask
     and penalty may both be None (no penalty)."""
     torch = _t()
+    V, code, _, _ = _info(handle)
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a [num_requests, V] tensor")
     n = int(logits.shape[0])
+    _need_logits(logits, "logits", (n, V), code)
+    if (seen_mask is None) != (penalty is None):
+        raise ValueError("seen_mask and penalty are given together or not at all")
+    _need_numel(seen_mask, "seen_mask", n * ((V + 31) // 32), torch.int32)
+    _need_numel(penalty, "penalty", n, torch.float32)
+    _need_numel(request_ids, "request_ids", n, torch.int64)
+    _need_numel(iterations, "iterations", n, torch.int32)
+    _need_numel(temperature, "temperature", n, torch.float32)
+    _need_numel(tokens_out, "tokens_out", n, torch.int32)
+    _need_numel(logprobs_out, "logprobs_out", n, torch.float32)
     _check(lib().ds_sample_ar(handle, _dev_ptr(request_ids, "request_ids", torch.int64), _dev_ptr(logits, "logits"),
                               _dev_ptr(seen_mask, "seen_mask", torch.int32), _dev_ptr(penalty, "penalty", torch.float32),
                               _dev_ptr(iterations, "iterations", torch.int32),
@@ -278,15 +374,24 @@ def ds_reveal_topk(handle: int, scores, num_rows: int, seq_lens: Sequence[int],
                    reveal_counts: Sequence[int], index_out, score_out=None, stream=None,
                    stage: Optional[RequestStage] = None) -> None:
     torch = _t()
+    _info(handle)
     n = stage.fill_reveal(seq_lens, reveal_counts) if stage is not None else -1
     if n > 0:
         psl, prc = stage.reveal_ptrs
+        sl, rc = stage.sl[:n], stage.rc[:n]
     else:
         sl = _host(seq_lens, np.int32)
         rc = _host(reveal_counts, np.int32)
         if sl.size != rc.size:
             raise ValueError("seq_lens and reveal_counts must have num_requests entries")
         n, psl, prc = sl.size, sl.ctypes.data, rc.ctypes.data
+    P = int(sl.sum())
+    total = int(rc.sum())
+    _need_shape(scores, "scores", (num_rows, P))
+    if scores.dtype != torch.float32:
+        raise TypeError(f"scores must have dtype torch.float32 (got {scores.dtype})")
+    _need_numel(index_out, "index_out", total, torch.int32)
+    _need_numel(score_out, "score_out", total, torch.float32)
     _check(lib().ds_reveal_topk(handle, _dev_ptr(scores, "scores", torch.float32), num_rows, psl, prc, n,
                                 _dev_ptr(index_out, "index_out", torch.int32),
                                 _dev_ptr(score_out, "score_out", torch.float32), _stream_ptr(stream, scores)))
