@@ -1,18 +1,23 @@
 """Benchmark of the per-position full-vocabulary sampler on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload omnivoice] [--no-suite]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress] [--no-suite]
 
 One step is one ``ds_sample`` call over one synthetic batch already resident in
-HBM: CFG combine, temperature, exact top-ratio threshold, Gumbel-max and the
+HBM: CFG combine, temperature, top-ratio filter, Gumbel-max and the
 full-vocabulary logprob for every (row, position) cell.  The headline workload is
-the OmniVoice-shaped masked-diffusion step (8 requests x 8 codebook rows, ragged
-lengths 80-120, V=1025 bf16).  Input buffers rotate through copies totalling at
-least 1 GiB so that neither the L2 nor the 256 MB Infinity Cache serves a repeat.
+the largest single-GPU configuration: 2048 positions x V=248320 bf16 conditional
+and unconditional logits, guidance 1.5, temperature 1.0, top-ratio k=24832, the
+vocabulary reduced in 4 contiguous chunks whose (max, lse, argmax) triples are
+merged on the GPU.  Input buffers rotate through copies totalling at least 1 GiB
+so that neither the L2 nor the 256 MB Infinity Cache serves a repeat.
 
-Prints ONE JSON line: positions/s for the headline step, the roofline of its
-kernel (algorithmic bytes over the kernel's average duration, timed live with HIP
-events on the launch stream), the CPU oracle timed on a bounded sample, and the
-same figures for the other workloads under "per_config".
+Prints ONE JSON line: positions/s of the headline step; the roofline of its
+kernels (algorithmic bytes over the average duration of the call, timed live with
+HIP events on the launch stream), next to a measured read ceiling at the same
+bytes and launch shape; the CPU oracle on a bounded sample of the same workload
+(one thread and every thread of the host share); the oracle's parity and near-tie
+counts per configuration; and the same figures for the other workloads under
+"per_config".
 """
 
 from __future__ import annotations
@@ -121,12 +126,17 @@ def draft_kernel(w) -> str:
     return "k_greedy_parts+k_greedy_merge"
 
 
+_WORKLOADS = {}
+
+
 def make_workload(name: str):
+    """The named synthetic workload, generated once per process (the large ones
+    take seconds to draw)."""
     import synth
 
-    if name == "tiny":
-        return synth.tiny(0.9)
-    return synth.WORKLOADS[name]()
+    if name not in _WORKLOADS:
+        _WORKLOADS[name] = synth.tiny(0.9) if name == "tiny" else synth.WORKLOADS[name]()
+    return _WORKLOADS[name]
 
 
 class Runner:
@@ -330,7 +340,9 @@ def auto_steps(r: "Runner", budget_s: float = SUITE_BUDGET_S) -> tuple:
 
 
 def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "eager") -> dict:
-    """Times one workload; steps=None sizes the run with auto_steps."""
+    """Times one workload; steps=None sizes the run with auto_steps.  The result
+    keeps the outputs of the last call (identical on every buffer set) under
+    "outputs" for the parity check."""
     import torch
 
     kind = name if name in ("draft", "reveal", "ar") else "sample"
@@ -338,7 +350,19 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     r = Runner(w, kind, threshold, mode)
     if steps is None:
         steps, warmup = auto_steps(r)
-    ms_step, ms_kernel, med, p10, p90 = time_runner(r, steps, warmup)
+    ms_step, ms_call, med, p10, p90 = time_runner(r, steps, warmup)
+    outputs = None
+    if kind in ("sample", "draft") and mode == "eager":
+        outputs = [t.reshape(-1).cpu().numpy() for t in r.out if t is not None]
+    ceiling = None
+    if kind == "draft" and draft_kernel(w) == "k_greedy_rows":
+        # the same bytes at the same launch shape: one 1024-thread workgroup per row
+        ceiling = read_ceiling([(x,) for x in r.x], w.vocab * w.elem_bytes, 1024)
+    elif kind == "sample" and name == "stress" and mode == "eager" and not threshold:
+        # the parts kernel's shape: one 512-thread workgroup per part of a chunk,
+        # over c and over u
+        L = -(-w.vocab // w.vocab_chunks)
+        ceiling = read_ceiling(list(zip(r.c, r.u)), L * w.elem_bytes, 512)
     r.close()
     del r
     torch.cuda.empty_cache()
@@ -346,11 +370,11 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     # positions: cells sampled, draft rows reduced, or cells ranked by the reveal
     cells = {"draft": lambda: w.n_rows, "reveal": lambda: w.rows * w.positions,
              "ar": lambda: w.rows}.get(kind, lambda: w.cells)()
-    # one step is one launch of the wave-per-cell kernel (every sampling workload
-    # here has <= 64 requests, one request table), so its back-to-back time per
-    # step is that kernel's average duration on its stream; or one parts + merge
-    # pair; or, for the autoregressive step, the penalty kernel and one sampler
-    # launch over all its requests (launches_per_step)
+    # one step is one call: one launch of the wave-per-cell kernel (every
+    # sampling workload here has <= 64 requests, one request table), one parts +
+    # merge pair, one draft kernel, or the autoregressive step's penalty kernel
+    # and sampler launches (launches_per_step); its back-to-back time per step is
+    # the call's average duration on its stream
     achieved = alg / (ms_step * 1e-3) / 1e9
     cfg = describe(w, kind)
     if threshold:
@@ -364,44 +388,160 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     elif mode == "compact_u":
         cfg["workload"] += "+compact_u"
         cfg["u_layout"] = "compacted: guided requests' positions only"
-    return {"config": cfg, "kernel": kname, "launches_per_step": launches_per_step(w, kind),
-            "steps": steps, "warmup": warmup, "positions_per_s": cells / (ms_step * 1e-3),
-            "ms_per_step": ms_step, "kernel_ms_mean": ms_step, "bracketed_ms_mean": ms_kernel,
-            "bracketed_ms_median": med, "bracketed_ms_p10": p10, "bracketed_ms_p90": p90, "algorithmic_bytes": alg,
-            "achieved_GBs": achieved, "frac_of_peak": achieved / HBM_PEAK_GBS, "workload_obj": w}
+    res = {"config": cfg, "kernel": kname, "launches_per_step": launches_per_step(w, kind),
+           "steps": steps, "warmup": warmup, "positions_per_s": cells / (ms_step * 1e-3),
+           "ms_per_step": ms_step, "call_ms_mean": ms_step, "bracketed_ms_mean": ms_call,
+           "bracketed_ms_median": med, "bracketed_ms_p10": p10, "bracketed_ms_p90": p90, "algorithmic_bytes": alg,
+           "achieved_GBs": achieved, "frac_of_peak": achieved / HBM_PEAK_GBS, "workload_obj": w,
+           "outputs": outputs}
+    if ceiling:
+        res["read_ceiling"] = ceiling
+        res["frac_of_read_ceiling"] = achieved / ceiling["GBs"]
+    return res
 
 
-def cpu_baseline(w, budget_s: float = 12.0) -> dict:
-    """The oracle as it stands (single-threaded C) on a bounded sample of cells:
-    enough of the batch, or whole passes over it, for about `budget_s` of work."""
+def read_ceiling(sets, row_bytes: int, threads: int, budget_s: float = 0.05) -> dict:
+    """The HBM read rate of ds_read_probe over the given sets of device tensors
+    (one set per step, in rotation; each tensor read as rows of row_bytes, one
+    workgroup of `threads` per row): the ceiling for a kernel that reads the same
+    bytes at that launch shape."""
+    import torch
+
+    import vocab_wise_logit_amd as ds
+
+    sinks = [[torch.empty(b.numel() * b.element_size() // row_bytes, dtype=torch.int32, device="cuda")
+              for b in st] for st in sets]
+    nbytes = sum(b.numel() * b.element_size() for b in sets[0])
+
+    def one(i):
+        k = i % len(sets)
+        for b, sk in zip(sets[k], sinks[k]):
+            ds.ds_read_probe(b, row_bytes, threads, sk)
+
+    for i in range(3):
+        one(i)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    one(3)
+    torch.cuda.synchronize()
+    n = int(min(max(budget_s / max(time.perf_counter() - t, 1e-6), 10), 2000))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        one(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    rows = nbytes // row_bytes
+    return {"GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "ms": round(ms, 6), "steps": n,
+            "shape": f"{rows} workgroups x {threads} threads, {row_bytes} B each",
+            "kernel": "k_read_rows (ds_read_probe)"}
+
+
+# ----------------------------------------------------------- the CPU oracle
+
+def host_threads() -> int:
+    """Worker threads for the oracle: the host CPUs this process may use, capped
+    at 16 (the share of one GPU on a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(n, env or n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_cells(w, cells: np.ndarray, threads: int):
+    """The oracle over the given cells, split across threads (its C entry points
+    release the GIL); returns (SampleResult fields concatenated, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
-    cells_all = np.arange(w.cells, dtype=np.int64)
-    # estimate cost on a small slice, then size the sample to the time budget
-    probe = cells_all[: min(256, w.cells)]
+    parts = [p for p in np.array_split(cells, threads) if p.size]
+    t = time.perf_counter()
+    if len(parts) == 1:
+        res = [oracle.sample_workload(w, cells=parts[0])]
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            res = list(ex.map(lambda p: oracle.sample_workload(w, cells=p), parts))
+    dt = time.perf_counter() - t
+    cat = {k: np.concatenate([getattr(r, k) for r in res]) for k in ("cells", "tokens", "logprobs", "near_tie")}
+    return cat, dt
+
+
+def parity_report(w, outputs, ref: dict) -> dict:
+    """GPU tokens and logprobs against the oracle on the cells it computed: greedy
+    cells and cells away from oracle near ties must draw the same token."""
+    import synth  # noqa: F401
+
+    cells = ref["cells"]
+    tok = outputs[0][cells]
+    lp = outputs[1][cells]
+    offs = np.concatenate([[0], np.cumsum(w.seq_lens)])
+    r = np.searchsorted(offs, cells % max(1, w.positions), side="right") - 1
+    greedy = w.temperature[r] == 0
+    near = ref["near_tie"].astype(bool) & ~greedy
+    same = tok == ref["tokens"]
+    err = np.abs(lp[same].astype(np.float64) - ref["logprobs"][same].astype(np.float64))
+    return {"cells_checked": int(cells.size), "sampled": int((~greedy).sum()), "near_ties": int(near.sum()),
+            "token_mismatch": int((~same & ~near).sum()), "near_tie_other_token": int((~same & near).sum()),
+            "max_logprob_err": float(err.max()) if err.size else 0.0}
+
+
+def cpu_baseline(w, outputs, single_s: float = 6.0, multi_s: float = 10.0) -> tuple:
+    """The oracle as it stands (plain C, double precision) on a bounded sample of
+    the workload's cells, evenly spread over the batch: about `single_s` seconds
+    on one thread, then about `multi_s` seconds on every thread of the host
+    share.  Returns (cpu_baseline entry, parity of the GPU outputs on the cells
+    the multi-threaded run computed)."""
+    import oracle
+
+    threads = host_threads()
+    probe = np.linspace(0, w.cells - 1, min(4, w.cells)).astype(np.int64)
     t = time.perf_counter()
     oracle.sample_workload(w, cells=probe)
     per_cell = (time.perf_counter() - t) / probe.size
-    want = int(max(probe.size, budget_s / max(per_cell, 1e-9)))
-    n = min(w.cells, want)
-    passes = max(1, want // w.cells) if n == w.cells else 1
-    sample = cells_all[:n]
-    t = time.perf_counter()
-    for _ in range(passes):
-        oracle.sample_workload(w, cells=sample)
-    dt = time.perf_counter() - t
-    what = (f"{passes} passes over the whole {w.cells}-cell batch" if n == w.cells
-            else f"first {n} of {w.cells} cells of the same workload")
-    return {"value": passes * n / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}, {dt:.2f} s, single-threaded C oracle"}
+    n1 = int(min(w.cells, max(probe.size, single_s / max(per_cell, 1e-9))))
+    one, dt1 = oracle_cells(w, np.linspace(0, w.cells - 1, n1).astype(np.int64), 1)
+    nm = int(min(w.cells, max(threads, multi_s * threads / max(per_cell, 1e-9))))
+    cells_m = np.unique(np.linspace(0, w.cells - 1, nm).astype(np.int64))
+    many, dtm = oracle_cells(w, cells_m, threads)
+    entry = {"value": cells_m.size / dtm, "unit": "positions/s", "cores": threads, "kind": "oracle",
+             "sample": (f"{cells_m.size} of the {w.cells} cells, evenly spaced over the batch, on {threads} threads "
+                        f"in {dtm:.2f} s; single-threaded: {n1} cells in {dt1:.2f} s"),
+             "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+             "single_thread": {"value": n1 / dt1, "unit": "positions/s", "cores": 1, "cells": n1,
+                               "seconds": round(dt1, 3)}}
+    return entry, parity_report(w, outputs, many) if outputs is not None else None
+
+
+def draft_parity(w, outputs) -> dict:
+    import oracle
+
+    g = oracle.greedy_lse(w.logits, vocab_chunks=w.vocab_chunks, want_triples=False)
+    tok, lse = outputs[0], outputs[1]
+    return {"rows_checked": int(g.token.size), "token_mismatch": int((tok != g.token).sum()),
+            "max_lse_err": float(np.max(np.abs(lse.astype(np.float64) - g.lse)))}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="omnivoice")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="stress")
     ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -409,8 +549,8 @@ def main() -> int:
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this sampler has no multi-GPU path; "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this build runs on a single GPU and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
@@ -429,16 +569,23 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "copies": 10}))
         return 0
 
+    print(f"[bench] headline {args.workload}: {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
+          flush=True)
     head = bench_one(args.workload, args.steps, args.warmup)
     w = head.pop("workload_obj")
+    head_out = head.pop("outputs")
     traffic = stored_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(head["achieved_GBs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(head["frac_of_peak"], 4),
                 "traffic": traffic,
                 "kernel": head["kernel"],
                 "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
-                "kernel_ms_mean": head["kernel_ms_mean"], "bracketed_ms_mean": head["bracketed_ms_mean"]}
-    per_config = {}
+                "call_ms_mean": head["call_ms_mean"], "bracketed_ms_mean": head["bracketed_ms_mean"]}
+    if "read_ceiling" in head:
+        roofline["read_ceiling_GBs"] = head["read_ceiling"]["GBs"]
+        roofline["frac_of_read_ceiling"] = round(head["frac_of_read_ceiling"], 4)
+    per_config, parity = {}, {}
+    threads = host_threads()
     if not args.no_suite:
         # every workload, then the two sampled shapes again with the threshold
         # output requested (it needs the exact k-th largest h of every row)
@@ -451,15 +598,29 @@ def main() -> int:
         runs += [("mixed", False, "compact_u")]
         for name, thr, mode in runs:
             if name == args.workload and not thr and mode == "eager":
-                res = head
+                res = dict(head, outputs=head_out)
             else:
+                print(f"[bench] {name} threshold={thr} mode={mode}", file=sys.stderr, flush=True)
                 res = bench_one(name, None, None, threshold=thr, mode=mode)
                 res.pop("workload_obj", None)
+            outs = res.pop("outputs", None)
+            if outs is not None and not thr and mode == "eager" and name != args.workload:
+                if name == "draft":
+                    parity[res["config"]["workload"]] = draft_parity(make_workload(name), outs)
+                elif name in ("tiny", "omnivoice", "mixed"):
+                    wn = make_workload(name)
+                    ref, _ = oracle_cells(wn, np.arange(wn.cells, dtype=np.int64), threads)
+                    parity[res["config"]["workload"]] = parity_report(wn, outs, ref)
             entry = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items() if k != "config"}
             if not thr and mode == "eager":
                 entry["traffic"] = stored_traffic(name)
             per_config[res["config"]["workload"]] = entry
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu, head_parity = cpu_baseline(w, head_out)
+        if head_parity is not None:
+            parity[head["config"]["workload"]] = head_parity
     line = {
         "metric": METRIC,
         "value": head["positions_per_s"],
@@ -471,11 +632,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # every step computes in binary32 (bf16 inputs widen exactly)
         "dtype": "f32",
         "data": "synthetic",
         "config": head["config"],
         "roofline": roofline,
+        "read_ceiling": head.get("read_ceiling"),
         "cpu_baseline": cpu,
+        "parity": parity,
         "per_config": per_config,
     }
     print(json.dumps(line))

@@ -301,6 +301,26 @@ int ds_sample_ar(ds_sampler *s, const int64_t *request_ids, void *logits, const 
                  int32_t num_requests, uint64_t seed, int32_t *tokens_out, float *logprobs_out,
                  void *stream);
 
+/*
+ * ds_read_probe -- measurement aid, not part of the sampling path: the HBM read
+ * ceiling at a launch shape.  n_rows workgroups of `threads` threads each read
+ * one row of row_bytes once, with the 16-byte nontemporal loads of the streaming
+ * sampler kernels, and write the xor of the row's words to sink[row] (so that no
+ * load can be dropped).  Timing this call next to a sampler call of the same
+ * bytes and shape shows how close the sampler comes to what the memory system
+ * delivers on the running device.  No handle is needed.
+ *
+ *   x          device, 16-byte aligned, n_rows * row_bytes bytes.
+ *   n_rows     1 .. 2^31 - 1 (one workgroup each).
+ *   row_bytes  a positive multiple of 16.
+ *   threads    256, 512 or 1024 threads per workgroup.
+ *   sink       device uint32 [n_rows], 4-byte aligned.
+ *   stream     hipStream_t.
+ * Returns DS_OK, DS_ERR_INVALID_ARG or DS_ERR_HIP.
+ */
+int ds_read_probe(const void *x, int64_t n_rows, int64_t row_bytes, int32_t threads, uint32_t *sink,
+                  void *stream);
+
 /* Release a handle and its device scratch.  NULL is a no-op.  The caller must
  * make sure no call on the handle is still pending on a stream. */
 void ds_sample_destroy(ds_sampler *s);

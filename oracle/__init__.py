@@ -74,6 +74,10 @@ def _setup(lib):
                                    P, P]
     lib.dso_f32_to_bf16.restype = C.c_uint16
     lib.dso_f32_to_bf16.argtypes = [C.c_float]
+    lib.dso_philox_range.argtypes = [P, P, C.c_int64, P]
+    lib.dso_noise_words.argtypes = [C.c_uint64, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                    C.c_int64, P]
+    lib.dso_gumbel_array.argtypes = [P, C.c_int64, P]
     lib.dso_penalized.restype = C.c_float
     lib.dso_penalized.argtypes = [C.c_float, C.c_float]
     lib.dso_repetition_penalty.restype = C.c_int
@@ -142,6 +146,35 @@ def philox4x32_10(ctr, key, lib=None) -> np.ndarray:
     k = np.asarray(key, dtype=np.uint32).copy()
     out = np.empty(4, dtype=np.uint32)
     lib.dso_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox_range(ctr, key, n: int, lib=None) -> np.ndarray:
+    """[n, 4] Philox4x32-10 words of the counters (ctr[0] + i, ctr[1], ctr[2],
+    ctr[3]), i = 0 .. n - 1 (the first word wrapping modulo 2^32)."""
+    lib = lib or _load()
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.empty((n, 4), dtype=np.uint32)
+    lib.dso_philox_range(_ptr(c), _ptr(k), n, _ptr(out))
+    return out
+
+
+def noise_words(seed: int, request_id: int, iteration: int, row: int, t: int, v0: int, n: int,
+                lib=None) -> np.ndarray:
+    """Noise words of ids v0 .. v0 + n - 1 of one cell."""
+    lib = lib or _load()
+    out = np.empty(n, dtype=np.uint32)
+    lib.dso_noise_words(seed, request_id, iteration, row, t, v0, n, _ptr(out))
+    return out
+
+
+def gumbel_array(x: np.ndarray, lib=None) -> np.ndarray:
+    """Gumbel values (double) of an array of noise words."""
+    lib = lib or _load()
+    xs = np.ascontiguousarray(x, dtype=np.uint32)
+    out = np.empty(xs.shape, dtype=np.float64)
+    lib.dso_gumbel_array(_ptr(xs), xs.size, _ptr(out))
     return out
 
 

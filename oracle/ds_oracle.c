@@ -591,3 +591,27 @@ int dso_reveal_topk(const float *scores, int32_t C, int64_t P, const int32_t *se
     }
     return 0;
 }
+
+/* ------------------------------------------- array forms (test helpers) */
+
+/* Loops over the functions above, for checks that need millions of values:
+ * Philox blocks of the counters (ctr[0] + i, ctr[1], ctr[2], ctr[3]),
+ * i = 0 .. n - 1 (the first word wraps modulo 2^32), four words each. */
+void dso_philox_range(const uint32_t ctr[4], const uint32_t key[2], int64_t n, uint32_t *out) {
+    for (int64_t i = 0; i < n; i++) {
+        uint32_t c[4] = {ctr[0] + (uint32_t)i, ctr[1], ctr[2], ctr[3]};
+        dso_philox4x32_10(c, key, out + 4 * i);
+    }
+}
+
+/* Noise words of ids v0 .. v0 + n - 1 of one cell. */
+void dso_noise_words(uint64_t seed, int64_t request_id, int32_t iteration, int32_t row, int32_t t,
+                     int32_t v0, int64_t n, uint32_t *out) {
+    for (int64_t i = 0; i < n; i++)
+        out[i] = dso_noise_word(seed, request_id, iteration, row, t, v0 + (int32_t)i);
+}
+
+/* Gumbel values of n noise words. */
+void dso_gumbel_array(const uint32_t *x, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = dso_gumbel(x[i]);
+}

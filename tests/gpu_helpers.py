@@ -17,6 +17,7 @@ Bar (fixed before any kernel was written):
 
 from __future__ import annotations
 
+import os
 import sys
 from dataclasses import dataclass
 
@@ -67,6 +68,20 @@ def run_sample(w, *, threshold: bool = True, force_fallback: bool = False, vocab
                          seed=w.seed, threshold=threshold)
         torch.cuda.synchronize()
     return [t.reshape(-1).cpu().numpy() for t in out]
+
+
+def oracle_threaded(w, cells: np.ndarray, threads: int = 0) -> "oracle.SampleResult":
+    """oracle.sample_workload over the given cells, split across threads (the
+    oracle's C entry point releases the GIL); the result is in the cells' order."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cells = np.ascontiguousarray(cells, dtype=np.int64)
+    threads = threads or min(16, os.cpu_count() or 1)
+    parts = [p for p in np.array_split(cells, threads) if p.size]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        res = list(ex.map(lambda p: oracle.sample_workload(w, cells=p), parts))
+    fields = {k: np.concatenate([getattr(r, k) for r in res]) for k in oracle.SampleResult.__dataclass_fields__}
+    return oracle.SampleResult(**fields)
 
 
 def cell_temperature(w, cells: np.ndarray) -> np.ndarray:

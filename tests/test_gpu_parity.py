@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import (check_greedy, check_reveal, check_sample, log, run_greedy, run_reveal, run_sample,
-                         to_dev)
+from gpu_helpers import (check_greedy, check_reveal, check_sample, log, oracle_threaded, run_greedy, run_reveal,
+                         run_sample, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,18 +87,26 @@ def test_stress_small_positions_dense_chunked_and_fallback():
 def test_stress_full_size_sampled_cells_and_chunk_equality():
     import torch
 
+    # the full 2048 x 248320 chunked stress step, in the production launch (4
+    # chunks) with and without the threshold output, and dense
     w = synth.stress()
     c = to_dev(w.c)
     u = to_dev(w.u)
+    got4t = run_sample(w, c_dev=c, u_dev=u, threshold=True)
     got4 = run_sample(w, c_dev=c, u_dev=u, threshold=False)
     got1 = run_sample(w, c_dev=c, u_dev=u, threshold=False, vocab_chunks=1)
     del c, u
     torch.cuda.empty_cache()
-    # the four-chunk result equals the dense single-pass result in every cell
+    # the four-chunk result equals the dense single-pass result in every cell, and
+    # asking for the threshold changes no draw
     assert np.array_equal(got4[0], got1[0])
     assert np.max(np.abs(got4[1] - got1[1])) <= 1e-5
-    cells = np.linspace(0, w.cells - 1, 40).astype(np.int64)
-    ref = oracle.sample_workload(w, cells=cells)
+    assert np.array_equal(got4t[0], got4[0]) and np.array_equal(got4t[1], got4[1])
+    # 256 evenly spaced cells against the oracle: tokens, logprobs and the
+    # top-ratio threshold (k = ceil(0.1 * V) = 24832) bit for bit
+    cells = np.linspace(0, w.cells - 1, 256).astype(np.int64)
+    ref = oracle_threaded(w, cells)
+    check_sample(w, got4t, ref, check_threshold=True)
     check_sample(w, got4, ref, check_threshold=False)
 
 

@@ -263,6 +263,24 @@ def test_noise_word_depends_on_every_key_field():
     assert words == [int(x) for x in full]
 
 
+def test_array_forms_equal_the_scalar_functions():
+    # the array helpers used by the GPU pins are loops over the pinned scalars
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        ctr = rng.integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+        ctr[0] = np.uint32(0xFFFFFFF0) if _ % 5 == 0 else ctr[0]  # wraps inside the range
+        key = rng.integers(0, 2**32, 2, dtype=np.uint64).astype(np.uint32)
+        blk = oracle.philox_range(ctr, key, 40)
+        for i in (0, 7, 15, 16, 39):
+            c = ctr.copy()
+            c[0] = np.uint32((int(ctr[0]) + i) & 0xFFFFFFFF)
+            assert blk[i].tolist() == oracle.philox4x32_10(c, key).tolist()
+    words = oracle.noise_words(42, 1000, 3, 5, 17, 1230, 9)
+    assert words.tolist() == [oracle.noise_word(42, 1000, 3, 5, 17, v) for v in range(1230, 1239)]
+    xs = rng.integers(0, 2**32, 50, dtype=np.uint64).astype(np.uint32)
+    assert oracle.gumbel_array(xs).tolist() == [oracle.gumbel(int(x)) for x in xs]
+
+
 # ---------------------------------------------------------- uniform / Gumbel
 
 def test_uniform_lattice_and_gumbel_quantile():

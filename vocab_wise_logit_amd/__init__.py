@@ -36,6 +36,7 @@ from ._binding import (  # noqa: F401
     ds_sample,
     ds_sample_create,
     ds_sample_destroy,
+    ds_read_probe,
     ds_sample_device_params,
     ds_version,
     lib,

@@ -24,7 +24,8 @@ DS_OK, DS_ERR_INVALID_ARG, DS_ERR_UNSUPPORTED, DS_ERR_CAPACITY, DS_ERR_NO_MEMORY
 DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK, DS_FLAG_COMPACT_U = 0, 1, 2
 
 EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_greedy_lse", "ds_reveal_topk",
-            "ds_repetition_penalty", "ds_sample_ar", "ds_sample_destroy", "ds_last_error", "ds_version")
+            "ds_repetition_penalty", "ds_sample_ar", "ds_sample_destroy", "ds_last_error", "ds_version",
+            "ds_read_probe")
 
 _lib = None
 
@@ -76,6 +77,8 @@ def lib():
         L.ds_last_error.argtypes = []
         L.ds_version.restype = C.c_int
         L.ds_version.argtypes = []
+        L.ds_read_probe.restype = C.c_int
+        L.ds_read_probe.argtypes = [P, I64, I64, I32, P, P]
         _lib = L
     return _lib
 
@@ -395,3 +398,19 @@ def ds_reveal_topk(handle: int, scores, num_rows: int, seq_lens: Sequence[int],
     _check(lib().ds_reveal_topk(handle, _dev_ptr(scores, "scores", torch.float32), num_rows, psl, prc, n,
                                 _dev_ptr(index_out, "index_out", torch.int32),
                                 _dev_ptr(score_out, "score_out", torch.float32), _stream_ptr(stream, scores)))
+
+
+def ds_read_probe(x, row_bytes: int, threads: int, sink, stream=None) -> None:
+    """Measurement aid: read the bytes of device tensor x once as rows of
+    row_bytes, one workgroup of `threads` threads per row; sink (int32, one entry
+    per row) receives the xor of each row's words."""
+    torch = _t()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch tensor on a HIP device")
+    nbytes = x.numel() * x.element_size()
+    if row_bytes <= 0 or nbytes % row_bytes:
+        raise ValueError(f"x holds {nbytes} bytes, not a whole number of {row_bytes}-byte rows")
+    n_rows = nbytes // row_bytes
+    _need_numel(sink, "sink", n_rows, torch.int32)
+    _check(lib().ds_read_probe(_dev_ptr(x, "x"), n_rows, row_bytes, threads, _dev_ptr(sink, "sink"),
+                               _stream_ptr(stream, x)))

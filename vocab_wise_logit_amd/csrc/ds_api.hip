@@ -588,4 +588,18 @@ int ds_reveal_topk(ds_sampler* s, const float* scores, int32_t num_rows, const i
     return DS_OK;
 }
 
+int ds_read_probe(const void* x, int64_t n_rows, int64_t row_bytes, int32_t threads, uint32_t* sink, void* stream) {
+    g_err.clear();
+    if (!x || !sink) return fail(DS_ERR_INVALID_ARG, "x and sink must be non-NULL");
+    if (!aligned(x, 16) || !aligned(sink, 4)) return fail(DS_ERR_INVALID_ARG, "x must be 16-byte and sink 4-byte aligned");
+    if (n_rows < 1 || n_rows > INT32_MAX) return fail(DS_ERR_INVALID_ARG, "n_rows must be in [1, 2^31 - 1]");
+    if (row_bytes < 16 || row_bytes % 16 != 0)
+        return fail(DS_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16");
+    if (threads != 256 && threads != 512 && threads != 1024)
+        return fail(DS_ERR_INVALID_ARG, "threads must be 256, 512 or 1024");
+    const hipError_t e = ds::launch_read_probe(x, n_rows, row_bytes / 16, threads, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return DS_OK;
+}
+
 }  // extern "C"

@@ -128,4 +128,9 @@ struct RevealArgs {
 
 hipError_t launch_reveal_topk(const RevealArgs& a, const RevealTable& rt, hipStream_t st);
 
+// Measurement aid: n_rows workgroups of `threads` (256, 512 or 1024) threads,
+// each reading one row of row_pieces 16-byte pieces once.
+hipError_t launch_read_probe(const void* x, int64_t n_rows, int64_t row_pieces, int threads, uint32_t* sink,
+                             hipStream_t st);
+
 }  // namespace ds
