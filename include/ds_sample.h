@@ -302,6 +302,35 @@ int ds_sample_ar(ds_sampler *s, const int64_t *request_ids, void *logits, const 
                  void *stream);
 
 /*
+ * ds_sample_static -- ds_sample without a handle, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, and harnesses that forbid hipMalloc.  It allocates nothing: the
+ * streaming kernels' per-(row, part) records live in a fixed 512 KB array of the
+ * library's own device memory (one copy per device, present from load to process
+ * exit), and the handle's settings come as arguments.
+ *
+ * Same computation, checks and outputs as ds_sample on a handle created with the
+ * same vocab, dtype, top_k, vocab_chunks and flags (see ds_sample_create), cell
+ * for cell, on the calling thread's current HIP device.  The handle's capacity
+ * limits are replaced by one: num_rows * sum(seq_lens) must stay below 2^31.
+ * Every vocabulary size runs: rows that need more records than the array holds
+ * are processed in several launches on `stream`, as ds_sample does with its
+ * workspace.
+ *
+ * The array is shared by every call on a device and keeps the last call's
+ * records: calls that may run at the same time on one device (different streams
+ * without ordering between them) race and give wrong results; order them on one
+ * stream.  The first call on each device looks up the array's address there
+ * (hipGetSymbolAddress, no allocation).  Returns what ds_sample returns, and
+ * DS_ERR_UNSUPPORTED on a device ordinal of 64 or more.
+ */
+int ds_sample_static(int32_t vocab, int32_t dtype, int32_t top_k, int32_t vocab_chunks, uint32_t flags,
+                     const int64_t *request_ids, const void *c_logits, const void *u_logits,
+                     const int32_t *seq_lens, const int32_t *iterations, const float *guidance_scale,
+                     const float *temperature, int32_t num_requests, int32_t num_rows, uint64_t seed,
+                     int32_t *tokens_out, float *logprobs_out, float *threshold_out, void *stream);
+
+/*
  * ds_read_probe -- measurement aid, not part of the sampling path: the HBM read
  * ceiling at a launch shape.  n_rows workgroups of `threads` threads each read
  * one row of row_bytes once, with the 16-byte nontemporal loads of the streaming

@@ -38,6 +38,7 @@ from ._binding import (  # noqa: F401
     ds_sample_destroy,
     ds_read_probe,
     ds_sample_device_params,
+    ds_sample_static,
     ds_version,
     lib,
 )

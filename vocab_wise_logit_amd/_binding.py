@@ -25,7 +25,7 @@ DS_FLAG_NONE, DS_FLAG_FORCE_FALLBACK, DS_FLAG_COMPACT_U = 0, 1, 2
 
 EXPORTED = ("ds_sample_create", "ds_sample", "ds_sample_device_params", "ds_greedy_lse", "ds_reveal_topk",
             "ds_repetition_penalty", "ds_sample_ar", "ds_sample_destroy", "ds_last_error", "ds_version",
-            "ds_read_probe")
+            "ds_read_probe", "ds_sample_static")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def lib():
         L.ds_last_error.argtypes = []
         L.ds_version.restype = C.c_int
         L.ds_version.argtypes = []
+        L.ds_sample_static.restype = C.c_int
+        L.ds_sample_static.argtypes = [I32, I32, I32, I32, U32, P, P, P, P, P, P, P, I32, I32, U64, P, P, P, P]
         L.ds_read_probe.restype = C.c_int
         L.ds_read_probe.argtypes = [P, I64, I64, I32, P, P]
         _lib = L
@@ -277,6 +279,37 @@ def ds_sample(handle: int, request_ids: Sequence[int], c_logits, u_logits, seq_l
                            _dev_ptr(logprobs_out, "logprobs_out", torch.float32),
                            _dev_ptr(threshold_out, "threshold_out", torch.float32),
                            _stream_ptr(stream, c_logits)))
+
+
+def ds_sample_static(vocab: int, dtype: int, top_k: int, vocab_chunks: int, flags: int, request_ids, c_logits,
+                     u_logits, seq_lens, iterations, guidance_scale, temperature, num_rows: int, seed: int,
+                     tokens_out, logprobs_out, threshold_out=None, stream=None) -> None:
+    """ds_sample without a handle: the settings a handle would hold are arguments,
+    and the library's static scratch replaces the handle's workspace, so the call
+    allocates no device memory (the caller passes every output).  Host
+    per-request sequences; device tensors as for ds_sample."""
+    torch = _t()
+    rid = _host(request_ids, np.int64)
+    sl = _host(seq_lens, np.int32)
+    it = _host(iterations, np.int32)
+    gs = _host(guidance_scale, np.float32)
+    tp = _host(temperature, np.float32)
+    n = rid.size
+    if not (sl.size == it.size == gs.size == tp.size == n):
+        raise ValueError("per-request arrays must all have num_requests entries")
+    P = int(sl.sum())
+    _need_logits(c_logits, "c_logits", (num_rows, P, vocab), dtype)
+    if u_logits is not None:
+        Pu = int(sl[gs != 0].sum()) if flags & DS_FLAG_COMPACT_U else P
+        _need_logits(u_logits, "u_logits", (num_rows, Pu, vocab), dtype)
+    _need_numel(tokens_out, "tokens_out", num_rows * P, torch.int32)
+    _need_numel(logprobs_out, "logprobs_out", num_rows * P, torch.float32)
+    _need_numel(threshold_out, "threshold_out", num_rows * P, torch.float32)
+    ptrs = (_dev_ptr(c_logits, "c_logits"), _dev_ptr(u_logits, "u_logits"), _dev_ptr(tokens_out, "tokens_out"),
+            _dev_ptr(logprobs_out, "logprobs_out"), _dev_ptr(threshold_out, "threshold_out"))
+    _check(lib().ds_sample_static(vocab, dtype, top_k, vocab_chunks, flags, rid.ctypes.data, ptrs[0], ptrs[1],
+                                  sl.ctypes.data, it.ctypes.data, gs.ctypes.data, tp.ctypes.data, n, num_rows,
+                                  seed & (2**64 - 1), ptrs[2], ptrs[3], ptrs[4], _stream_ptr(stream, c_logits)))
 
 
 def ds_sample_device_params(handle: int, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,

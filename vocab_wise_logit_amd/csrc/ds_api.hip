@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -35,6 +36,12 @@ struct ds_sampler {
     float z0;
     int32_t cus;  // compute units of the device
 };
+
+// Workspace of ds_sample_static: the streaming kernels' per-(row, part) records,
+// one copy per device for the life of the process (512 KB).  Host code never
+// passes this name to a kernel: it is a host-side stand-in, and the device
+// address of each device's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) ds::PartRec scratch[ds::kWorkParts];
 
 namespace {
 
@@ -72,9 +79,9 @@ double normal_quantile(double p) {
 struct DeviceGuard {
     int prev = -1;
     hipError_t err = hipSuccess;
-    explicit DeviceGuard(int dev) {
+    explicit DeviceGuard(int dev) {  // dev < 0: stay on the current device
         err = hipGetDevice(&prev);
-        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+        if (err == hipSuccess && dev >= 0 && prev != dev) err = hipSetDevice(dev);
     }
     ~DeviceGuard() {
         int cur = -1;
@@ -92,6 +99,44 @@ bool small_fits(const ds_sampler* s) {
 }
 
 bool use_small_kernel(const ds_sampler* s) { return !(s->flags & DS_FLAG_FORCE_FALLBACK) && small_fits(s); }
+
+// What a sampling call needs from its sampler: a handle's settings and limits,
+// or the arguments of the handle-free entry point.
+struct SamplerCfg {
+    int32_t vocab, dtype, top_k, vocab_chunks;
+    uint32_t flags;
+    float z0;
+    int32_t max_rows, max_requests;
+    int64_t max_positions;
+    int device;  // -1: the calling thread's current device
+};
+
+SamplerCfg cfg_of(const ds_sampler* s) {
+    return SamplerCfg{s->vocab, s->dtype, s->top_k, s->vocab_chunks, s->flags, s->z0,
+                      s->max_rows, s->max_requests, s->max_positions, s->device};
+}
+
+// First pivot of the wave-per-cell kernel's exact threshold search: the normal
+// quantile whose upper tail holds a little more than top_k of V ids.
+float pivot_quantile(int32_t top_k, int32_t vocab) {
+    double q0 = 1.25 * (double)top_k / vocab + 2.0 / std::sqrt((double)vocab);
+    if (q0 > 0.5) q0 = 0.5;
+    return (float)normal_quantile(1.0 - q0);
+}
+
+// Argument checks shared by ds_sample_create and ds_sample_static.
+int check_sampler_settings(int32_t vocab, int32_t dtype, int32_t top_k, int32_t vocab_chunks, uint32_t flags) {
+    if (vocab < 1) return fail(DS_ERR_INVALID_ARG, "vocab must be >= 1 (got %d)", vocab);
+    if (dtype != DS_DTYPE_F32 && dtype != DS_DTYPE_BF16)
+        return fail(DS_ERR_INVALID_ARG, "dtype must be DS_DTYPE_F32 or DS_DTYPE_BF16 (got %d)", dtype);
+    if (top_k < 0 || top_k > vocab) return fail(DS_ERR_INVALID_ARG, "top_k must be in [0, vocab]");
+    const int32_t max_chunks = vocab < 1024 ? vocab : 1024;
+    if (vocab_chunks < 1 || vocab_chunks > max_chunks)
+        return fail(DS_ERR_INVALID_ARG, "vocab_chunks must be in [1, %d]", max_chunks);
+    if (flags & ~(uint32_t)(DS_FLAG_FORCE_FALLBACK | DS_FLAG_COMPACT_U))
+        return fail(DS_ERR_INVALID_ARG, "unknown flags");
+    return DS_OK;
+}
 
 // Limits of ds_sample_device_params: one wave reads every request's length,
 // and 64 clamped lengths must sum below 2^31.
@@ -147,12 +192,10 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
     if (max_requests < 1) return fail(DS_ERR_INVALID_ARG, "max_requests must be >= 1");
     if ((int64_t)max_rows * max_positions > (int64_t)INT32_MAX)
         return fail(DS_ERR_INVALID_ARG, "max_rows * max_positions exceeds 2^31 - 1 cells");
-    if (top_k < 0 || top_k > vocab) return fail(DS_ERR_INVALID_ARG, "top_k must be in [0, vocab]");
-    const int32_t max_chunks = vocab < 1024 ? vocab : 1024;
-    if (vocab_chunks < 1 || vocab_chunks > max_chunks)
-        return fail(DS_ERR_INVALID_ARG, "vocab_chunks must be in [1, %d]", max_chunks);
-    if (flags & ~(uint32_t)(DS_FLAG_FORCE_FALLBACK | DS_FLAG_COMPACT_U))
-        return fail(DS_ERR_INVALID_ARG, "unknown flags");
+    {
+        const int rc = check_sampler_settings(vocab, dtype, top_k, vocab_chunks, flags);
+        if (rc != DS_OK) return rc;
+    }
     int ndev = 0;
     hipError_t e = hipGetDeviceCount(&ndev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
@@ -172,10 +215,7 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
     s->top_k = top_k ? top_k : (vocab + 9) / 10;
     s->vocab_chunks = vocab_chunks;
     s->flags = flags;
-    // first pivot of the threshold search aims at a count a little above top_k
-    double q0 = 1.25 * (double)s->top_k / vocab + 2.0 / std::sqrt((double)vocab);
-    if (q0 > 0.5) q0 = 0.5;
-    s->z0 = (float)normal_quantile(1.0 - q0);
+    s->z0 = pivot_quantile(s->top_k, vocab);
     {
         DeviceGuard dg(device);
         if (dg.err != hipSuccess) {
@@ -201,21 +241,25 @@ void ds_sample_destroy(ds_sampler* s) {
     delete s;
 }
 
-int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
-              const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
-              const float* temperature, int32_t num_requests, int32_t num_rows, uint64_t seed,
-              int32_t* tokens_out, float* logprobs_out, float* threshold_out, void* stream) {
-    g_err.clear();
-    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+}  // extern "C"
+
+namespace {
+
+// ds_sample's checks and launches, for a handle's settings or the handle-free
+// entry point's; ws is the streaming kernels' record workspace.
+int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids, const void* c_logits,
+                const void* u_logits, const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
+                const float* temperature, int32_t num_requests, int32_t num_rows, uint64_t seed, int32_t* tokens_out,
+                float* logprobs_out, float* threshold_out, void* stream) {
     if (!request_ids || !seq_lens || !iterations || !guidance_scale || !temperature)
         return fail(DS_ERR_INVALID_ARG, "a per-request host array is NULL");
     if (!c_logits || !tokens_out || !logprobs_out)
         return fail(DS_ERR_INVALID_ARG, "c_logits, tokens_out and logprobs_out must be non-NULL");
-    if (num_requests < 1 || num_requests > s->max_requests)
-        return fail(DS_ERR_CAPACITY, "num_requests %d outside [1, %d]", num_requests, s->max_requests);
-    if (num_rows < 1 || num_rows > s->max_rows)
-        return fail(DS_ERR_CAPACITY, "num_rows %d outside [1, %d]", num_rows, s->max_rows);
-    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if (num_requests < 1 || num_requests > s.max_requests)
+        return fail(DS_ERR_CAPACITY, "num_requests %d outside [1, %d]", num_requests, s.max_requests);
+    if (num_rows < 1 || num_rows > s.max_rows)
+        return fail(DS_ERR_CAPACITY, "num_rows %d outside [1, %d]", num_rows, s.max_rows);
+    const uintptr_t es = s.dtype == DS_DTYPE_BF16 ? 2 : 4;
     if (!aligned(c_logits, es)) return fail(DS_ERR_INVALID_ARG, "c_logits is not %d-byte aligned", (int)es);
     if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4) || (threshold_out && !aligned(threshold_out, 4)))
         return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
@@ -231,10 +275,12 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         P += seq_lens[r];
         if (guidance_scale[r] != 0.0f) Pu += seq_lens[r];
     }
-    const bool compact_u = (s->flags & DS_FLAG_COMPACT_U) != 0;
-    if (P > s->max_positions)
+    const bool compact_u = (s.flags & DS_FLAG_COMPACT_U) != 0;
+    if (P > s.max_positions)
         return fail(DS_ERR_CAPACITY, "sum(seq_lens) = %lld exceeds max_positions %lld", (long long)P,
-                    (long long)s->max_positions);
+                    (long long)s.max_positions);
+    if ((int64_t)num_rows * P > (int64_t)INT32_MAX)
+        return fail(DS_ERR_CAPACITY, "num_rows * sum(seq_lens) exceeds 2^31 - 1 cells");
     if (need_u && !u_logits)
         return fail(DS_ERR_INVALID_ARG, "u_logits is NULL but a request has guidance_scale != 0");
     if (need_u) {
@@ -242,31 +288,32 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         if ((((uintptr_t)u_logits - (uintptr_t)c_logits) & 15u) != 0)
             return fail(DS_ERR_UNSUPPORTED, "u_logits and c_logits must have the same address modulo 16 bytes");
     }
-    const bool bf16 = s->dtype == DS_DTYPE_BF16;
-    const bool small = use_small_kernel(s);
-    if (compact_u && need_u && !small && ((int64_t)s->vocab * (int64_t)es) % 16 != 0)
+    const bool bf16 = s.dtype == DS_DTYPE_BF16;
+    const bool small = !(s.flags & DS_FLAG_FORCE_FALLBACK) &&
+                       ds::small_slots_needed(bf16, s.vocab) <= (bf16 ? ds::kSmallMaxSlotsBf16 : ds::kSmallMaxSlotsF32);
+    if (compact_u && need_u && !small && ((int64_t)s.vocab * (int64_t)es) % 16 != 0)
         return fail(DS_ERR_UNSUPPORTED, "a compacted u layout needs V * %d bytes to be a multiple of 16 here", (int)es);
     if (P == 0) return DS_OK;
 
-    DeviceGuard dg(s->device);
+    DeviceGuard dg(s.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t st = (hipStream_t)stream;
 
     ds::SampleArgs a;
     a.c = c_logits;
     a.u = need_u ? u_logits : nullptr;
-    a.V = s->vocab;
+    a.V = s.vocab;
     a.rows = num_rows;
-    a.top_k = s->top_k;
-    a.vocab_chunks = s->vocab_chunks;
+    a.top_k = s.top_k;
+    a.vocab_chunks = s.vocab_chunks;
     a.k0 = (uint32_t)seed;
     a.k1 = (uint32_t)(seed >> 32);
-    a.z0 = s->z0;
-    a.force_fallback = (s->flags & DS_FLAG_FORCE_FALLBACK) ? 1 : 0;
+    a.z0 = s.z0;
+    a.force_fallback = (s.flags & DS_FLAG_FORCE_FALLBACK) ? 1 : 0;
     a.tokens = tokens_out;
     a.logprobs = logprobs_out;
     a.thresholds = threshold_out;
-    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    a.w = ds::RowWork{ws, 0, 0, 0, 0};
 
     // one launch per group of up to 64 non-empty requests (contiguous positions)
     int32_t r = 0;
@@ -313,8 +360,8 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         } else {
             // the streaming kernel: cells in batches that fit the workspace
             const int64_t cells = (int64_t)num_rows * rel;
-            a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
-            a.w.nparts = a.w.ppc * s->vocab_chunks;
+            a.w.ppc = ds::row_parts_per_chunk(bf16, s.vocab, s.vocab_chunks, cells);
+            a.w.nparts = a.w.ppc * s.vocab_chunks;
             const int64_t slots = ds::kWorkParts / a.w.nparts;
             for (int64_t c0 = 0; c0 < cells; c0 += slots) {
                 a.w.cell_base = c0;
@@ -326,6 +373,71 @@ int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, c
         pos += rel;
     }
     return DS_OK;
+}
+
+// The static scratch of ds_sample_static on each device, found once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+ds::PartRec* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+extern "C" {
+
+int ds_sample(ds_sampler* s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
+              const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
+              const float* temperature, int32_t num_requests, int32_t num_rows, uint64_t seed,
+              int32_t* tokens_out, float* logprobs_out, float* threshold_out, void* stream) {
+    g_err.clear();
+    if (!s) return fail(DS_ERR_INVALID_ARG, "sampler is NULL");
+    return sample_call(cfg_of(s), s->ws_part, request_ids, c_logits, u_logits, seq_lens, iterations,
+                       guidance_scale, temperature, num_requests, num_rows, seed, tokens_out, logprobs_out,
+                       threshold_out, stream);
+}
+
+int ds_sample_static(int32_t vocab, int32_t dtype, int32_t top_k, int32_t vocab_chunks, uint32_t flags,
+                     const int64_t* request_ids, const void* c_logits, const void* u_logits, const int32_t* seq_lens,
+                     const int32_t* iterations, const float* guidance_scale, const float* temperature,
+                     int32_t num_requests, int32_t num_rows, uint64_t seed, int32_t* tokens_out, float* logprobs_out,
+                     float* threshold_out, void* stream) {
+    g_err.clear();
+    {
+        const int rc = check_sampler_settings(vocab, dtype, top_k, vocab_chunks, flags);
+        if (rc != DS_OK) return rc;
+    }
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DS_ERR_UNSUPPORTED, "device %d beyond the first %d", dev, kMaxDevices);
+    ds::PartRec* ws = nullptr;
+    {
+        // the device copy of `scratch` of this device: its address, looked up once
+        // with this device current (the array's name is not a device address in
+        // host code)
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            void* p = nullptr;
+            const hipError_t e2 = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e2 != hipSuccess || !p) return hip_fail(e2 != hipSuccess ? e2 : hipErrorInvalidSymbol,
+                                                        "hipGetSymbolAddress(scratch)");
+            g_scratch_ptr[dev] = static_cast<ds::PartRec*>(p);
+        }
+        ws = g_scratch_ptr[dev];
+    }
+    // settings of a handle without its limits (the cell count must fit 31 bits);
+    // the first pivot quantile depends only on (top_k, vocab), so the last one is
+    // kept per thread
+    const int32_t k = top_k ? top_k : (vocab + 9) / 10;
+    thread_local int32_t z_k = -1, z_v = -1;
+    thread_local float z0 = 0.0f;
+    if (z_k != k || z_v != vocab) {
+        z0 = pivot_quantile(k, vocab);
+        z_k = k;
+        z_v = vocab;
+    }
+    const SamplerCfg cfg{vocab, dtype, k, vocab_chunks, flags, z0, INT32_MAX, INT32_MAX, INT32_MAX, -1};
+    return sample_call(cfg, ws, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale, temperature,
+                       num_requests, num_rows, seed, tokens_out, logprobs_out, threshold_out, stream);
 }
 
 int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
