@@ -40,6 +40,10 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "sampled positions/sec + achieved HBM GB/s (% of MI355X peak) per config"
 ROTATE_BYTES = 1 << 30
 SUITE_BUDGET_S = 0.03  # timed work per suite entry
+# threads per workgroup of the one-workgroup-per-row draft kernel and of the
+# streaming parts kernel (the launch shapes the read ceilings are measured at)
+GREEDY_ROW_THREADS = 512
+PARTS_THREADS = 512
 
 
 # Sources each kernel is built from: a stored counter reading is valid only while
@@ -356,13 +360,13 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
         outputs = [t.reshape(-1).cpu().numpy() for t in r.out if t is not None]
     ceiling = None
     if kind == "draft" and draft_kernel(w) == "k_greedy_rows":
-        # the same bytes at the same launch shape: one 1024-thread workgroup per row
-        ceiling = read_ceiling([(x,) for x in r.x], w.vocab * w.elem_bytes, 1024)
+        # the same bytes at the same launch shape: one workgroup per row
+        ceiling = read_ceiling([(x,) for x in r.x], w.vocab * w.elem_bytes, GREEDY_ROW_THREADS)
     elif kind == "sample" and name == "stress" and mode == "eager" and not threshold:
         # the parts kernel's shape: one 512-thread workgroup per part of a chunk,
         # over c and over u
         L = -(-w.vocab // w.vocab_chunks)
-        ceiling = read_ceiling(list(zip(r.c, r.u)), L * w.elem_bytes, 512)
+        ceiling = read_ceiling(list(zip(r.c, r.u)), L * w.elem_bytes, PARTS_THREADS)
     r.close()
     del r
     torch.cuda.empty_cache()

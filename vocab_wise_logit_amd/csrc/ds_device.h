@@ -258,6 +258,35 @@ __device__ __forceinline__ int row16_min_i(int x) {
     return min(x, dpp_i<kDppMirror>(x));
 }
 
+// The same inside each group of 8 lanes (xor 1, xor 2, half mirror), or of 16.
+template <int G>
+__device__ __forceinline__ float grp_max(float x) {
+    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    x = __builtin_fmaxf(x, dpp_f<kDppXor1>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppXor2>(x));
+    x = __builtin_fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    if (G == 16) x = __builtin_fmaxf(x, dpp_f<kDppMirror>(x));
+    return x;
+}
+template <int G>
+__device__ __forceinline__ float grp_sum(float x) {
+    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    if (G == 16) x += dpp_f<kDppMirror>(x);
+    return x;
+}
+template <int G>
+__device__ __forceinline__ int grp_min_i(int x) {
+    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    x = min(x, dpp_i<kDppXor1>(x));
+    x = min(x, dpp_i<kDppXor2>(x));
+    x = min(x, dpp_i<kDppHalfMirror>(x));
+    if (G == 16) x = min(x, dpp_i<kDppMirror>(x));
+    return x;
+}
+
 // Wave argmax of (z, id): larger z wins, equal z keeps the smaller id.  Returns
 // the winning lane's (z, id) in every lane, and the winning lane index.  The
 // id reduction runs only when several lanes hold the maximum.

@@ -1064,9 +1064,9 @@ __global__ __launch_bounds__(kWave) void k_greedy_merge(GreedyArgs a) {
 // vocabulary chunk after another, four 16-byte pieces in flight per group; at
 // the end of a chunk each wave reduces its lanes' (max, exp-sum, smallest
 // argmax) and writes one record to LDS, with no barrier, so the loads of the
-// next chunk follow at once.  After the row, lane j of the first wave folds
-// chunk j's wave records into its triple ([DRAFT] "Design and invariants"), and
-// the wave folds the triples into the row.  Chunk boundaries fall on piece
+// next chunk follow at once.  After the row, the first wave folds each chunk's
+// wave records into its triple ([DRAFT] "Design and invariants"), and the
+// triples into the row.  Chunk boundaries fall on piece
 // boundaries (the host checks V and ceil(V / chunks) are multiples of the ids
 // per piece and that rows start 16-byte aligned).
 template <bool BF16>
@@ -1099,22 +1099,25 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
         int mq = 0;
         u32x4 mraw = u32x4{ninf, ninf, ninf, ninf};
         // Whole groups load without any test, so all their loads are in flight
-        // together; the chunk's last, partial group clamps its indices and
-        // selects -inf past the end (a load under a branch would make the
-        // compiler wait for the loads before it).
-        auto group = [&](int base, auto full_tag) {
-            constexpr bool FULL = decltype(full_tag)::value;
-            u32x4 raw[UR];
+        // together, and the next whole group's loads are issued before this
+        // group is reduced (with one workgroup per compute unit there are two
+        // waves per SIMD, too few to hide the reduction behind other waves'
+        // loads); the chunk's last, partial group clamps its indices and selects
+        // -inf past the end (a load under a branch would make the compiler wait
+        // for the loads before it).
+        auto load_full = [&](int base, u32x4(&raw)[UR]) {
+#pragma unroll
+            for (int u = 0; u < UR; ++u) raw[u] = stream_load(xc + base + u * NTR + t);
+        };
+        auto load_tail = [&](int base, u32x4(&raw)[UR]) {
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
                 const int jp = base + u * NTR + t;
-                if (FULL) {
-                    raw[u] = stream_load(xc + jp);
-                } else {
-                    raw[u] = stream_load(xc + min(jp, nq - 1));
-                    if (jp >= nq) raw[u] = u32x4{ninf, ninf, ninf, ninf};
-                }
+                raw[u] = stream_load(xc + min(jp, nq - 1));
+                if (jp >= nq) raw[u] = u32x4{ninf, ninf, ninf, ninf};
             }
+        };
+        auto group = [&](int base, const u32x4(&raw)[UR]) {
             Piece<BF16> P[UR];
             float pm[UR];
             float gm = kNegInf;
@@ -1148,9 +1151,27 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
 #pragma unroll
                 for (int e = 0; e < EPP; ++e) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(P[u].h[e], kLog2e, -mL));
         };
+        constexpr int GP = NTR * UR;  // pieces per group
+        const int nfull = nq / GP;
         int base = 0;
-        for (; base + NTR * UR <= nq; base += NTR * UR) group(base, std::true_type{});
-        if (base < nq) group(base, std::false_type{});
+        if (nfull > 0) {
+            u32x4 cur[UR], nxt[UR];
+            load_full(0, cur);
+            for (int g = 1; g < nfull; ++g) {
+                load_full(g * GP, nxt);
+                group(base, cur);
+                base += GP;
+#pragma unroll
+                for (int u = 0; u < UR; ++u) cur[u] = nxt[u];
+            }
+            group(base, cur);
+            base += GP;
+        }
+        if (base < nq) {
+            u32x4 raw[UR];
+            load_tail(base, raw);
+            group(base, raw);
+        }
         // undo the rounding of m * log2(e), then the wave's share of the chunk
         if (m > kNegInf) acc *= __builtin_amdgcn_exp2f(-__builtin_fmaf(m, kLog2e, -(m * kLog2e)));
         const float wm = wave_max(m);
@@ -1175,15 +1196,16 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
     }
     __syncthreads();
     if (wv != 0) return;
-    // The first wave folds the records: lane l takes wave (l & 15)'s record of
-    // chunk 4g + (l >> 4), each row of 16 lanes reduces one chunk to its triple,
-    // and the triples fold into the row (larger max wins, equal maxima keep the
-    // smaller id, sums add in probability space).
+    // The first wave folds the records: in groups of NW lanes, lane l takes wave
+    // (l % NW)'s record of chunk g + l / NW, each group reduces one chunk to its
+    // triple, and the triples fold into the row (larger max wins, equal maxima
+    // keep the smaller id, sums add in probability space).
+    constexpr int CPP = kWave / NW;  // chunks per pass of the wave
     float M = kNegInf, S = 0.0f;
     int id = 0x7FFFFFFF;
-    for (int g = 0; g < nch; g += 4) {
-        const int c = g + (lane >> 4);
-        const int w = lane & 15;
+    for (int g = 0; g < nch; g += CPP) {
+        const int c = g + lane / NW;
+        const int w = lane % NW;
         float rm = kNegInf, rs = 0.0f;
         int ri = 0x7FFFFFFF;
         if (c < nch) {
@@ -1191,16 +1213,16 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
             rs = s_s[c][w];
             ri = s_id[c][w];
         }
-        const float mj = row16_max(rm);
-        const float sj = row16_sum((rm > kNegInf) ? rs * __builtin_amdgcn_exp2f((rm - mj) * kLog2e) : 0.0f);
-        const int idj = row16_min_i((mj > kNegInf && rm == mj) ? ri : 0x7FFFFFFF);
+        const float mj = grp_max<NW>(rm);
+        const float sj = grp_sum<NW>((rm > kNegInf) ? rs * __builtin_amdgcn_exp2f((rm - mj) * kLog2e) : 0.0f);
+        const int idj = grp_min_i<NW>((mj > kNegInf && rm == mj) ? ri : 0x7FFFFFFF);
         if (a.triples && w == 0 && c < nch) {
             float* o = a.triples + ((int64_t)c * a.n_rows + row) * 3;
             o[0] = mj;
             o[1] = (mj > kNegInf) ? mj + __builtin_logf(sj) : kNegInf;
             o[2] = __int_as_float(idj);
         }
-        // fold this group's chunks (the first lane of each row) into the row
+        // fold this pass's chunk triples (the first lane of each group) into the row
         const bool lead = w == 0;
         const float gm = wave_max(lead ? mj : kNegInf);
         const float mn = __builtin_fmaxf(M, gm);
