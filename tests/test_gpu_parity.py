@@ -222,6 +222,37 @@ def test_row_kernel_threshold_sample_misses_a_hidden_cluster():
         check_sample(w, run_sample(w, threshold=thr), ref)
 
 
+def test_threshold_window_edge_rows_at_full_vocabulary():
+    # V = 248320 in four chunks with the threshold output: each row's threshold
+    # comes from the keys its parts collected inside a window bracketing it, or,
+    # when the window misses or overflows its buffer, from the exact passes over
+    # the row.  In one launch: ordinary rows, a row of heavy exact ties (the
+    # window holds far more keys than its buffer), a row with all but 8320 ids
+    # masked (threshold -inf), a constant row (threshold = maximum) and a row
+    # whose largest ids hide in runs the window's sample skips.
+    V, P = 248320, 7
+    w = synth.diffusion("window_edges", seed=77, vocab=V, rows=1, seq_lens=[P], sigma=4.0, guidance=1.5,
+                        temperature=1.0, top_k=24832, vocab_chunks=4)
+    c = oracle.bf16_to_f32(w.c)
+    u = oracle.bf16_to_f32(w.u)
+    rng = np.random.default_rng(5)
+    c[0, 1] = rng.integers(0, 3, V).astype(np.float32)  # values 0, 1, 2: massive ties
+    u[0, 1] = c[0, 1]
+    masked = rng.permutation(V)[: V - 8320]
+    c[0, 2, masked] = -np.inf
+    u[0, 2, masked] = -np.inf
+    c[0, 3] = 1.25
+    u[0, 3] = 0.5
+    c[0, 5, 512:4096] += np.float32(60.0)  # ids 512..4095, skipped by a 1-in-33 run sample
+    w.c = synth.bf16_from_f32(c)
+    w.u = synth.bf16_from_f32(u)
+    ref = oracle.sample_workload(w)
+    assert np.isneginf(ref.thresholds[2]) and ref.thresholds[3] == ref.max_h[3]
+    for thr in (True, False):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+    check_sample(w, run_sample(w, force_fallback=True), ref)
+
+
 def test_row_kernel_many_parts_per_row():
     # 4 positions x 4 chunks: each chunk is cut into several parts, each running
     # its own race

@@ -25,6 +25,11 @@ struct ds_sampler {
     int device;
     // streaming-kernel workspace: one partial record per (row, vocabulary part)
     ds::PartRec* ws_part;
+    // threshold windows and their key buffers for win_rows rows per launch
+    // (vocabularies on the streaming path only; nullptr otherwise)
+    ds::WinRec* ws_win;
+    uint32_t* ws_keys;
+    int64_t win_rows;
     int32_t vocab;
     int32_t dtype;
     int32_t max_rows;
@@ -109,11 +114,31 @@ struct SamplerCfg {
     int32_t max_rows, max_requests;
     int64_t max_positions;
     int device;  // -1: the calling thread's current device
+    // threshold windows of the streaming path (none: nullptr, 0 rows)
+    ds::WinRec* win;
+    uint32_t* keys;
+    int64_t win_rows;
 };
 
 SamplerCfg cfg_of(const ds_sampler* s) {
-    return SamplerCfg{s->vocab, s->dtype, s->top_k, s->vocab_chunks, s->flags, s->z0,
-                      s->max_rows, s->max_requests, s->max_positions, s->device};
+    return SamplerCfg{s->vocab,    s->dtype,        s->top_k,         s->vocab_chunks, s->flags,
+                      s->z0,       s->max_rows,     s->max_requests,  s->max_positions, s->device,
+                      s->ws_win,   s->ws_keys,      s->win_rows};
+}
+
+// Rows per streaming launch, and the window buffers it uses: with the threshold
+// output and window buffers, as many rows as they hold (and the records allow).
+int64_t stream_slots(ds::SampleArgs& a, ds::WinRec* win, uint32_t* keys, int64_t win_rows) {
+    int64_t slots = ds::kWorkParts / a.w.nparts;
+    if (a.thresholds && !a.force_fallback && win && keys && win_rows > 0) {
+        a.w.win = win;
+        a.w.keys = keys;
+        if (slots > win_rows) slots = win_rows;
+    } else {
+        a.w.win = nullptr;
+        a.w.keys = nullptr;
+    }
+    return slots;
 }
 
 // First pivot of the wave-per-cell kernel's exact threshold search: the normal
@@ -160,7 +185,7 @@ int launch_dev_params(ds_sampler* s, ds::SampleArgs& a, const ds::DevReq& d, int
     const int64_t cells = (int64_t)num_rows * positions;
     a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
     a.w.nparts = a.w.ppc * s->vocab_chunks;
-    const int64_t slots = ds::kWorkParts / a.w.nparts;
+    const int64_t slots = stream_slots(a, s->ws_win, s->ws_keys, s->win_rows);
     for (int64_t c0 = 0; c0 < cells; c0 += slots) {
         a.w.cell_base = c0;
         a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
@@ -204,6 +229,9 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
     ds_sampler* s = new (std::nothrow) ds_sampler();
     if (s) {
         s->ws_part = nullptr;
+        s->ws_win = nullptr;
+        s->ws_keys = nullptr;
+        s->win_rows = 0;
     }
     if (!s) return fail(DS_ERR_NO_MEMORY, "host allocation failed");
     s->device = device;
@@ -229,6 +257,22 @@ int ds_sample_create(ds_sampler** out, int device, int32_t vocab, int32_t dtype,
             delete s;
             return fail(DS_ERR_NO_MEMORY, "device workspace allocation failed");
         }
+        if (!small_fits(s)) {
+            // the streaming path's threshold windows: a record and a key buffer
+            // (64 KB) per row of a launch, at most kWinRows rows (128 MB)
+            const int64_t cells = (int64_t)max_rows * max_positions;
+            s->win_rows = cells < ds::kWinRows ? cells : ds::kWinRows;
+            const hipError_t e2 = hipMalloc(&s->ws_win, sizeof(ds::WinRec) * s->win_rows);
+            const hipError_t e3 =
+                e2 == hipSuccess ? hipMalloc(&s->ws_keys, sizeof(uint32_t) * ds::kWinKeysPerRow * s->win_rows)
+                                 : e2;
+            if (e2 != hipSuccess || e3 != hipSuccess) {
+                (void)hipFree(s->ws_win);
+                (void)hipFree(s->ws_part);
+                delete s;
+                return fail(DS_ERR_NO_MEMORY, "device workspace allocation failed");
+            }
+        }
     }
     *out = s;
     return DS_OK;
@@ -238,6 +282,8 @@ void ds_sample_destroy(ds_sampler* s) {
     if (!s) return;
     DeviceGuard dg(s->device);
     (void)hipFree(s->ws_part);
+    (void)hipFree(s->ws_win);
+    (void)hipFree(s->ws_keys);
     delete s;
 }
 
@@ -313,7 +359,7 @@ int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids
     a.tokens = tokens_out;
     a.logprobs = logprobs_out;
     a.thresholds = threshold_out;
-    a.w = ds::RowWork{ws, 0, 0, 0, 0};
+    a.w = ds::RowWork{ws, 0, 0, 0, 0, nullptr, nullptr};
 
     // one launch per group of up to 64 non-empty requests (contiguous positions)
     int32_t r = 0;
@@ -362,7 +408,7 @@ int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids
             const int64_t cells = (int64_t)num_rows * rel;
             a.w.ppc = ds::row_parts_per_chunk(bf16, s.vocab, s.vocab_chunks, cells);
             a.w.nparts = a.w.ppc * s.vocab_chunks;
-            const int64_t slots = ds::kWorkParts / a.w.nparts;
+            const int64_t slots = stream_slots(a, s.win, s.keys, s.win_rows);
             for (int64_t c0 = 0; c0 < cells; c0 += slots) {
                 a.w.cell_base = c0;
                 a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
@@ -435,7 +481,8 @@ int ds_sample_static(int32_t vocab, int32_t dtype, int32_t top_k, int32_t vocab_
         z_k = k;
         z_v = vocab;
     }
-    const SamplerCfg cfg{vocab, dtype, k, vocab_chunks, flags, z0, INT32_MAX, INT32_MAX, INT32_MAX, -1};
+    const SamplerCfg cfg{vocab, dtype, k, vocab_chunks, flags, z0, INT32_MAX, INT32_MAX, INT32_MAX, -1,
+                         nullptr, nullptr, 0};
     return sample_call(cfg, ws, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale, temperature,
                        num_requests, num_rows, seed, tokens_out, logprobs_out, threshold_out, stream);
 }
@@ -490,7 +537,7 @@ int ds_sample_device_params(ds_sampler* s, const int64_t* request_ids, const voi
     a.tokens = tokens_out;
     a.logprobs = logprobs_out;
     a.thresholds = threshold_out;
-    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0, nullptr, nullptr};
     ds::DevReq d;
     d.request_ids = request_ids;
     d.seq_lens = seq_lens;
@@ -531,7 +578,7 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
     a.logprob = logprob_out;
     a.triples = triples_out;
     const bool bf16 = s->dtype == DS_DTYPE_BF16;
-    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0, nullptr, nullptr};
     // Rows that fill every compute unit (whole rounds of one row per unit, or
     // enough rounds that the last partial one costs little) take one workgroup
     // per row and no second kernel; otherwise rows are split into parts.
@@ -625,7 +672,7 @@ int ds_sample_ar(ds_sampler* s, const int64_t* request_ids, void* logits, const 
     a.tokens = tokens_out;
     a.logprobs = logprobs_out;
     a.thresholds = nullptr;
-    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0};
+    a.w = ds::RowWork{s->ws_part, 0, 0, 0, 0, nullptr, nullptr};
     ds::DevReq d;
     d.request_ids = request_ids;
     d.seq_lens = nullptr;

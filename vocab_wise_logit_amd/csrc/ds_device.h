@@ -228,6 +228,14 @@ __device__ __forceinline__ float wave_sum(float x) {
     x += dpp_f<kDppMirror>(x);
     return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
 }
+__device__ __forceinline__ int wave_sum_i(int x) {
+    x += dpp_i<kDppXor1>(x);
+    x += dpp_i<kDppXor2>(x);
+    x += dpp_i<kDppHalfMirror>(x);
+    x += dpp_i<kDppMirror>(x);
+    return (__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16)) +
+           (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
+}
 __device__ __forceinline__ int wave_min_i(int x) {
     x = min(x, dpp_i<kDppXor1>(x));
     x = min(x, dpp_i<kDppXor2>(x));

@@ -19,8 +19,21 @@ struct PartRec {
     float bz;     // best perturbed score h/tau + G among them
     int be;       // its id (smallest on equal scores)
     float bh;     // its h
-    int pad;
+    int above;    // keys above the row's threshold window (when the row has one)
 };
+
+// The exact threshold's window of one row (threshold output requested): order
+// keys [lo, hi] bracketing the row's top_k-th largest key, from a sample of the
+// row (lo > hi: no window).  While they stream, the parts count the keys above
+// it (PartRec::above) and append the h (raw bits) of the ids inside it to the
+// row's key buffer.
+struct WinRec {
+    uint32_t lo, hi;
+    int32_t count;  // keys appended so far (may exceed the buffer: then unusable)
+    int32_t pad;
+};
+constexpr int kWinKeysPerRow = 16384;  // key buffer per row (64 KB)
+constexpr int kWinRows = 2048;         // rows per launch the handle's window buffers hold (128 MB)
 struct Cand {
     float h;
     int e;
@@ -35,6 +48,8 @@ struct RowWork {
     int32_t ppc;       // parts per chunk
     int64_t cell_base; // first launch-relative cell handled by this launch
     int32_t ncells;    // cells in this launch (<= slots)
+    WinRec* win;       // [slots] threshold windows, or nullptr (no window path)
+    uint32_t* keys;    // [slots][kWinKeysPerRow] h (raw bits) inside each row's window
 };
 
 // Arguments common to one sampler launch (one group of <= 64 requests).

@@ -48,7 +48,7 @@ struct WaveRec {
     int id;
     float bz, bh;
     int be, nq;
-    int pad;
+    int above;  // keys above the row's threshold window
 };
 
 // Cross-wave reduction slots of a block of NW_ waves.
@@ -67,15 +67,28 @@ using Red = RedT<NWAVES>;
 // above the bound (their decoded h and first id), and ids at or above the bound.
 // Each is drained once it holds 64 entries, and one step adds at most 64, so 128
 // entries never overflow.
-template <bool BF16, bool SAMPLE>
+template <bool BF16, bool SAMPLE, bool WIN = false>
 struct PartLDS {
     static constexpr int EPP = BF16 ? 8 : 4;
     static constexpr int kQ = SAMPLE ? 2 * kWave : 1;
     float ph[NWAVES][kQ][EPP];
     int pv[NWAVES][kQ];
     Cand q[NWAVES][kQ];
+    // threshold window: pieces holding an id inside it (up to 64 per wave, ids
+    // outside the part as NaN), and the h (raw bits) of those ids, staged per wave
+    // and written to the row's key buffer 64 at a time
+    float wq[NWAVES][WIN ? kWave : 1][EPP];
+    uint32_t wk[NWAVES][WIN ? 2 * kWave : 1];
     uint32_t bkey;  // order key of the block's race bound (only grows)
     Red r;
+};
+
+// What a part needs to know about its row's threshold window.
+struct WinCtx {
+    bool on;          // the row has a window
+    float lo, hi;     // its bounds as floats
+    uint32_t* keys;   // the row's buffer [kWinKeysPerRow] of h (raw bits) inside the window
+    int32_t* count;   // keys appended to it by all of the row's parts
 };
 
 // The exact threshold select: digits of 11, 11 and 10 bits of the order key;
@@ -94,6 +107,8 @@ constexpr int kMergeThreadsFast = 256;
 constexpr int kKeyCapFast = 2048;
 constexpr int kMergeThreadsExact = 512;
 constexpr int kKeyCapExact = 8192;
+// The window kernel: one workgroup per row, sampling it into LDS.
+constexpr int kWindowThreads = 512;
 
 // The merge's staged part records (or the threshold select's keys) and histogram.
 template <int MT_, int KCAP>
@@ -325,115 +340,204 @@ __device__ __forceinline__ int wave_append(bool pred, int* counter) {
     return pred ? base + lanes_below(m) : -1;
 }
 
-// Exact top_k-th largest h of the row (an LDS radix select on order keys).
-//
-// On long rows a sample comes first: the keys of every `every`-th run of 64
-// pieces (at most kKeyCap of them) go to LDS, and two selects there bracket the
-// answer between the sample's order statistics around rank k * n / V, three
-// standard deviations out each way.  One pass over the row then counts the keys
-// above the bracket and collects those inside it; when the k-th largest falls
-// inside and the bracket fits in LDS, it is selected there exactly.  Otherwise
-// (an unlucky sample, or too many keys in the bracket) the full path runs: one
-// pass histograms the first 11-bit digit, a second collects the keys in the
-// chosen bin into LDS, where the last two digits are selected, and if that bin
-// holds more than kKeyCap keys the last digits take a pass over the row each.
-// The result is exact either way; the sample only saves a pass.
+// One pass of an LDS radix select: histogram the digit `dg` of the keys that
+// share the selected prefix (from LDS, or over the whole row), then fix that
+// digit (the bin holding the kk-th largest; kk becomes the rank inside it).
 template <bool BF16, typename SH>
-__device__ __forceinline__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, SH& sh) {
+__device__ __forceinline__ void select_pass(const RowGeom& G, float s, bool use_u, SH& sh, int dg, bool from_lds, int n,
+                                            uint32_t& prefix, uint32_t& pmask, int& kk) {
+    constexpr int BT = SH::kThreads;
+    const int shift = kDigitShift[dg];
+    const uint32_t dmask = (1u << kDigitBits[dg]) - 1u;
+    for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
+    __syncthreads();
+    if (from_lds) {
+        for (int i = threadIdx.x; i < n; i += BT) {
+            const uint32_t key = sh.u.keys[i];
+            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+        }
+    } else {
+        for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
+            const uint32_t key = order_key(h + 0.0f);
+            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+        });
+    }
+    __syncthreads();
+    const uint32_t d = find_digit(sh, 1 << kDigitBits[dg], kk);
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+}
+
+// The rank-th largest of the n keys in sh.u.keys (1 <= rank <= n), exactly.
+template <bool BF16, typename SH>
+__device__ __forceinline__ uint32_t lds_kth(const RowGeom& G, SH& sh, int n, int rank) {
+    uint32_t prefix = 0, pmask = 0;
+    int kk = rank;
+    select_pass<BF16>(G, 0.0f, false, sh, 0, true, n, prefix, pmask, kk);
+    select_pass<BF16>(G, 0.0f, false, sh, 1, true, n, prefix, pmask, kk);
+    select_pass<BF16>(G, 0.0f, false, sh, 2, true, n, prefix, pmask, kk);
+    return prefix;
+}
+
+// A window of order keys that holds the row's top_k-th largest key with high
+// probability, from a sample: the keys of every `every`-th run of 64 pieces (at
+// most kKeyCap of them) go to LDS, and two selects there give the sample's order
+// statistics at ranks k * n / V -+ (sigmas standard deviations + 4).  The window
+// [key_lo, key_hi] is expected to hold about 2 (sigmas sqrt(k f) + 4) / f row ids
+// (f the sampled share); whether it holds the answer is checked by whoever uses
+// it.  Returns false when the row is too short for a sample to pay, or the
+// expected window would not leave room in `cap` keys; then no window exists.
+template <bool BF16, typename SH>
+__device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool use_u, int k, SH& sh, float sigmas,
+                                              int cap, uint32_t& key_lo, uint32_t& key_hi) {
     constexpr int BT = SH::kThreads;
     constexpr int EPP = Piece<BF16>::EPP;
-    uint32_t prefix = 0, pmask = 0;
-    int kk = k;
-    auto hist_pass = [&](int dg, bool from_lds, int n) {
-        const int shift = kDigitShift[dg];
-        const uint32_t dmask = (1u << kDigitBits[dg]) - 1u;
-        for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
-        __syncthreads();
-        if (from_lds) {
-            for (int i = threadIdx.x; i < n; i += BT) {
-                const uint32_t key = sh.u.keys[i];
-                if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-            }
-        } else {
-            for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
-                const uint32_t key = order_key(h + 0.0f);
-                if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-            });
-        }
-        __syncthreads();
-        const uint32_t d = find_digit(sh, 1 << kDigitBits[dg], kk);
-        prefix |= d << shift;
-        pmask |= dmask << shift;
-    };
-    // the rank-th largest of the n keys in LDS (1 <= rank <= n)
-    auto lds_kth = [&](int n, int rank) {
-        prefix = 0;
-        pmask = 0;
-        kk = rank;
-        hist_pass(0, true, n);
-        hist_pass(1, true, n);
-        hist_pass(2, true, n);
-        return prefix;
-    };
-
-    // ---- sampled bracket
     const int64_t runs = ((G.gbase + G.V - 1) / EPP - G.gbase / EPP) / kWave + 1;
     constexpr int kRunIds = kWave * EPP;
     constexpr int kSampleRuns = SH::kKeyCap / kRunIds - 1;  // ceil(runs / every) <= runs / every + 1
     const int every = kSampleRuns > 0 ? (int)((runs + kSampleRuns - 1) / kSampleRuns) : 0;
-    // the bracket's expected width in row ids, 2 m / f with f the sampled share,
+    // the window's expected width in row ids, 2 m / f with f the sampled share,
     // must leave room in LDS (checked again on the sample actually drawn)
     const float f_exp = (float)(((runs + every - 1) / max(every, 1)) * kRunIds) / (float)G.V;
-    const float m_exp = 3.0f * __builtin_sqrtf((float)k * f_exp) + 4.0f;
-    if (every >= 4 && 2.0f * m_exp < 0.7f * (float)SH::kKeyCap * f_exp) {
-        if (threadIdx.x == 0) sh.nkeys = 0;
+    const float m_exp = sigmas * __builtin_sqrtf((float)k * f_exp) + 4.0f;
+    if (!(every >= 4 && 2.0f * m_exp < 0.7f * (float)cap * f_exp)) return false;
+    if (threadIdx.x == 0) sh.nkeys = 0;
+    __syncthreads();
+    for_each_sampled_id<BF16, BT>(G, s, use_u, every, [&](int, float h) {
+        const int at = wave_append(true, &sh.nkeys);
+        if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = order_key(h + 0.0f);
+    });
+    __syncthreads();
+    const int ns = min(sh.nkeys, SH::kKeyCap);
+    // expected sample rank of the answer and a margin of `sigmas` standard deviations
+    const float f = (float)ns / (float)G.V;
+    const float r = (float)k * f;
+    const float m = sigmas * __builtin_sqrtf(r) + 4.0f;
+    if (!(ns > 0 && 2.0f * m < 0.7f * (float)cap * f)) return false;
+    const int r_hi = (int)__builtin_floorf(r - m);
+    const int r_lo = (int)__builtin_ceilf(r + m);
+    // the two order statistics to 22 bits (two 11-bit digits, the first pass
+    // shared), the window widened outward to whole 22-bit bins: at most 1023
+    // keys of widening each way
+    uint32_t p0 = 0, m0 = 0;
+    int kk = 0;
+    select_pass<BF16>(G, 0.0f, false, sh, 0, true, ns, p0, m0, kk);  // histogram only (kk = 0)
+    uint32_t ph = 0, pl = 0;
+    int kh = r_hi, kl = r_lo;
+    if (r_hi >= 1) ph = find_digit(sh, 1 << kDigitBits[0], kh) << kDigitShift[0];
+    if (r_lo <= ns) pl = find_digit(sh, 1 << kDigitBits[0], kl) << kDigitShift[0];
+    const uint32_t mk0 = ((1u << kDigitBits[0]) - 1u) << kDigitShift[0];
+    constexpr uint32_t kLow = (1u << kDigitShift[1]) - 1u;  // bits below the second digit
+    if (r_hi >= 1) {
+        uint32_t mh = mk0;
+        select_pass<BF16>(G, 0.0f, false, sh, 1, true, ns, ph, mh, kh);
+        key_hi = ph | kLow;
+    } else {
+        key_hi = 0xFFFFFFFFu;
+    }
+    if (r_lo <= ns) {
+        uint32_t ml = mk0;
+        select_pass<BF16>(G, 0.0f, false, sh, 1, true, ns, pl, ml, kl);
+        key_lo = pl;
+    } else {
+        key_lo = 0u;
+    }
+    return true;
+}
+
+// The rank-th largest (1 <= rank <= n) order key of the n h values (raw bits,
+// keys of h + 0) in global memory at hb, all with keys in [base, base + span]: a
+// radix select on key - base with as many 11-bit digits as the span needs (a
+// narrow span would otherwise put every key of the first digit into one bin),
+// each pass reading the values again (they are few, and cached after the first).
+template <typename SH>
+__device__ __forceinline__ uint32_t window_kth(SH& sh, const uint32_t* hb, int n, int rank, uint32_t base,
+                                               uint32_t span) {
+    constexpr int BT = SH::kThreads;
+    constexpr int kBits = 11;
+    static_assert((1 << kBits) == kHistBins, "one digit per histogram");
+    const gptr<uint32_t> g = as_global<uint32_t>(hb);
+    const int span_bits = span ? 32 - __builtin_clz(span) : 1;
+    const int passes = (span_bits + kBits - 1) / kBits;
+    uint32_t prefix = 0, pmask = 0;
+    int kk = rank;
+    for (int pidx = passes - 1; pidx >= 0; --pidx) {
+        const int shift = kBits * pidx;
+        const uint32_t dmask = (1u << kBits) - 1u;
+        for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
         __syncthreads();
-        for_each_sampled_id<BF16, BT>(G, s, use_u, every, [&](int, float h) {
-            const int at = wave_append(true, &sh.nkeys);
+        auto add = [&](uint32_t bits) {
+            const uint32_t rel = order_key(__uint_as_float(bits) + 0.0f) - base;
+            if ((rel & pmask) == prefix) atomicAdd(&sh.hist[(rel >> shift) & dmask], 1u);
+        };
+        int i = threadIdx.x;
+        for (; i + 3 * BT < n; i += 4 * BT) {  // four loads in flight per thread
+            const uint32_t a = g[i], b = g[i + BT], c = g[i + 2 * BT], d = g[i + 3 * BT];
+            add(a);
+            add(b);
+            add(c);
+            add(d);
+        }
+        for (; i < n; i += BT) add(g[i]);
+        __syncthreads();
+        const uint32_t d = find_digit(sh, kHistBins, kk);
+        prefix |= d << shift;
+        pmask |= shift + kBits >= 32 ? ~0u << shift : dmask << shift;
+    }
+    return base + prefix;
+}
+
+// The float bounds of a key window, for comparing h directly (the key order is
+// the order of h + 0, and h is never NaN where this is used); the open ends,
+// keys 0xFFFFFFFF and 0 (which decode to NaN), become +-inf.
+__device__ __forceinline__ float window_hi(uint32_t key_hi) {
+    return key_hi == 0xFFFFFFFFu ? __builtin_inff() : key_value(key_hi);
+}
+__device__ __forceinline__ float window_lo(uint32_t key_lo) {
+    return key_lo == 0u ? -__builtin_inff() : key_value(key_lo);
+}
+
+// Exact top_k-th largest h of the row (an LDS radix select on order keys), by
+// passes over the row.
+//
+// On long rows a sample comes first (sample_window), then one pass over the row
+// counts the keys above the window and collects those inside it; when the k-th
+// largest falls inside and the window fits in LDS, it is selected there
+// exactly.  Otherwise (an unlucky sample, or too many keys in the window) the
+// full path runs: one pass histograms the first 11-bit digit, a second collects
+// the keys in the chosen bin into LDS, where the last two digits are selected,
+// and if that bin holds more than kKeyCap keys the last digits take a pass over
+// the row each.  The result is exact either way; the sample only saves a pass.
+template <bool BF16, typename SH>
+__device__ __forceinline__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, SH& sh) {
+    constexpr int BT = SH::kThreads;
+    uint32_t key_lo, key_hi;
+    if (sample_window<BF16>(G, s, use_u, k, sh, 3.0f, SH::kKeyCap, key_lo, key_hi)) {
+        if (threadIdx.x == 0) {
+            sh.nkeys = 0;
+            sh.nabove = 0;
+        }
+        __syncthreads();
+        const float f_hi = window_hi(key_hi);
+        const float f_lo = window_lo(key_lo);
+        int above = 0;
+        for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
+            above += h > f_hi ? 1 : 0;
+            const int at = wave_append(h >= f_lo && h <= f_hi, &sh.nkeys);
             if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = order_key(h + 0.0f);
         });
+        if (above) atomicAdd(&sh.nabove, above);
         __syncthreads();
-        const int ns = min(sh.nkeys, SH::kKeyCap);
-        // expected sample rank of the answer and a margin of three standard deviations
-        const float f = (float)ns / (float)G.V;
-        const float r = (float)k * f;
-        const float m = 3.0f * __builtin_sqrtf(r) + 4.0f;
-        // the bracket's expected width in row ids must leave room in LDS
-        if (ns > 0 && 2.0f * m < 0.7f * (float)SH::kKeyCap * f) {
-            const int r_hi = (int)__builtin_floorf(r - m);
-            const int r_lo = (int)__builtin_ceilf(r + m);
-            const uint32_t key_hi = r_hi >= 1 ? lds_kth(ns, r_hi) : 0xFFFFFFFFu;
-            const uint32_t key_lo = r_lo <= ns ? lds_kth(ns, r_lo) : 0u;
-            if (threadIdx.x == 0) {
-                sh.nkeys = 0;
-                sh.nabove = 0;
-            }
-            __syncthreads();
-            // compared as floats (the key order is the order of h + 0, and h is
-            // never NaN here); only the collected ids need their key
-            // (the open ends, keys 0xFFFFFFFF and 0, decode to NaN: they become +-inf)
-            const float f_hi = key_hi == 0xFFFFFFFFu ? __builtin_inff() : key_value(key_hi);
-            const float f_lo = key_lo == 0u ? -__builtin_inff() : key_value(key_lo);
-            int above = 0;
-            for_each_id<BF16, BT>(G, s, use_u, [&](int, float h) {
-                above += h > f_hi ? 1 : 0;
-                const int at = wave_append(h >= f_lo && h <= f_hi, &sh.nkeys);
-                if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = order_key(h + 0.0f);
-            });
-            if (above) atomicAdd(&sh.nabove, above);
-            __syncthreads();
-            const int n = sh.nkeys;
-            const int A = sh.nabove;
-            __syncthreads();
-            if (n <= SH::kKeyCap && A < k && k <= A + n) return key_value(lds_kth(n, k - A));
-        }
-        prefix = 0;
-        pmask = 0;
-        kk = k;
+        const int n = sh.nkeys;
+        const int A = sh.nabove;
+        __syncthreads();
+        if (n <= SH::kKeyCap && A < k && k <= A + n) return key_value(lds_kth<BF16>(G, sh, n, k - A));
     }
 
     // ---- full path
-    hist_pass(0, false, 0);
+    uint32_t prefix = 0, pmask = 0;
+    int kk = k;
+    select_pass<BF16>(G, s, use_u, sh, 0, false, 0, prefix, pmask, kk);
     // keep the keys that share the first digit with the answer
     if (threadIdx.x == 0) sh.nkeys = 0;
     __syncthreads();
@@ -445,8 +549,8 @@ __device__ __forceinline__ float radix_select_row(const RowGeom& G, float s, boo
     __syncthreads();
     const int n = sh.nkeys;
     const bool fit = n <= SH::kKeyCap;
-    hist_pass(1, fit, n);
-    hist_pass(2, fit, n);
+    select_pass<BF16>(G, s, use_u, sh, 1, fit, n, prefix, pmask, kk);
+    select_pass<BF16>(G, s, use_u, sh, 2, fit, n, prefix, pmask, kk);
     return key_value(prefix);
 }
 
@@ -468,6 +572,7 @@ struct PartOut {
     // how many ids were queued
     float bz, bh;
     int be, nq;
+    int above;  // keys above the threshold window (WIN)
 };
 
 // Stream one part: online max / exp-sum per thread, block-reduced to (m, s,
@@ -476,9 +581,12 @@ struct PartOut {
 // `race`, each wave also runs the Gumbel race over the ids that can still win
 // (queued in LDS, scored 64 at a time).  At most 64 VGPRs: four workgroups per CU
 // keep enough loads in flight.
-template <bool BF16, bool SAMPLE, bool FIX>
+// With WIN (the threshold output requested) each thread also counts the ids
+// whose h lies above the row's threshold window and appends the order keys of
+// those inside it to the row's key buffer, through a per-wave LDS stage.
+template <bool BF16, bool SAMPLE, bool FIX, bool WIN>
 __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, const CellParams& cp, bool use_u,
-                               bool race, PartLDS<BF16, SAMPLE>& sh) {
+                               bool race, PartLDS<BF16, SAMPLE, WIN>& sh, const WinCtx& wc) {
     constexpr int EPP = Piece<BF16>::EPP;
     const float s = cp.s;
     float m = kNegInf, acc = 0.0f;
@@ -543,6 +651,43 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
         }
     };
 
+    // threshold window: ids above it, queued pieces and staged keys (all counted
+    // per wave, wave-uniform)
+    int wabove = 0, wqn = 0, wn = 0;
+    // write the newest n (<= 64) staged keys to the row's buffer (keys past its
+    // capacity are dropped; the count still grows, which marks the row's window
+    // as unusable)
+    auto win_flush = [&](int n) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(wc.count, n);
+        base = __builtin_amdgcn_readlane(base, 0);
+        wn -= n;
+        if (lane < n && base + lane < kWinKeysPerRow) wc.keys[base + lane] = sh.wk[wv][wn + lane];
+    };
+    auto win_push = [&](float h) {
+        const uint64_t mk = __builtin_amdgcn_ballot_w64(h >= wc.lo) & __builtin_amdgcn_ballot_w64(h <= wc.hi);
+        if (mk) {
+            if ((mk >> lane) & 1ull) sh.wk[wv][wn + lanes_below(mk)] = __float_as_uint(h);
+            wn += popc(mk);
+            if (wn >= kWave) {
+                __builtin_amdgcn_wave_barrier();
+                win_flush(kWave);
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+    };
+    // the ids inside the window from the queued pieces, one piece per lane
+    // (a rolled loop, so that its pushes and flushes are emitted once per call)
+    auto win_expand = [&]() {
+        const int n = wqn;
+        wqn = 0;
+#pragma unroll 1
+        for (int i = 0; i < EPP; ++i) {
+            const float h = lane < n ? sh.wq[wv][lane][i] : __builtin_nanf("");
+            win_push(h);
+        }
+    };
+
     // ids [lo, hi) cover every element of pieces 1 .. nq-2; only the first and the
     // last iteration can hold a partial or missing piece
     // raw 16-byte pieces of one group (u only when it is read)
@@ -591,6 +736,49 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
 #pragma unroll
             for (int i = 1; i < EPP; ++i) pm[uu] = __builtin_fmaxf(pm[uu], P[uu].h[i]);
             gm = __builtin_fmaxf(gm, pm[uu]);
+        }
+        if constexpr (WIN) {
+            if (wc.on) {
+                // ids above the window are counted per wave; a piece with an id
+                // inside it is queued whole (ids outside the part as NaN) and its
+                // ids are sorted out 64 pieces at a time, which keeps the per-id
+                // work to two compares
+#pragma unroll
+                for (int uu = 0; uu < U; ++uu) {
+                    const int j = it * NT * U + uu * NT + (int)threadIdx.x;
+                    const int v0 = vbase + j * EPP;
+                    // lane masks straight from the compares (a bool taken through
+                    // ballot() would be turned into a 0/1 value and compared again)
+                    uint64_t any = 0;
+#pragma unroll
+                    for (int i = 0; i < EPP; ++i) {
+                        const float h = P[uu].h[i];
+                        const uint64_t gt = __builtin_amdgcn_ballot_w64(h > wc.hi);
+                        wabove += popc(gt);
+                        uint64_t in = __builtin_amdgcn_ballot_w64(h >= wc.lo) & ~gt;
+                        // ids outside the part hold -inf here: never inside
+                        if (EDGE) in &= __builtin_amdgcn_ballot_w64(j < nqi && v0 + i >= pr.lo && v0 + i < pr.hi);
+                        any |= in;
+                    }
+                    if (any) {
+                        const int add = popc(any);
+                        if (wqn + add > kWave) {
+                            __builtin_amdgcn_wave_barrier();
+                            win_expand();
+                            __builtin_amdgcn_wave_barrier();
+                        }
+                        if ((any >> lane) & 1ull) {
+                            float* dst = sh.wq[wv][wqn + lanes_below(any)];
+#pragma unroll
+                            for (int i = 0; i < EPP; ++i) {
+                                const bool ok = !EDGE || (j < nqi && v0 + i >= pr.lo && v0 + i < pr.hi);
+                                dst[i] = ok ? P[uu].h[i] : __builtin_nanf("");
+                            }
+                        }
+                        wqn += add;
+                    }
+                }
+            }
         }
         if (gm > m) {
             // first piece, then first id, holding the new maximum (ids grow with
@@ -697,6 +885,12 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
             }
         }
     }
+    if (WIN && wc.on) {
+        __builtin_amdgcn_wave_barrier();
+        if (wqn > 0) win_expand();
+        __builtin_amdgcn_wave_barrier();
+        if (wn > 0) win_flush(wn);
+    }
     // wave shares, then one exchange through LDS; thread 0 combines them
     const float wm = wave_max(m);
     const float ws = wave_sum((m > kNegInf) ? acc * __builtin_amdgcn_exp2f((m - wm) * kLog2e) : 0.0f);
@@ -705,7 +899,8 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
         const int wl = wave_argmax(bz, be);
         bh = readlane_f(bh, wl);
     }
-    if (lane == 0) sh.r.w[wv] = WaveRec{wm, ws, wid, bz, bh, be, qtot, 0};
+    const int wab = WIN ? wabove : 0;
+    if (lane == 0) sh.r.w[wv] = WaveRec{wm, ws, wid, bz, bh, be, qtot, wab};
     __syncthreads();
     PartOut o;
     o.nan = false;
@@ -720,6 +915,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
     o.bh = kNegInf;
     o.be = 0x7FFFFFFF;
     o.nq = 0;
+    o.above = 0;
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int i = 0; i < NWAVES; ++i) o.m = __builtin_fmaxf(o.m, sh.r.w[i].m);
@@ -738,6 +934,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
                 }
                 o.nq += r.nq;
             }
+            o.above += r.above;
         }
     }
     return o;
@@ -768,21 +965,36 @@ __device__ __forceinline__ const void* cell_u(const void* uptr, const CellParams
 }
 
 // Kernel 1 body: stream part `part` of the row and write its partial record.
-template <bool BF16, bool SAMPLE>
+// With WIN the part also takes its share of the row's threshold window; it then
+// streams with masked ids already mapped to -inf (FIX), since appended keys
+// cannot be taken back by a second pass.
+template <bool BF16, bool SAMPLE, bool WIN = false>
 __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bool force_fallback,
                           const RowWork& w, const CellParams& cp, int64_t slot, int part) {
-    __shared__ PartLDS<BF16, SAMPLE> sh;
+    __shared__ PartLDS<BF16, SAMPLE, WIN> sh;
     const int j = part / w.ppc;
     const int q = part - j * w.ppc;
     const bool use_u = SAMPLE && cp.s != 0.0f;
     const bool race = SAMPLE && cp.tau != 0.0f && !force_fallback;
     const RowGeom G = row_geom<BF16>(cptr, cell_u(uptr, cp, V, BF16), use_u, cp.cell, V, nch, w.ppc);
     const PartRange<BF16> pr(G, j, q);
-    PartOut po = stream_part<BF16, SAMPLE, false>(G, pr, cp, use_u, race, sh);
-    if (po.nan) {
-        // a masked id under guidance: stream the part again with h = -inf there
-        __syncthreads();
-        po = stream_part<BF16, SAMPLE, true>(G, pr, cp, use_u, race, sh);
+    WinCtx wc{false, 0.0f, 0.0f, nullptr, nullptr};
+    PartOut po;
+    if constexpr (WIN) {
+        const WinRec wr = w.win[slot];
+        wc.on = wr.lo <= wr.hi;
+        wc.lo = window_lo(wr.lo);
+        wc.hi = window_hi(wr.hi);
+        wc.keys = w.keys + slot * kWinKeysPerRow;
+        wc.count = &w.win[slot].count;
+        po = stream_part<BF16, SAMPLE, true, true>(G, pr, cp, use_u, race, sh, wc);
+    } else {
+        po = stream_part<BF16, SAMPLE, false, false>(G, pr, cp, use_u, race, sh, wc);
+        if (po.nan) {
+            // a masked id under guidance: stream the part again with h = -inf there
+            __syncthreads();
+            po = stream_part<BF16, SAMPLE, true, false>(G, pr, cp, use_u, race, sh, wc);
+        }
     }
     if (threadIdx.x == 0) {
         PartRec* rec = w.part + slot * w.nparts + part;
@@ -793,13 +1005,37 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
         rec->bz = po.bz;
         rec->be = po.be;
         rec->bh = po.bh;
+        rec->above = po.above;
     }
+}
+
+// The window kernel's body: the threshold window of a sampled row from a sample
+// of the row (sample_window); greedy rows, and rows too short for a sample to
+// pay, get none.  The row's key count starts at 0.
+template <bool BF16>
+__device__ void window_body(const void* cptr, const void* uptr, int V, int k, const RowWork& w, const CellParams& cp,
+                            int64_t slot) {
+    __shared__ MergeLDS<kWindowThreads, kKeyCapExact> sh;
+    uint32_t lo = 1u, hi = 0u;  // no window
+    if (cp.tau != 0.0f) {
+        const bool use_u = cp.s != 0.0f;
+        const RowGeom G = row_geom<BF16>(cptr, cell_u(uptr, cp, V, BF16), use_u, cp.cell, V, 1, 1);
+        uint32_t a, b;
+        // five standard deviations: with thousands of rows per launch, one row
+        // whose window misses costs its merge a pass over the row, and the launch
+        // waits for its slowest row
+        if (sample_window<BF16>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
+            lo = a;
+            hi = b;
+        }
+    }
+    if (threadIdx.x == 0) w.win[slot] = WinRec{lo, hi, 0, 0};
 }
 
 // Kernel 2 body: merge the row's partial records ([DRAFT]: larger max wins,
 // equal maxima keep the smaller id, sums add in probability space), then finish
 // the greedy or sampled decision.
-template <bool BF16, bool SAMPLE, int MT_, int KCAP>
+template <bool BF16, bool SAMPLE, int MT_, int KCAP, bool WIN = false>
 __device__ __forceinline__ void merge_body(const void* cptr, const void* uptr, int V, int nch, int top_k, bool force_fallback,
                            const RowWork& w, const CellParams& cp, int64_t slot, int* tokens, float* logprobs,
                            float* lse_out, float* thresholds, float* triples, int64_t n_rows) {
@@ -812,7 +1048,7 @@ __device__ __forceinline__ void merge_body(const void* cptr, const void* uptr, i
     // race winners of the parts
     float bz = kNegInf, bh = kNegInf;
     int be = 0x7FFFFFFF;
-    int64_t queued = 0;
+    int64_t queued = 0, above = 0;
     bool raced = sampled && !force_fallback;
     // records in chunk-major order, staged through LDS kMergeStage at a time
     float mj = kNegInf, sj = 0.0f;
@@ -825,6 +1061,7 @@ __device__ __forceinline__ void merge_body(const void* cptr, const void* uptr, i
         for (int i = 0; i < n; ++i) {
             const int p = t0 + i;
             const PartRec r = sh.u.rec[i];
+            if (WIN) above += r.above;
             if (sampled) {
                 raced &= r.nq >= 0;
                 queued += r.nq;
@@ -881,7 +1118,19 @@ __device__ __forceinline__ void merge_body(const void* cptr, const void* uptr, i
     bool done = raced && queued <= (int64_t)k;
     float t = kNegInf;
     const RowGeom G = row_geom<BF16>(cptr, cell_u(uptr, cp, V, BF16), use_u, cp.cell, V, nch, w.ppc);
-    if (!done || thresholds) t = radix_select_row<BF16>(G, cp.s, use_u, k, sh);
+    bool have_t = false;
+    if constexpr (WIN) {
+        // the parts counted the keys above the row's window and appended those
+        // inside it: when the top_k-th largest falls inside and every key was
+        // kept, it is selected among them in LDS, with no pass over the row
+        const WinRec wr = w.win[slot];
+        const int n = wr.count;
+        if (wr.lo <= wr.hi && n <= kWinKeysPerRow && above < (int64_t)k && (int64_t)k <= above + n) {
+            t = key_value(window_kth(sh, w.keys + slot * kWinKeysPerRow, n, k - (int)above, wr.lo, wr.hi - wr.lo));
+            have_t = true;
+        }
+    }
+    if (!have_t && (!done || thresholds)) t = radix_select_row<BF16>(G, cp.s, use_u, k, sh);
     done = done || (raced && bz > kNegInf && bh >= t);
     if (!done) {
         // exact pass over the kept ids that can beat the argmax
@@ -962,36 +1211,51 @@ __device__ __forceinline__ CellParams greedy_cell(const GreedyArgs& a, int64_t s
 // workgroups stream neighbouring memory.  The greedy parts kernel keeps to 64
 // VGPRs (four workgroups per CU); the sampled one may take 80 (three), which the
 // race's noise code needs without spilling.
-template <bool BF16>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_sample_parts(SampleArgs a, ReqTable rq) {
+// The parts kernels keep to 80 VGPRs (six waves per SIMD, three workgroups per
+// compute unit); with the threshold window they may take 128 (two workgroups),
+// which its per-id tests need without spilling.
+template <bool BF16, bool WIN>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIN ? 4 : 6, 8))) void k_sample_parts(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x / a.w.nparts;
     const int part = (int)(blockIdx.x - slot * a.w.nparts);
-    part_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot), slot,
-                          part);
+    part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot),
+                               slot, part);
 }
-template <bool BF16, int MT_, int KCAP>
+template <bool BF16, int MT_, int KCAP, bool WIN>
 __global__ __launch_bounds__(MT_) void k_sample_merge(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x;
-    merge_body<BF16, true, MT_, KCAP>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
-                                      sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr, a.thresholds,
-                                      nullptr, 0);
+    merge_body<BF16, true, MT_, KCAP, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
+                                           sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr,
+                                           a.thresholds, nullptr, 0);
 }
-// The same two kernels with the per-request parameters in device memory.
 template <bool BF16>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_sample_parts_dev(SampleArgs a, DevReq d) {
+__global__ __launch_bounds__(kWindowThreads) void k_sample_window(SampleArgs a, ReqTable rq) {
+    const int64_t slot = blockIdx.x;
+    window_body<BF16>(a.c, a.u, a.V, a.top_k, a.w, sample_cell(a, rq, slot), slot);
+}
+// The same kernels with the per-request parameters in device memory.
+template <bool BF16, bool WIN>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIN ? 4 : 6, 8))) void k_sample_parts_dev(SampleArgs a, DevReq d) {
     const int64_t slot = blockIdx.x / a.w.nparts;
     const int part = (int)(blockIdx.x - slot * a.w.nparts);
     CellParams cp;
     if (!sample_cell_dev(a, d, slot, cp)) return;
-    part_body<BF16, true>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part);
+    part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part);
 }
-template <bool BF16, int MT_, int KCAP>
+template <bool BF16, int MT_, int KCAP, bool WIN>
 __global__ __launch_bounds__(MT_) void k_sample_merge_dev(SampleArgs a, DevReq d) {
     const int64_t slot = blockIdx.x;
     CellParams cp;
     if (!sample_cell_dev(a, d, slot, cp)) return;
-    merge_body<BF16, true, MT_, KCAP>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w, cp, slot,
-                                      a.tokens, a.logprobs, nullptr, a.thresholds, nullptr, 0);
+    merge_body<BF16, true, MT_, KCAP, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w, cp,
+                                           slot, a.tokens, a.logprobs, nullptr, a.thresholds, nullptr, 0);
+}
+template <bool BF16>
+__global__ __launch_bounds__(kWindowThreads) void k_sample_window_dev(SampleArgs a, DevReq d) {
+    const int64_t slot = blockIdx.x;
+    CellParams cp;
+    if (!sample_cell_dev(a, d, slot, cp)) return;  // padding: its parts and merge leave too
+    window_body<BF16>(a.c, a.u, a.V, a.top_k, a.w, cp, slot);
 }
 template <bool BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_greedy_parts(GreedyArgs a) {
@@ -1257,55 +1521,61 @@ int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells) {
     return (int)(p < 1 ? 1 : p);
 }
 
-hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
+namespace {
+
+// The kernels of one streaming launch: with the threshold output and a window
+// workspace, the window kernel first and the parts and merge kernels with the
+// window; otherwise parts and merge, the merge in its exact shape whenever every
+// row selects its threshold.
+template <bool BF16, typename Src, typename KW, typename KP, typename KPW, typename KM, typename KME, typename KMEW>
+hipError_t launch_row(const SampleArgs& a, const Src& src, hipStream_t st, KW kwin, KP kparts, KPW kparts_win,
+                      KM kmerge, KME kmerge_exact, KMEW kmerge_exact_win) {
     const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
     if (parts == 0) return hipSuccess;
     const dim3 mg((unsigned)a.w.ncells);
     const bool exact = a.thresholds != nullptr || a.force_fallback != 0;  // every row selects its threshold
-    if (bf16) {
-        hipLaunchKernelGGL(k_sample_parts<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
-        if (exact)
-            hipLaunchKernelGGL((k_sample_merge<true, kMergeThreadsExact, kKeyCapExact>), mg, dim3(kMergeThreadsExact),
-                               0, st, a, rq);
-        else
-            hipLaunchKernelGGL((k_sample_merge<true, kMergeThreadsFast, kKeyCapFast>), mg, dim3(kMergeThreadsFast), 0,
-                               st, a, rq);
+    const bool win = a.thresholds != nullptr && a.force_fallback == 0 && a.w.win != nullptr && a.w.keys != nullptr;
+    if (win) {
+        hipLaunchKernelGGL(kwin, mg, dim3(kWindowThreads), 0, st, a, src);
+        hipLaunchKernelGGL(kparts_win, dim3((unsigned)parts), dim3(NT), 0, st, a, src);
+        hipLaunchKernelGGL(kmerge_exact_win, mg, dim3(kMergeThreadsExact), 0, st, a, src);
     } else {
-        hipLaunchKernelGGL(k_sample_parts<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, rq);
+        hipLaunchKernelGGL(kparts, dim3((unsigned)parts), dim3(NT), 0, st, a, src);
         if (exact)
-            hipLaunchKernelGGL((k_sample_merge<false, kMergeThreadsExact, kKeyCapExact>), mg,
-                               dim3(kMergeThreadsExact), 0, st, a, rq);
+            hipLaunchKernelGGL(kmerge_exact, mg, dim3(kMergeThreadsExact), 0, st, a, src);
         else
-            hipLaunchKernelGGL((k_sample_merge<false, kMergeThreadsFast, kKeyCapFast>), mg, dim3(kMergeThreadsFast),
-                               0, st, a, rq);
+            hipLaunchKernelGGL(kmerge, mg, dim3(kMergeThreadsFast), 0, st, a, src);
     }
     return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq, hipStream_t st) {
+    if (bf16)
+        return launch_row<true>(a, rq, st, k_sample_window<true>, k_sample_parts<true, false>,
+                                k_sample_parts<true, true>, k_sample_merge<true, kMergeThreadsFast, kKeyCapFast, false>,
+                                k_sample_merge<true, kMergeThreadsExact, kKeyCapExact, false>,
+                                k_sample_merge<true, kMergeThreadsExact, kKeyCapExact, true>);
+    return launch_row<false>(a, rq, st, k_sample_window<false>, k_sample_parts<false, false>,
+                             k_sample_parts<false, true>, k_sample_merge<false, kMergeThreadsFast, kKeyCapFast, false>,
+                             k_sample_merge<false, kMergeThreadsExact, kKeyCapExact, false>,
+                             k_sample_merge<false, kMergeThreadsExact, kKeyCapExact, true>);
+}
+
 hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st) {
-    const int64_t parts = (int64_t)a.w.ncells * a.w.nparts;
-    if (parts == 0) return hipSuccess;
     if (d.n < 1 || (d.n > kWave && !d.one_per_request) || d.P < 1) return hipErrorInvalidValue;
-    const dim3 mg((unsigned)a.w.ncells);
-    const bool exact = a.thresholds != nullptr || a.force_fallback != 0;  // every row selects its threshold
-    if (bf16) {
-        hipLaunchKernelGGL(k_sample_parts_dev<true>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
-        if (exact)
-            hipLaunchKernelGGL((k_sample_merge_dev<true, kMergeThreadsExact, kKeyCapExact>), mg,
-                               dim3(kMergeThreadsExact), 0, st, a, d);
-        else
-            hipLaunchKernelGGL((k_sample_merge_dev<true, kMergeThreadsFast, kKeyCapFast>), mg,
-                               dim3(kMergeThreadsFast), 0, st, a, d);
-    } else {
-        hipLaunchKernelGGL(k_sample_parts_dev<false>, dim3((unsigned)parts), dim3(NT), 0, st, a, d);
-        if (exact)
-            hipLaunchKernelGGL((k_sample_merge_dev<false, kMergeThreadsExact, kKeyCapExact>), mg,
-                               dim3(kMergeThreadsExact), 0, st, a, d);
-        else
-            hipLaunchKernelGGL((k_sample_merge_dev<false, kMergeThreadsFast, kKeyCapFast>), mg,
-                               dim3(kMergeThreadsFast), 0, st, a, d);
-    }
-    return hipGetLastError();
+    if (bf16)
+        return launch_row<true>(a, d, st, k_sample_window_dev<true>, k_sample_parts_dev<true, false>,
+                                k_sample_parts_dev<true, true>,
+                                k_sample_merge_dev<true, kMergeThreadsFast, kKeyCapFast, false>,
+                                k_sample_merge_dev<true, kMergeThreadsExact, kKeyCapExact, false>,
+                                k_sample_merge_dev<true, kMergeThreadsExact, kKeyCapExact, true>);
+    return launch_row<false>(a, d, st, k_sample_window_dev<false>, k_sample_parts_dev<false, false>,
+                             k_sample_parts_dev<false, true>,
+                             k_sample_merge_dev<false, kMergeThreadsFast, kKeyCapFast, false>,
+                             k_sample_merge_dev<false, kMergeThreadsExact, kKeyCapExact, false>,
+                             k_sample_merge_dev<false, kMergeThreadsExact, kKeyCapExact, true>);
 }
 
 bool greedy_rows_fits(bool bf16, int V, int chunks, const void* x) {
