@@ -98,10 +98,12 @@ def test_stress_full_size_sampled_cells_and_chunk_equality():
     del c, u
     torch.cuda.empty_cache()
     # the four-chunk result equals the dense single-pass result in every cell, and
-    # asking for the threshold changes no draw
+    # asking for the threshold changes no draw (its parts kernel adds the exp-sum
+    # in another order, so the logprobs agree to rounding)
     assert np.array_equal(got4[0], got1[0])
     assert np.max(np.abs(got4[1] - got1[1])) <= 1e-5
-    assert np.array_equal(got4t[0], got4[0]) and np.array_equal(got4t[1], got4[1])
+    assert np.array_equal(got4t[0], got4[0])
+    assert np.max(np.abs(got4t[1] - got4[1])) <= 1e-5
     # 256 evenly spaced cells against the oracle: tokens, logprobs and the
     # top-ratio threshold (k = ceil(0.1 * V) = 24832) bit for bit
     cells = np.linspace(0, w.cells - 1, 256).astype(np.int64)

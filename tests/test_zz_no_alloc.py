@@ -1,10 +1,15 @@
 """ds_sample_static (the entry point that allocates nothing) against ds_sample.
 
 Both run the same kernels; the static one keeps the streaming kernels' records
-in the library's fixed device array instead of a handle's workspace.  Each case
-calls the two entry points through the C ABI, twice in a row with the second
-input smaller (so the second static call finds the first call's records in the
-shared array), and requires identical tokens, logprobs and thresholds.  The
+in the library's fixed device array instead of a handle's workspace.  With the
+threshold output on a long row ds_sample also uses its handle's threshold
+windows (a parts kernel of another workgroup size), which the static entry point
+has no memory for: it takes the exact passes instead, so there the logprobs,
+summed in another order, agree to rounding.  Each case calls the two entry
+points through the C ABI, twice in a row with the second input smaller (so the
+second static call finds the first call's records in the shared array), and
+requires identical tokens and thresholds and logprobs identical or, on that
+one path, within 1e-5.  The
 streaming path (V = 248320 and V = 60000, which use the array) and the
 wave-per-cell path (V = 1025, which does not) are both covered, as is the forced
 multi-pass path.
@@ -66,9 +71,12 @@ def _pair(w, *, threshold, flags):
     return [t.cpu().numpy() for t in ref if t is not None], [t.cpu().numpy() for t in got if t is not None]
 
 
-def _assert_same(ref, got, what):
+def _assert_same(ref, got, what, exact_logprobs):
     for a, b, name in zip(ref, got, ("tokens", "logprobs", "thresholds")):
-        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{what}: {name} differ"
+        if name == "logprobs" and not exact_logprobs:
+            assert np.max(np.abs(a - b), initial=0.0) <= 1e-5, f"{what}: {name} differ"
+        else:
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{what}: {name} differ"
     assert (got[0] >= 0).all(), f"{what}: a cell was not written"
 
 
@@ -89,7 +97,9 @@ def test_static_entry_point_equals_ds_sample_twice_second_smaller(flags):
         assert small.cells < big.cells
         for w, thr in ((big, True), (small, True), (big, False), (small, False)):
             ref, got = _pair(w, threshold=thr, flags=flags)
-            _assert_same(ref, got, f"{w.name} threshold={thr}")
+            # the handle's threshold windows: long rows, threshold output, not forced
+            windows = thr and flags == 0 and w.vocab > 1025
+            _assert_same(ref, got, f"{w.name} threshold={thr}", exact_logprobs=not windows)
 
 
 def test_static_entry_point_rejects_bad_settings_before_launch():

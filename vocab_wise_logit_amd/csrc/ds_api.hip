@@ -126,18 +126,19 @@ SamplerCfg cfg_of(const ds_sampler* s) {
                       s->ws_win,   s->ws_keys,      s->win_rows};
 }
 
-// Rows per streaming launch, and the window buffers it uses: with the threshold
-// output and window buffers, as many rows as they hold (and the records allow).
-int64_t stream_slots(ds::SampleArgs& a, ds::WinRec* win, uint32_t* keys, int64_t win_rows) {
+// Parts per chunk and rows per streaming launch, and the window buffers it
+// uses.  With the threshold output and window buffers the parts kernel that
+// takes the window runs (smaller workgroups, so more parts of a row), and a
+// launch holds as many rows as the buffers do (and the records allow).
+int64_t stream_layout(ds::SampleArgs& a, bool bf16, int32_t vocab, int32_t chunks, int64_t cells, ds::WinRec* win,
+                      uint32_t* keys, int64_t win_rows) {
+    const bool use_win = a.thresholds && !a.force_fallback && win && keys && win_rows > 0;
+    a.w.ppc = ds::row_parts_per_chunk(bf16, vocab, chunks, cells, use_win);
+    a.w.nparts = a.w.ppc * chunks;
     int64_t slots = ds::kWorkParts / a.w.nparts;
-    if (a.thresholds && !a.force_fallback && win && keys && win_rows > 0) {
-        a.w.win = win;
-        a.w.keys = keys;
-        if (slots > win_rows) slots = win_rows;
-    } else {
-        a.w.win = nullptr;
-        a.w.keys = nullptr;
-    }
+    a.w.win = use_win ? win : nullptr;
+    a.w.keys = use_win ? keys : nullptr;
+    if (use_win && slots > win_rows) slots = win_rows;
     return slots;
 }
 
@@ -183,9 +184,7 @@ int launch_dev_params(ds_sampler* s, ds::SampleArgs& a, const ds::DevReq& d, int
     // the streaming kernels over every cell of the fixed layout, in batches that
     // fit the workspace; padding cells leave at once
     const int64_t cells = (int64_t)num_rows * positions;
-    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, cells);
-    a.w.nparts = a.w.ppc * s->vocab_chunks;
-    const int64_t slots = stream_slots(a, s->ws_win, s->ws_keys, s->win_rows);
+    const int64_t slots = stream_layout(a, bf16, s->vocab, s->vocab_chunks, cells, s->ws_win, s->ws_keys, s->win_rows);
     for (int64_t c0 = 0; c0 < cells; c0 += slots) {
         a.w.cell_base = c0;
         a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
@@ -406,9 +405,7 @@ int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids
         } else {
             // the streaming kernel: cells in batches that fit the workspace
             const int64_t cells = (int64_t)num_rows * rel;
-            a.w.ppc = ds::row_parts_per_chunk(bf16, s.vocab, s.vocab_chunks, cells);
-            a.w.nparts = a.w.ppc * s.vocab_chunks;
-            const int64_t slots = stream_slots(a, s.win, s.keys, s.win_rows);
+            const int64_t slots = stream_layout(a, bf16, s.vocab, s.vocab_chunks, cells, s.win, s.keys, s.win_rows);
             for (int64_t c0 = 0; c0 < cells; c0 += slots) {
                 a.w.cell_base = c0;
                 a.w.ncells = (int32_t)(cells - c0 < slots ? cells - c0 : slots);
@@ -589,7 +586,7 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
         if (e != hipSuccess) return hip_fail(e, "greedy kernel launch");
         return DS_OK;
     }
-    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, n_rows);
+    a.w.ppc = ds::row_parts_per_chunk(bf16, s->vocab, s->vocab_chunks, n_rows, false);
     a.w.nparts = a.w.ppc * s->vocab_chunks;
     const int64_t slots = ds::kWorkParts / a.w.nparts;
     for (int64_t c0 = 0; c0 < n_rows; c0 += slots) {

@@ -39,6 +39,7 @@ struct Cand {
     int e;
 };
 constexpr int kRowThreads = 512;
+constexpr int kRowThreadsWin = 128;   // the parts kernel with the threshold window
 constexpr int kRowU = 4;            // 16-byte pieces per thread per group
 constexpr int kWorkParts = 16384;   // parts the workspace holds per launch
 
@@ -94,7 +95,7 @@ struct GreedyArgs {
 };
 
 // Parts per chunk for a launch of `cells` rows (see ds_row.hip).
-int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells);
+int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells, bool window);
 
 hipError_t launch_greedy_lse(bool bf16, const GreedyArgs& a, hipStream_t st);
 

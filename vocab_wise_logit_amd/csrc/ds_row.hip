@@ -41,6 +41,13 @@ namespace {
 constexpr int NT = kRowThreads;
 constexpr int NWAVES = NT / kWave;
 constexpr int U = kRowU;
+// The parts kernel with the threshold window runs smaller workgroups: its
+// per-wave work at the ends of a part (the first group's race bound, the queue
+// drains) is then spread over four times as many groups.
+template <bool WIN>
+constexpr int kPartThreads = WIN ? kRowThreadsWin : kRowThreads;
+template <bool WIN>
+constexpr int kPartWaves = kPartThreads<WIN> / kWave;
 
 // One wave's share of a part: (max, exp-sum, argmax) and its race winner.
 struct WaveRec {
@@ -61,7 +68,6 @@ struct RedT {
     uint32_t bcast_u;
     int bcast_i;
 };
-using Red = RedT<NWAVES>;
 
 // A sampled part's Gumbel race queues, per wave: pieces holding an id at or
 // above the bound (their decoded h and first id), and ids at or above the bound.
@@ -71,16 +77,17 @@ template <bool BF16, bool SAMPLE, bool WIN = false>
 struct PartLDS {
     static constexpr int EPP = BF16 ? 8 : 4;
     static constexpr int kQ = SAMPLE ? 2 * kWave : 1;
-    float ph[NWAVES][kQ][EPP];
-    int pv[NWAVES][kQ];
-    Cand q[NWAVES][kQ];
+    static constexpr int NW = kPartWaves<WIN>;
+    float ph[NW][kQ][EPP];
+    int pv[NW][kQ];
+    Cand q[NW][kQ];
     // threshold window: pieces holding an id inside it (up to 64 per wave, ids
     // outside the part as NaN), and the h (raw bits) of those ids, staged per wave
     // and written to the row's key buffer 64 at a time
-    float wq[NWAVES][WIN ? kWave : 1][EPP];
-    uint32_t wk[NWAVES][WIN ? 2 * kWave : 1];
+    float wq[NW][WIN ? kWave : 1][EPP];
+    uint32_t wk[NW][WIN ? 2 * kWave : 1];
     uint32_t bkey;  // order key of the block's race bound (only grows)
-    Red r;
+    RedT<NW> r;
 };
 
 // What a part needs to know about its row's threshold window.
@@ -588,6 +595,8 @@ template <bool BF16, bool SAMPLE, bool FIX, bool WIN>
 __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, const CellParams& cp, bool use_u,
                                bool race, PartLDS<BF16, SAMPLE, WIN>& sh, const WinCtx& wc) {
     constexpr int EPP = Piece<BF16>::EPP;
+    constexpr int NT = kPartThreads<WIN>;
+    constexpr int NWAVES = kPartWaves<WIN>;
     const float s = cp.s;
     float m = kNegInf, acc = 0.0f;
     int mid = 0x7FFFFFFF;  // smallest id of this thread attaining m
@@ -1215,7 +1224,7 @@ __device__ __forceinline__ CellParams greedy_cell(const GreedyArgs& a, int64_t s
 // compute unit); with the threshold window they may take 128 (two workgroups),
 // which its per-id tests need without spilling.
 template <bool BF16, bool WIN>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIN ? 4 : 6, 8))) void k_sample_parts(SampleArgs a, ReqTable rq) {
+__global__ __launch_bounds__(kPartThreads<WIN>) __attribute__((amdgpu_waves_per_eu(WIN ? 4 : 6, 8))) void k_sample_parts(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x / a.w.nparts;
     const int part = (int)(blockIdx.x - slot * a.w.nparts);
     part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot),
@@ -1235,7 +1244,7 @@ __global__ __launch_bounds__(kWindowThreads) void k_sample_window(SampleArgs a, 
 }
 // The same kernels with the per-request parameters in device memory.
 template <bool BF16, bool WIN>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIN ? 4 : 6, 8))) void k_sample_parts_dev(SampleArgs a, DevReq d) {
+__global__ __launch_bounds__(kPartThreads<WIN>) __attribute__((amdgpu_waves_per_eu(WIN ? 4 : 6, 8))) void k_sample_parts_dev(SampleArgs a, DevReq d) {
     const int64_t slot = blockIdx.x / a.w.nparts;
     const int part = (int)(blockIdx.x - slot * a.w.nparts);
     CellParams cp;
@@ -1508,12 +1517,13 @@ __global__ __launch_bounds__(kGreedyRowThreads) void k_greedy_rows(GreedyArgs a)
 
 }  // namespace
 
-int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells) {
+int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells, bool window) {
     const int epp = bf16 ? 8 : 4;
     const int64_t L = ((int64_t)V + chunks - 1) / chunks;
     const int64_t pieces = L / epp + 2;
-    // enough workgroups to cover the GPU several times over, parts of >= 1024 pieces
-    const int64_t target = 1024;
+    // enough waves to cover the GPU several times over (8192: 1024 workgroups of
+    // the plain parts kernel), parts of >= 1024 pieces
+    const int64_t target = 8192 / (window ? kPartWaves<true> : kPartWaves<false>);
     int64_t p = (target + cells * chunks - 1) / (cells * chunks);
     const int64_t p_cap = pieces / 1024 > 1 ? pieces / 1024 : 1;
     if (p > p_cap) p = p_cap;
@@ -1537,7 +1547,7 @@ hipError_t launch_row(const SampleArgs& a, const Src& src, hipStream_t st, KW kw
     const bool win = a.thresholds != nullptr && a.force_fallback == 0 && a.w.win != nullptr && a.w.keys != nullptr;
     if (win) {
         hipLaunchKernelGGL(kwin, mg, dim3(kWindowThreads), 0, st, a, src);
-        hipLaunchKernelGGL(kparts_win, dim3((unsigned)parts), dim3(NT), 0, st, a, src);
+        hipLaunchKernelGGL(kparts_win, dim3((unsigned)parts), dim3(kPartThreads<true>), 0, st, a, src);
         hipLaunchKernelGGL(kmerge_exact_win, mg, dim3(kMergeThreadsExact), 0, st, a, src);
     } else {
         hipLaunchKernelGGL(kparts, dim3((unsigned)parts), dim3(NT), 0, st, a, src);
