@@ -456,7 +456,10 @@ __device__ __forceinline__ ReqParams req_params(const ReqTable& rq, int r) {
     return q;
 }
 
-// The request owning launch-relative position pl: the last r with offs[r] <= pl.
+// The request owning launch-relative position pl: the last r with offs[r] <= pl,
+// by a binary search of scalar loads from the kernel arguments (they hit the
+// scalar cache; one vector load of every start per wave measured no faster, its
+// memory round trip delaying a guided cell's u loads).
 __device__ __forceinline__ int find_request(const ReqTable& rq, int pl) {
     int lo = 0, hi = rq.n - 1;
     while (lo < hi) {

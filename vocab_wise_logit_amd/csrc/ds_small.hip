@@ -82,32 +82,39 @@ struct Row {
     __device__ __forceinline__ int count_ge(float x) const {
         int n = 0;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) n += popc(ballot(h[i] >= x));
+        for (int i = 0; i < NE; ++i) n += popc(__builtin_amdgcn_ballot_w64(h[i] >= x));
         return n;
     }
 
-    // Count the ids whose h is >= x and, if there are at most `cap` (<= kListCap)
-    // of them, write them to `list` as (h, id).  Each lane counts its own ids, a
-    // wave prefix sum places each lane's run, and the lane writes its ids there in
-    // register order.  Every lane stores every slot, the ids below x to its own
-    // spare entry past kListCap, so the pass has no per-slot ballot or branch.
-    // Returns the count.
-    __device__ __forceinline__ int count_compact(float x, Entry* list, int lane, int cap = kListCap) const {
-        int mine = 0;
+    // Write the ids whose h is >= x to `list` as (h, id) in slot order (slot i's
+    // ids after those of slot i - 1, in lane order within a slot): one ballot per
+    // slot gives its count, and mbcnt on it, started at the running count, each
+    // id's place.  A slot that would take the list past `cap` (<= kListCap)
+    // entries is not written, so the list holds every such id exactly when the
+    // returned count is <= cap.
+    __device__ __forceinline__ int write_ge(float x, Entry* list, int cap) const {
+        int base = 0;  // wave-uniform
 #pragma unroll
-        for (int i = 0; i < NE; ++i) mine += (h[i] >= x) ? 1 : 0;
-        const int incl = wave_incl_scan(mine);
-        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        if (total <= cap) {
-            const int spare = kListCap + lane;
-            int o = incl - mine;  // < total for every id this lane writes
-#pragma unroll
-            for (int i = 0; i < NE; ++i) {
-                const bool p = h[i] >= x;
-                list[p ? o : spare] = Entry{h[i], id_of(i)};
-                o += p ? 1 : 0;
+        for (int i = 0; i < NE; ++i) {
+            const bool p = h[i] >= x;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(p);
+            const int nm = popc(m);
+            if (base + nm <= cap && p) {
+                const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)base));
+                list[at] = Entry{h[i], id_of(i)};
             }
+            base += nm;
         }
+        __builtin_amdgcn_wave_barrier();
+        return base;
+    }
+
+    // Count the ids whose h is >= x and, if there are at most `cap` (<= kListCap)
+    // of them, write them to `list` (write_ge).  Returns the count.
+    __device__ __forceinline__ int count_compact(float x, Entry* list, int cap = kListCap) const {
+        const int total = count_ge(x);
+        if (total <= cap) write_ge(x, list, cap);
         __builtin_amdgcn_wave_barrier();
         return total;
     }
@@ -625,7 +632,8 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
     for (int i = 0; i < (NE < 4 ? NE : 4); ++i) sub += popc(ballot(R.h[i] >= prune));
     const bool flat = sub * NE > 6 * cap;  // about 1.5 * cap ids expected
     if (!want_t && !flat) {
-        const int nb = R.count_compact(prune, list, lane, cap);
+        // (written straight away: a row that is not flat rarely has more)
+        const int nb = R.write_ge(prune, list, cap);
         if (nb <= cap) {
             n_list = nb;
             if (nb > k) race_listed(nb, prune);
@@ -639,7 +647,8 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
         float c;
         int n;
         if (top_set_by_histogram(R, list, k, prune, M, lane, c, n) && n <= kListCap) {
-            const int nc = R.count_compact(c, list, lane);
+            // n ids have h >= c, so the list is written without counting first
+            const int nc = R.write_ge(c, list, kListCap);
             if (nc <= kListCap) {
                 n_list = nc;
                 if (!want_t) {
@@ -678,7 +687,7 @@ __device__ __forceinline__ void sample_small_body(const SampleArgs& a, const Src
             have_t = true;
         }
         for (int tries = 0; tries < 8 && !have_t; ++tries) {
-            const int c_lo = R.count_compact(lo, list, lane);
+            const int c_lo = R.count_compact(lo, list);
             if (c_lo >= k && c_lo <= kListCap) {
                 t = list_kth(list, c_lo, k, lo, M, lane);
                 n_list = c_lo;
