@@ -72,19 +72,22 @@ struct RedT {
 // A sampled part's Gumbel race queues, per wave: pieces holding an id at or
 // above the bound (their decoded h and first id), and ids at or above the bound.
 // Each is drained once it holds 64 entries, and one step adds at most 64, so 128
-// entries never overflow.
+// entries never overflow.  The pieces' h are stored element-major ([element]
+// [entry]): a drain reads element i of 64 consecutive entries, one per lane, and
+// with the entries contiguous per element those reads (and the writes) fall on
+// distinct banks.
 template <bool BF16, bool SAMPLE, bool WIN = false>
 struct PartLDS {
     static constexpr int EPP = BF16 ? 8 : 4;
     static constexpr int kQ = SAMPLE ? 2 * kWave : 1;
     static constexpr int NW = kPartWaves<WIN>;
-    float ph[NW][kQ][EPP];
+    float ph[NW][EPP][kQ];
     int pv[NW][kQ];
     Cand q[NW][kQ];
     // threshold window: pieces holding an id inside it (up to 64 per wave, ids
     // outside the part as NaN), and the h (raw bits) of those ids, staged per wave
     // and written to the row's key buffer 64 at a time
-    float wq[NW][WIN ? kWave : 1][EPP];
+    float wq[NW][EPP][WIN ? kWave : 1];
     uint32_t wk[NW][WIN ? 2 * kWave : 1];
     uint32_t bkey;  // order key of the block's race bound (only grows)
     RedT<NW> r;
@@ -643,7 +646,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
         const int v0 = sh.pv[wv][pi];
 #pragma unroll 1
         for (int i = 0; i < EPP; ++i) {
-            const float h = sh.ph[wv][pi][i];
+            const float h = sh.ph[wv][i][pi];
             const bool pred = h >= Bq;
             const uint64_t mk = ballot(pred);
             if (mk) {
@@ -692,7 +695,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
         wqn = 0;
 #pragma unroll 1
         for (int i = 0; i < EPP; ++i) {
-            const float h = lane < n ? sh.wq[wv][lane][i] : __builtin_nanf("");
+            const float h = lane < n ? sh.wq[wv][i][lane] : __builtin_nanf("");
             win_push(h);
         }
     };
@@ -777,11 +780,11 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
                             __builtin_amdgcn_wave_barrier();
                         }
                         if ((any >> lane) & 1ull) {
-                            float* dst = sh.wq[wv][wqn + lanes_below(any)];
+                            const int at = wqn + lanes_below(any);
 #pragma unroll
                             for (int i = 0; i < EPP; ++i) {
                                 const bool ok = !EDGE || (j < nqi && v0 + i >= pr.lo && v0 + i < pr.hi);
-                                dst[i] = ok ? P[uu].h[i] : __builtin_nanf("");
+                                sh.wq[wv][i][at] = ok ? P[uu].h[i] : __builtin_nanf("");
                             }
                         }
                         wqn += add;
@@ -848,7 +851,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
                     if (pred) {
                         const int at = pn + lanes_below(mk);
 #pragma unroll
-                        for (int i = 0; i < EPP; ++i) sh.ph[wv][at][i] = P[uu].h[i];
+                        for (int i = 0; i < EPP; ++i) sh.ph[wv][i][at] = P[uu].h[i];
                         sh.pv[wv][at] = vbase + (it * NT * U + uu * NT + (int)threadIdx.x) * EPP;
                     }
                     pn += popc(mk);
@@ -879,7 +882,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
             if (lane >= take) sh.pv[wv][lane] = 0;
             if (lane >= take)
 #pragma unroll
-                for (int i = 0; i < EPP; ++i) sh.ph[wv][lane][i] = kNegInf;
+                for (int i = 0; i < EPP; ++i) sh.ph[wv][i][lane] = kNegInf;
             __builtin_amdgcn_wave_barrier();
             expand(Bw);
             __builtin_amdgcn_wave_barrier();
