@@ -385,6 +385,11 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
         cfg["workload"] += "+threshold"
         cfg["threshold_out"] = True
     kname = kernel_name(w, kind)
+    launches = launches_per_step(w, kind)
+    if threshold and kname == "k_sample_parts+k_sample_merge":
+        # the threshold output on the streaming path: the window kernel first
+        kname = "k_sample_window+" + kname
+        launches += 1
     if mode in ("device_params", "graph"):
         cfg["workload"] += "+" + mode
         cfg["entry_point"] = "ds_sample_device_params" + (" in a replayed HIP graph" if mode == "graph" else "")
@@ -392,7 +397,7 @@ def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "ea
     elif mode == "compact_u":
         cfg["workload"] += "+compact_u"
         cfg["u_layout"] = "compacted: guided requests' positions only"
-    res = {"config": cfg, "kernel": kname, "launches_per_step": launches_per_step(w, kind),
+    res = {"config": cfg, "kernel": kname, "launches_per_step": launches,
            "steps": steps, "warmup": warmup, "positions_per_s": cells / (ms_step * 1e-3),
            "ms_per_step": ms_step, "call_ms_mean": ms_step, "bracketed_ms_mean": ms_call,
            "bracketed_ms_median": med, "bracketed_ms_p10": p10, "bracketed_ms_p90": p90, "algorithmic_bytes": alg,
@@ -547,6 +552,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="stress")
     ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
+    ap.add_argument("--threshold", action="store_true",
+                    help="time the headline workload with the threshold output (for profiling that path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (10 times), to scale "
@@ -575,10 +582,10 @@ def main() -> int:
 
     print(f"[bench] headline {args.workload}: {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
-    head = bench_one(args.workload, args.steps, args.warmup)
+    head = bench_one(args.workload, args.steps, args.warmup, threshold=args.threshold)
     w = head.pop("workload_obj")
     head_out = head.pop("outputs")
-    traffic = stored_traffic(args.workload)
+    traffic = None if args.threshold else stored_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(head["achieved_GBs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(head["frac_of_peak"], 4),
                 "traffic": traffic,
@@ -601,7 +608,7 @@ def main() -> int:
         # the mixed batch with u holding only the guided requests' positions
         runs += [("mixed", False, "compact_u")]
         for name, thr, mode in runs:
-            if name == args.workload and not thr and mode == "eager":
+            if name == args.workload and thr == args.threshold and mode == "eager":
                 res = dict(head, outputs=head_out)
             else:
                 print(f"[bench] {name} threshold={thr} mode={mode}", file=sys.stderr, flush=True)
