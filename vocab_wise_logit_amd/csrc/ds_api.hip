@@ -292,10 +292,17 @@ namespace {
 
 // ds_sample's checks and launches, for a handle's settings or the handle-free
 // entry point's; ws is the streaming kernels' record workspace.
-int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids, const void* c_logits,
-                const void* u_logits, const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
-                const float* temperature, int32_t num_requests, int32_t num_rows, uint64_t seed, int32_t* tokens_out,
-                float* logprobs_out, float* threshold_out, void* stream) {
+// What a valid call asks for, found by check_call.
+struct CallShape {
+    int64_t P, Pu;   // positions, and positions whose requests read u
+    bool need_u, compact_u, small, bf16;
+};
+
+// Every argument check of a sampling call, before anything touches the device.
+int check_call(const SamplerCfg& s, const int64_t* request_ids, const void* c_logits, const void* u_logits,
+               const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale, const float* temperature,
+               int32_t num_requests, int32_t num_rows, const int32_t* tokens_out, const float* logprobs_out,
+               const float* threshold_out, CallShape& sh) {
     if (!request_ids || !seq_lens || !iterations || !guidance_scale || !temperature)
         return fail(DS_ERR_INVALID_ARG, "a per-request host array is NULL");
     if (!c_logits || !tokens_out || !logprobs_out)
@@ -338,6 +345,22 @@ int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids
                        ds::small_slots_needed(bf16, s.vocab) <= (bf16 ? ds::kSmallMaxSlotsBf16 : ds::kSmallMaxSlotsF32);
     if (compact_u && need_u && !small && ((int64_t)s.vocab * (int64_t)es) % 16 != 0)
         return fail(DS_ERR_UNSUPPORTED, "a compacted u layout needs V * %d bytes to be a multiple of 16 here", (int)es);
+    sh = CallShape{P, Pu, need_u, compact_u, small, bf16};
+    return DS_OK;
+}
+
+int sample_call(const SamplerCfg& s, ds::PartRec* ws, const int64_t* request_ids, const void* c_logits,
+                const void* u_logits, const int32_t* seq_lens, const int32_t* iterations, const float* guidance_scale,
+                const float* temperature, int32_t num_requests, int32_t num_rows, uint64_t seed, int32_t* tokens_out,
+                float* logprobs_out, float* threshold_out, void* stream) {
+    CallShape sh;
+    {
+        const int rc = check_call(s, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale, temperature,
+                                  num_requests, num_rows, tokens_out, logprobs_out, threshold_out, sh);
+        if (rc != DS_OK) return rc;
+    }
+    const int64_t P = sh.P, Pu = sh.Pu;
+    const bool need_u = sh.need_u, compact_u = sh.compact_u, small = sh.small, bf16 = sh.bf16;
     if (P == 0) return DS_OK;
 
     DeviceGuard dg(s.device);
@@ -448,6 +471,27 @@ int ds_sample_static(int32_t vocab, int32_t dtype, int32_t top_k, int32_t vocab_
         const int rc = check_sampler_settings(vocab, dtype, top_k, vocab_chunks, flags);
         if (rc != DS_OK) return rc;
     }
+    // settings of a handle without its limits (the cell count must fit 31 bits);
+    // the first pivot quantile depends only on (top_k, vocab), so the last one is
+    // kept per thread
+    const int32_t k = top_k ? top_k : (vocab + 9) / 10;
+    thread_local int32_t z_k = -1, z_v = -1;
+    thread_local float z0 = 0.0f;
+    if (z_k != k || z_v != vocab) {
+        z0 = pivot_quantile(k, vocab);
+        z_k = k;
+        z_v = vocab;
+    }
+    // no threshold windows, and no memory beyond the static records
+    const SamplerCfg cfg{vocab, dtype, k, vocab_chunks, flags, z0, INT32_MAX, INT32_MAX, INT32_MAX, -1,
+                         nullptr, nullptr, 0};
+    // every argument is checked before the device is asked anything
+    {
+        CallShape sh;
+        const int rc = check_call(cfg, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale,
+                                  temperature, num_requests, num_rows, tokens_out, logprobs_out, threshold_out, sh);
+        if (rc != DS_OK || sh.P == 0) return rc;
+    }
     int dev = -1;
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -467,19 +511,6 @@ int ds_sample_static(int32_t vocab, int32_t dtype, int32_t top_k, int32_t vocab_
         }
         ws = g_scratch_ptr[dev];
     }
-    // settings of a handle without its limits (the cell count must fit 31 bits);
-    // the first pivot quantile depends only on (top_k, vocab), so the last one is
-    // kept per thread
-    const int32_t k = top_k ? top_k : (vocab + 9) / 10;
-    thread_local int32_t z_k = -1, z_v = -1;
-    thread_local float z0 = 0.0f;
-    if (z_k != k || z_v != vocab) {
-        z0 = pivot_quantile(k, vocab);
-        z_k = k;
-        z_v = vocab;
-    }
-    const SamplerCfg cfg{vocab, dtype, k, vocab_chunks, flags, z0, INT32_MAX, INT32_MAX, INT32_MAX, -1,
-                         nullptr, nullptr, 0};
     return sample_call(cfg, ws, request_ids, c_logits, u_logits, seq_lens, iterations, guidance_scale, temperature,
                        num_requests, num_rows, seed, tokens_out, logprobs_out, threshold_out, stream);
 }
