@@ -264,6 +264,19 @@ def test_row_kernel_many_parts_per_row():
         check_sample(w, run_sample(w, threshold=thr), ref)
 
 
+def test_threshold_windows_over_several_launches():
+    # 2500 cells on the streaming path with the threshold output: the handle's
+    # window buffers hold 2048 rows, so the call is two launches whose window
+    # kernels, parts and merges reuse the same window slots; every cell against
+    # the oracle, thresholds bit for bit
+    w = synth.diffusion("windows_2500", seed=91, vocab=3000, rows=2, seq_lens=[700, 0, 550], sigma=3.0,
+                        guidance=[1.5, 0.0, 2.0], temperature=[1.0, 0.8, 0.0], top_k=300)
+    assert w.cells == 2500
+    ref = oracle_threaded(w, np.arange(w.cells, dtype=np.int64))
+    check_sample(w, run_sample(w, threshold=True), ref)
+    check_sample(w, run_sample(w, threshold=False), ref, check_threshold=False)
+
+
 def test_masked_ids_stay_masked():
     V = 1025
     w = synth.diffusion("masked", seed=5, vocab=V, rows=4, seq_lens=[30, 20], sigma=3.0,
