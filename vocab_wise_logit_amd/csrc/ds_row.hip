@@ -1528,9 +1528,10 @@ int row_parts_per_chunk(bool bf16, int V, int chunks, int64_t cells, bool window
     const int epp = bf16 ? 8 : 4;
     const int64_t L = ((int64_t)V + chunks - 1) / chunks;
     const int64_t pieces = L / epp + 2;
-    // enough waves to cover the GPU several times over (8192: 1024 workgroups of
-    // the plain parts kernel), parts of >= 1024 pieces
-    const int64_t target = 8192 / (window ? kPartWaves<true> : kPartWaves<false>);
+    // enough waves to cover the GPU several times over (12288: two rounds of 6
+    // waves per SIMD for the plain parts kernel), parts of >= 1024 pieces; for a
+    // 256-row autoregressive step that is six parts per row, 5% faster than four
+    const int64_t target = 12288 / (window ? kPartWaves<true> : kPartWaves<false>);
     int64_t p = (target + cells * chunks - 1) / (cells * chunks);
     const int64_t p_cap = pieces / 1024 > 1 ? pieces / 1024 : 1;
     if (p > p_cap) p = p_cap;
