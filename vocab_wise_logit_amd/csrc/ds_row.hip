@@ -121,8 +121,10 @@ constexpr int kMergeThreadsExact = 512;
 // the window kernel, which needs few registers, then runs its 2048 rows in two
 // rounds instead of three (55 -> 46 us on the large-vocabulary step).
 constexpr int kKeyCapExact = 8064;
-// The window kernel: one workgroup per row, sampling it into LDS.
-constexpr int kWindowThreads = 512;
+// The window kernel: one workgroup per row, a sample of the row histogrammed in
+// LDS.  Small workgroups with few registers and little LDS keep every row of a
+// 2048-row launch resident at once.
+constexpr int kWindowThreads = 256;
 
 // The merge's staged part records (or the threshold select's keys) and histogram.
 template <int MT_, int KCAP>
@@ -137,6 +139,14 @@ struct MergeLDS {
     int nkeys;
     int nabove;
     RedT<MT_ / kWave> r;
+};
+
+// The window kernel's LDS: the sample's histogram and the reduction slots.
+template <int BT_>
+struct WindowLDS {
+    static constexpr int kThreads = BT_;
+    uint32_t hist[kHistBins];
+    RedT<BT_ / kWave> r;
 };
 
 // Block argmax of (z, id, h): larger z, then smaller id.
@@ -277,29 +287,6 @@ __device__ __forceinline__ void for_each_id(const RowGeom& G, float s, bool use_
     }
 }
 
-// Visit the ids of every `every`-th run of 64 pieces of the row: f(v, h).  One
-// piece per lane; the sample's runs are spread over the whole row.
-template <bool BF16, int BT, typename F>
-__device__ __forceinline__ void for_each_sampled_id(const RowGeom& G, float s, bool use_u, int every, F&& f) {
-    constexpr int EPP = Piece<BF16>::EPP;
-    const int64_t q0 = G.gbase / EPP;
-    const int64_t q1 = (G.gbase + G.V - 1) / EPP;
-    const int64_t runs = (q1 - q0) / kWave + 1;
-    for (int64_t r = (int64_t)(threadIdx.x / kWave) * every; r < runs; r += (int64_t)(BT / kWave) * every) {
-        const int64_t q = q0 + r * kWave + lane_id();
-        if (q <= q1) {
-            const u32x4 cw = stream_load(G.c16 + q);
-            const u32x4 uw = use_u ? stream_load(G.u16 + q) : cw;
-            Piece<BF16> P;
-            decode_piece<BF16>(cw, uw, s, use_u, P);
-            const int64_t v0 = q * EPP - G.gbase;
-#pragma unroll
-            for (int e = 0; e < EPP; ++e)
-                if (v0 + e >= 0 && v0 + e < G.V) f((int)(v0 + e), P.h[e]);
-        }
-    }
-}
-
 // The digit (histogram bin) holding the kk-th largest key among those counted
 // in sh.hist[0, nbins), with 1 <= kk <= their number; kk becomes the rank inside
 // that bin.  Thread j owns bins nbins-1-j*b .. nbins-b-j*b (b = nbins / threads),
@@ -394,67 +381,132 @@ __device__ __forceinline__ uint32_t lds_kth(const RowGeom& G, SH& sh, int n, int
 }
 
 // A window of order keys that holds the row's top_k-th largest key with high
-// probability, from a sample: the keys of every `every`-th run of 64 pieces (at
-// most kKeyCap of them) go to LDS, and two selects there give the sample's order
-// statistics at ranks k * n / V -+ (sigmas standard deviations + 4).  The window
-// [key_lo, key_hi] is expected to hold about 2 (sigmas sqrt(k f) + 4) / f row ids
-// (f the sampled share); whether it holds the answer is checked by whoever uses
-// it.  Returns false when the row is too short for a sample to pay, or the
-// expected window would not leave room in `cap` keys; then no window exists.
-template <bool BF16, typename SH>
+// probability, from a sample of the row: the ids of every `every`-th run of 64
+// pieces (at most SCAP ids), one histogram of their h over kHistBins equal bins
+// between the sample's finite minimum and maximum, and the bins holding the
+// sample's order statistics at ranks k * n / V -+ (sigmas standard deviations +
+// 4).  The window [key_lo, key_hi] runs from the lower edge of the one bin to the
+// upper edge of the other (open at an end bin), and is expected to hold about
+// 2 (sigmas sqrt(k f) + 4) / f row ids (f the sampled share) plus a bin's width
+// at either end; whether it holds the answer is checked by whoever uses it.  The
+// bins are a monotone function of h, so ranks counted over them bracket the
+// sample's order statistics.  Every wave loads all of its runs before it decodes
+// any, and the ids stay in registers: one pass, no keys in LDS.  Returns false
+// (no window) when the row is too short for a sample to pay, the expected window
+// would not leave room in `cap` keys, or the sample's finite values are all
+// equal.
+template <bool BF16, int SCAP, typename SH>
 __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool use_u, int k, SH& sh, float sigmas,
                                               int cap, uint32_t& key_lo, uint32_t& key_hi) {
     constexpr int BT = SH::kThreads;
+    constexpr int NW = BT / kWave;
     constexpr int EPP = Piece<BF16>::EPP;
-    const int64_t runs = ((G.gbase + G.V - 1) / EPP - G.gbase / EPP) / kWave + 1;
     constexpr int kRunIds = kWave * EPP;
-    constexpr int kSampleRuns = SH::kKeyCap / kRunIds - 1;  // ceil(runs / every) <= runs / every + 1
-    const int every = kSampleRuns > 0 ? (int)((runs + kSampleRuns - 1) / kSampleRuns) : 0;
+    constexpr int kSampleRuns = SCAP / kRunIds - 1;
+    constexpr int RPW = (kSampleRuns + NW - 1) / NW;  // runs per wave
+    static_assert(kSampleRuns >= 1, "a sample of at least one run");
+    const int64_t q0 = G.gbase / EPP;
+    const int64_t q1 = (G.gbase + G.V - 1) / EPP;
+    const int64_t runs = (q1 - q0) / kWave + 1;
+    const int every = (int)((runs + kSampleRuns - 1) / kSampleRuns);
+    const int nsr = (int)((runs + every - 1) / every);  // runs in the sample, at most kSampleRuns
     // the window's expected width in row ids, 2 m / f with f the sampled share,
-    // must leave room in LDS (checked again on the sample actually drawn)
-    const float f_exp = (float)(((runs + every - 1) / max(every, 1)) * kRunIds) / (float)G.V;
+    // must leave room in `cap` keys (checked again on the sample actually drawn)
+    const float f_exp = (float)(nsr * kRunIds) / (float)G.V;
     const float m_exp = sigmas * __builtin_sqrtf((float)k * f_exp) + 4.0f;
     if (!(every >= 4 && 2.0f * m_exp < 0.7f * (float)cap * f_exp)) return false;
-    if (threadIdx.x == 0) sh.nkeys = 0;
+    const int wv = threadIdx.x / kWave;
+    const int lane = lane_id();
+    for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
+    // run wv + j * NW of the sample is run (wv + j * NW) * every of the row
+    u32x4 cw[RPW], uw[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int i = wv + j * NW;
+        const int64_t q = q0 + (int64_t)i * every * kWave + lane;
+        cw[j] = u32x4{0u, 0u, 0u, 0u};
+        uw[j] = cw[j];
+        if (i < nsr && q <= q1) {
+            cw[j] = stream_load(G.c16 + q);
+            if (use_u) uw[j] = stream_load(G.u16 + q);
+        }
+    }
+    // h of the sampled ids (NaN where a slot holds none), their count and finite
+    // range; every id counted is binned once below
+    float h[RPW][EPP];
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    int nv = 0;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int i = wv + j * NW;
+        const int64_t q = q0 + (int64_t)i * every * kWave + lane;
+        const int64_t v0 = q * EPP - G.gbase;
+        Piece<BF16> P;
+        decode_piece<BF16>(cw[j], uw[j], s, use_u, P);
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) {
+            const float x = P.h[e];
+            const bool ok = i < nsr && q <= q1 && v0 + e >= 0 && v0 + e < G.V && x == x;
+            h[j][e] = ok ? x : __builtin_nanf("");
+            nv += ok ? 1 : 0;
+            if (ok && __builtin_fabsf(x) < __builtin_inff()) {
+                mn = __builtin_fminf(mn, x);
+                mx = __builtin_fmaxf(mx, x);
+            }
+        }
+    }
+    {
+        const float wmn = wave_min(mn), wmx = wave_max(mx);
+        const int wn = wave_sum_i(nv);
+        if (lane == 0) {
+            sh.r.f[wv] = wmn;
+            sh.r.f2[wv] = wmx;
+            sh.r.i[wv] = wn;
+        }
+    }
     __syncthreads();
-    for_each_sampled_id<BF16, BT>(G, s, use_u, every, [&](int, float h) {
-        const int at = wave_append(true, &sh.nkeys);
-        if (at >= 0 && at < SH::kKeyCap) sh.u.keys[at] = order_key(h + 0.0f);
-    });
-    __syncthreads();
-    const int ns = min(sh.nkeys, SH::kKeyCap);
+    float bmn = __builtin_inff(), bmx = -__builtin_inff();
+    int ns = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+        bmn = __builtin_fminf(bmn, sh.r.f[w2]);
+        bmx = __builtin_fmaxf(bmx, sh.r.f2[w2]);
+        ns += sh.r.i[w2];
+    }
     // expected sample rank of the answer and a margin of `sigmas` standard deviations
     const float f = (float)ns / (float)G.V;
     const float r = (float)k * f;
     const float m = sigmas * __builtin_sqrtf(r) + 4.0f;
-    if (!(ns > 0 && 2.0f * m < 0.7f * (float)cap * f)) return false;
+    const float scale = (float)kHistBins / (bmx - bmn);
+    if (!(ns > 0 && 2.0f * m < 0.7f * (float)cap * f && bmx > bmn && scale < __builtin_inff())) return false;
+    // bin of h: floor((h - min) * scale) clamped to the bins (-inf to the lowest,
+    // +inf to the highest), a non-decreasing function of h
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) {
+            const float x = h[j][e];
+            if (x == x) {
+                const float t = (x - bmn) * scale;
+                const int bin = t >= (float)(kHistBins - 1) ? kHistBins - 1 : (t > 0.0f ? (int)t : 0);
+                atomicAdd(&sh.hist[bin], 1u);
+            }
+        }
+    __syncthreads();
     const int r_hi = (int)__builtin_floorf(r - m);
     const int r_lo = (int)__builtin_ceilf(r + m);
-    // the two order statistics to 22 bits (two 11-bit digits, the first pass
-    // shared), the window widened outward to whole 22-bit bins: at most 1023
-    // keys of widening each way
-    uint32_t p0 = 0, m0 = 0;
-    int kk = 0;
-    select_pass<BF16>(G, 0.0f, false, sh, 0, true, ns, p0, m0, kk);  // histogram only (kk = 0)
-    uint32_t ph = 0, pl = 0;
-    int kh = r_hi, kl = r_lo;
-    if (r_hi >= 1) ph = find_digit(sh, 1 << kDigitBits[0], kh) << kDigitShift[0];
-    if (r_lo <= ns) pl = find_digit(sh, 1 << kDigitBits[0], kl) << kDigitShift[0];
-    const uint32_t mk0 = ((1u << kDigitBits[0]) - 1u) << kDigitShift[0];
-    constexpr uint32_t kLow = (1u << kDigitShift[1]) - 1u;  // bits below the second digit
+    const float width = (bmx - bmn) / (float)kHistBins;
+    key_hi = 0xFFFFFFFFu;  // open above
+    key_lo = 0u;           // open below
     if (r_hi >= 1) {
-        uint32_t mh = mk0;
-        select_pass<BF16>(G, 0.0f, false, sh, 1, true, ns, ph, mh, kh);
-        key_hi = ph | kLow;
-    } else {
-        key_hi = 0xFFFFFFFFu;
+        int kh = r_hi;
+        const int b = (int)find_digit(sh, kHistBins, kh);
+        if (b + 1 < kHistBins) key_hi = order_key(__builtin_fmaf((float)(b + 1), width, bmn) + 0.0f);
     }
     if (r_lo <= ns) {
-        uint32_t ml = mk0;
-        select_pass<BF16>(G, 0.0f, false, sh, 1, true, ns, pl, ml, kl);
-        key_lo = pl;
-    } else {
-        key_lo = 0u;
+        int kl = r_lo;
+        const int b = (int)find_digit(sh, kHistBins, kl);
+        if (b > 0) key_lo = order_key(__builtin_fmaf((float)b, width, bmn) + 0.0f);
     }
     return true;
 }
@@ -526,7 +578,7 @@ template <bool BF16, typename SH>
 __device__ __forceinline__ float radix_select_row(const RowGeom& G, float s, bool use_u, int k, SH& sh) {
     constexpr int BT = SH::kThreads;
     uint32_t key_lo, key_hi;
-    if (sample_window<BF16>(G, s, use_u, k, sh, 3.0f, SH::kKeyCap, key_lo, key_hi)) {
+    if (sample_window<BF16, SH::kKeyCap>(G, s, use_u, k, sh, 3.0f, SH::kKeyCap, key_lo, key_hi)) {
         if (threadIdx.x == 0) {
             sh.nkeys = 0;
             sh.nabove = 0;
@@ -1031,7 +1083,7 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
 template <bool BF16>
 __device__ void window_body(const void* cptr, const void* uptr, int V, int k, const RowWork& w, const CellParams& cp,
                             int64_t slot) {
-    __shared__ MergeLDS<kWindowThreads, kKeyCapExact> sh;
+    __shared__ WindowLDS<kWindowThreads> sh;
     uint32_t lo = 1u, hi = 0u;  // no window
     if (cp.tau != 0.0f) {
         const bool use_u = cp.s != 0.0f;
@@ -1040,7 +1092,7 @@ __device__ void window_body(const void* cptr, const void* uptr, int V, int k, co
         // five standard deviations: with thousands of rows per launch, one row
         // whose window misses costs its merge a pass over the row, and the launch
         // waits for its slowest row
-        if (sample_window<BF16>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
+        if (sample_window<BF16, kKeyCapExact>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
             lo = a;
             hi = b;
         }
@@ -1237,8 +1289,11 @@ __global__ __launch_bounds__(kPartThreads<WIN>) __attribute__((amdgpu_waves_per_
     part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot),
                                slot, part);
 }
+// With the threshold window the bf16 merge is held to 64 VGPRs, so that four of
+// its 512-thread blocks share a compute unit (41 -> 38 us on the large-vocabulary
+// step, with six spilled registers; the f32 one would spill many more).
 template <bool BF16, int MT_, int KCAP, bool WIN>
-__global__ __launch_bounds__(MT_) void k_sample_merge(SampleArgs a, ReqTable rq) {
+__global__ __launch_bounds__(MT_) __attribute__((amdgpu_waves_per_eu(WIN && BF16 ? 8 : 1, 8))) void k_sample_merge(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x;
     merge_body<BF16, true, MT_, KCAP, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.top_k, a.force_fallback != 0, a.w,
                                            sample_cell(a, rq, slot), slot, a.tokens, a.logprobs, nullptr,
@@ -1259,7 +1314,7 @@ __global__ __launch_bounds__(kPartThreads<WIN>) __attribute__((amdgpu_waves_per_
     part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part);
 }
 template <bool BF16, int MT_, int KCAP, bool WIN>
-__global__ __launch_bounds__(MT_) void k_sample_merge_dev(SampleArgs a, DevReq d) {
+__global__ __launch_bounds__(MT_) __attribute__((amdgpu_waves_per_eu(WIN && BF16 ? 8 : 1, 8))) void k_sample_merge_dev(SampleArgs a, DevReq d) {
     const int64_t slot = blockIdx.x;
     CellParams cp;
     if (!sample_cell_dev(a, d, slot, cp)) return;
