@@ -58,6 +58,21 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// binary32 -> bf16 pattern, round to nearest even: adding 0x7FFF plus the
+// pattern's lowest kept bit carries into the kept half exactly when the dropped
+// half is above the tie, or at it with an odd kept half.  Infinities pass
+// through; finite values past the largest bf16 carry into infinity.
+__device__ __forceinline__ uint16_t bf16_rne(float y) {
+    const uint32_t b = __float_as_uint(y);
+    if ((b & 0x7F800000u) == 0x7F800000u) return (uint16_t)(b >> 16);
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// [ISSUE] repetition penalty over seen-token masks (the pages give no formula):
+// read as the multiplicative penalty, a seen id's logit x becomes x / theta when
+// x > 0 and x * theta otherwise, in binary32 (IEEE division, correctly rounded).
+__device__ __forceinline__ float penalized(float x, float theta) { return x > 0.0f ? x / theta : x * theta; }
+
 // [ISSUE] CFG combine in fp32 with one rounding of s*(c-u)+c.  At a masked id
 // (c = u = -inf) the difference is NaN.  `guided` maps it back to -inf (IEEE
 // maxNum returns the non-NaN operand; every other input passes through

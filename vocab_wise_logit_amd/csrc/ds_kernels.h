@@ -113,8 +113,10 @@ bool greedy_rows_fits(bool bf16, int V, int chunks, const void* x);
 hipError_t launch_greedy_rows(bool bf16, const GreedyArgs& a, hipStream_t st);
 
 // Repetition penalty of the autoregressive mode, in place: one thread per
-// seen-mask word.
+// kPenaltyWords seen-mask words.
 constexpr int kPenaltyThreads = 256;
+constexpr int kPenaltyWords = 2;
+constexpr int kPenaltyBatch = 4;  // seen ids whose logits one thread reads at once
 struct PenaltyArgs {
     void* logits;           // [n_rows, V], modified in place
     const uint32_t* seen;   // [n_rows, W]
