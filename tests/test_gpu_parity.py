@@ -268,13 +268,26 @@ def test_threshold_windows_over_several_launches():
     # 2500 cells on the streaming path with the threshold output: the handle's
     # window buffers hold 2048 rows, so the call is two launches whose window
     # kernels, parts and merges reuse the same window slots; every cell against
-    # the oracle, thresholds bit for bit
-    w = synth.diffusion("windows_2500", seed=91, vocab=3000, rows=2, seq_lens=[700, 0, 550], sigma=3.0,
-                        guidance=[1.5, 0.0, 2.0], temperature=[1.0, 0.8, 0.0], top_k=300)
+    # the oracle, thresholds bit for bit.  V = 32768 bf16 is long enough for the
+    # window's sample (every fifth run of 512 ids), so every sampled row has one.
+    w = synth.diffusion("windows_2500", seed=91, vocab=32768, rows=2, seq_lens=[700, 0, 550], sigma=3.0,
+                        guidance=[1.5, 0.0, 2.0], temperature=[1.0, 0.8, 0.0], top_k=3277)
     assert w.cells == 2500
     ref = oracle_threaded(w, np.arange(w.cells, dtype=np.int64))
     check_sample(w, run_sample(w, threshold=True), ref)
     check_sample(w, run_sample(w, threshold=False), ref, check_threshold=False)
+
+
+@pytest.mark.parametrize("chunks", [1, 3])
+def test_threshold_window_f32(chunks):
+    # f32 rows long enough for the threshold window (V = 40000: every sixth run
+    # of 256 ids is sampled), guided and not, with a masked id
+    w = synth.diffusion("window_f32", seed=93, vocab=40000, rows=2, seq_lens=[5, 4], dtype="f32", sigma=3.0,
+                        guidance=[1.5, 0.0], temperature=[1.0, 0.7], vocab_chunks=chunks, masked_ids=[11])
+    ref = oracle.sample_workload(w)
+    for thr in (True, False):
+        check_sample(w, run_sample(w, threshold=thr), ref)
+    check_sample(w, run_sample(w, force_fallback=True), ref)
 
 
 def test_masked_ids_stay_masked():
