@@ -40,6 +40,11 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "sampled positions/sec + achieved HBM GB/s (% of MI355X peak) per config"
 ROTATE_BYTES = 1 << 30
 SUITE_BUDGET_S = 0.03  # timed work per suite entry
+# Untimed work before a timed region: a sustained load after idle runs slower for
+# its first 20-30 ms (the large-vocabulary parts kernel goes from 300 to 425 us
+# within 3 ms, then back to 300 us by about 25 ms), so every timed region starts
+# after at least this much warmup.
+WARMUP_MIN_S = 0.05
 # threads per workgroup of the one-workgroup-per-row draft kernel and of the
 # streaming parts kernel (the launch shapes the read ceilings are measured at)
 GREEDY_ROW_THREADS = 512
@@ -340,7 +345,7 @@ def auto_steps(r: "Runner", budget_s: float = SUITE_BUDGET_S) -> tuple:
     torch.cuda.synchronize()
     est = (time.perf_counter() - t) / 10
     steps = int(min(max(budget_s / max(est, 1e-7), 10), 5000))
-    return steps, max(steps // 5, 3)
+    return steps, max(steps // 5, math.ceil(WARMUP_MIN_S / max(est, 1e-7)), 3)
 
 
 def bench_one(name: str, steps, warmup, threshold: bool = False, mode: str = "eager") -> dict:
@@ -549,7 +554,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)  # about 65 ms of the headline step: WARMUP_MIN_S
     ap.add_argument("--workload", default="stress")
     ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
     ap.add_argument("--threshold", action="store_true",
