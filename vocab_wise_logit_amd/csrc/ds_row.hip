@@ -117,9 +117,8 @@ constexpr int kMergeThreadsFast = 256;
 constexpr int kKeyCapFast = 2048;
 constexpr int kMergeThreadsExact = 512;
 // 8064, not 8192: with it a 512-thread block's LDS (keys, the 2048-bin
-// histogram, the reduction slots) stays under 40 KB, so four blocks fit a CU;
-// the window kernel, which needs few registers, then runs its 2048 rows in two
-// rounds instead of three (55 -> 46 us on the large-vocabulary step).
+// histogram, the reduction slots) stays under 40 KB, so four blocks fit a CU
+// (the window merge, held to 64 VGPRs, runs four per CU).
 constexpr int kKeyCapExact = 8064;
 // The window kernel: one workgroup per row, a sample of the row histogrammed in
 // LDS.  Small workgroups with few registers and little LDS keep every row of a
