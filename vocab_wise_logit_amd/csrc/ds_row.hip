@@ -39,7 +39,6 @@ namespace ds {
 namespace {
 
 constexpr int NT = kRowThreads;
-constexpr int NWAVES = NT / kWave;
 constexpr int U = kRowU;
 // The parts kernel with the threshold window runs smaller workgroups: its
 // per-wave work at the ends of a part (the first group's race bound, the queue
