@@ -268,10 +268,10 @@ def test_threshold_windows_over_several_launches():
     # 2500 cells on the streaming path with the threshold output: the handle's
     # window buffers hold 2048 rows, so the call is two launches whose window
     # kernels, parts and merges reuse the same window slots; every cell against
-    # the oracle, thresholds bit for bit.  V = 32768 bf16 is long enough for the
+    # the oracle, thresholds bit for bit.  V = 65536 bf16 is long enough for the
     # window's sample (every fifth run of 512 ids), so every sampled row has one.
-    w = synth.diffusion("windows_2500", seed=91, vocab=32768, rows=2, seq_lens=[700, 0, 550], sigma=3.0,
-                        guidance=[1.5, 0.0, 2.0], temperature=[1.0, 0.8, 0.0], top_k=3277)
+    w = synth.diffusion("windows_2500", seed=91, vocab=65536, rows=2, seq_lens=[700, 0, 550], sigma=3.0,
+                        guidance=[1.5, 0.0, 2.0], temperature=[1.0, 0.8, 0.0], top_k=6554)
     assert w.cells == 2500
     ref = oracle_threaded(w, np.arange(w.cells, dtype=np.int64))
     check_sample(w, run_sample(w, threshold=True), ref)
@@ -280,9 +280,9 @@ def test_threshold_windows_over_several_launches():
 
 @pytest.mark.parametrize("chunks", [1, 3])
 def test_threshold_window_f32(chunks):
-    # f32 rows long enough for the threshold window (V = 40000: every sixth run
+    # f32 rows long enough for the threshold window (V = 65536: every fifth run
     # of 256 ids is sampled), guided and not, with a masked id
-    w = synth.diffusion("window_f32", seed=93, vocab=40000, rows=2, seq_lens=[5, 4], dtype="f32", sigma=3.0,
+    w = synth.diffusion("window_f32", seed=93, vocab=65536, rows=2, seq_lens=[5, 4], dtype="f32", sigma=3.0,
                         guidance=[1.5, 0.0], temperature=[1.0, 0.7], vocab_chunks=chunks, masked_ids=[11])
     ref = oracle.sample_workload(w)
     for thr in (True, False):

@@ -120,9 +120,15 @@ constexpr int kMergeThreadsExact = 512;
 // (the window merge, held to 64 VGPRs, runs four per CU).
 constexpr int kKeyCapExact = 8064;
 // The window kernel: one workgroup per row, a sample of the row histogrammed in
-// LDS.  Small workgroups with few registers and little LDS keep every row of a
-// 2048-row launch resident at once.
-constexpr int kWindowThreads = 256;
+// LDS.  Its sample of up to kWindowSample ids (30 runs of 512 bf16 ids): the
+// window's width goes as 1 / sqrt(sampled share), and the parts' and the merge's
+// work with it, against the sample's reads here.  On the large-vocabulary step
+// (thresholds included) 7168 ids: window 25 us, parts 500, merge 37; 15360: 42,
+// 467, 30 (28 us less in all); 31744: 126, 443, 27.  512 threads keep each wave's
+// part of the sample (four runs) in 60 VGPRs; with 256 threads the registers of
+// eight runs cost more than the workgroups gained.
+constexpr int kWindowThreads = 512;
+constexpr int kWindowSample = 16128;
 
 // The merge's staged part records (or the threshold select's keys) and histogram.
 template <int MT_, int KCAP>
@@ -1090,7 +1096,7 @@ __device__ void window_body(const void* cptr, const void* uptr, int V, int k, co
         // five standard deviations: with thousands of rows per launch, one row
         // whose window misses costs its merge a pass over the row, and the launch
         // waits for its slowest row
-        if (sample_window<BF16, kKeyCapExact>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
+        if (sample_window<BF16, kWindowSample>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
             lo = a;
             hi = b;
         }
