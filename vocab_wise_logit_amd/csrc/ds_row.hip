@@ -109,16 +109,22 @@ constexpr int kHistBins = 2048;
 // The merge runs in one of two shapes.  When the call asks for no threshold, a
 // row's merge almost always only folds its part records, so the kernel is
 // latency-bound: small blocks with little LDS let every row of a launch run at
-// once.  When every row needs the exact select, larger blocks keep more keys of
-// the threshold's first-digit bin in LDS, which saves passes over the row.
+// once.  When every row needs the exact select over the row (the threshold
+// without a window, or the forced fallback), larger blocks keep more keys of the
+// threshold's first-digit bin in LDS, which saves passes over the row.
 constexpr int kMergeStage = 64;    // part records staged in LDS at a time
 constexpr int kMergeThreadsFast = 256;
 constexpr int kKeyCapFast = 2048;
 constexpr int kMergeThreadsExact = 512;
 // 8064, not 8192: with it a 512-thread block's LDS (keys, the 2048-bin
-// histogram, the reduction slots) stays under 40 KB, so four blocks fit a CU
-// (the window merge, held to 64 VGPRs, runs four per CU).
+// histogram, the reduction slots) stays under 40 KB, so four blocks fit a CU.
 constexpr int kKeyCapExact = 8064;
+// With the threshold window the merge selects among the window's keys in global
+// memory and needs LDS keys only when the window misses, so it takes the small
+// shape: eight of its blocks share a compute unit and a 2048-row launch runs in
+// one round (29.4 -> 25.8 us on the large-vocabulary step).
+constexpr int kMergeThreadsWin = kMergeThreadsFast;
+constexpr int kKeyCapWin = kKeyCapFast;
 // The window kernel: one workgroup per row, a sample of the row histogrammed in
 // LDS.  Its sample of up to kWindowSample ids (30 runs of 512 bf16 ids): the
 // window's width goes as 1 / sqrt(sampled share), and the parts' and the merge's
@@ -1293,9 +1299,9 @@ __global__ __launch_bounds__(kPartThreads<WIN>) __attribute__((amdgpu_waves_per_
     part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, sample_cell(a, rq, slot),
                                slot, part);
 }
-// With the threshold window the bf16 merge is held to 64 VGPRs, so that four of
-// its 512-thread blocks share a compute unit (41 -> 38 us on the large-vocabulary
-// step, with six spilled registers; the f32 one would spill many more).
+// With the threshold window the bf16 merge is held to 64 VGPRs, so that eight of
+// its 256-thread blocks share a compute unit (four spilled registers; the f32 one
+// would spill many more).
 template <bool BF16, int MT_, int KCAP, bool WIN>
 __global__ __launch_bounds__(MT_) __attribute__((amdgpu_waves_per_eu(WIN && BF16 ? 8 : 1, 8))) void k_sample_merge(SampleArgs a, ReqTable rq) {
     const int64_t slot = blockIdx.x;
@@ -1615,7 +1621,7 @@ hipError_t launch_row(const SampleArgs& a, const Src& src, hipStream_t st, KW kw
     if (win) {
         hipLaunchKernelGGL(kwin, mg, dim3(kWindowThreads), 0, st, a, src);
         hipLaunchKernelGGL(kparts_win, dim3((unsigned)parts), dim3(kPartThreads<true>), 0, st, a, src);
-        hipLaunchKernelGGL(kmerge_exact_win, mg, dim3(kMergeThreadsExact), 0, st, a, src);
+        hipLaunchKernelGGL(kmerge_exact_win, mg, dim3(kMergeThreadsWin), 0, st, a, src);
     } else {
         hipLaunchKernelGGL(kparts, dim3((unsigned)parts), dim3(NT), 0, st, a, src);
         if (exact)
@@ -1633,11 +1639,11 @@ hipError_t launch_sample_row(bool bf16, const SampleArgs& a, const ReqTable& rq,
         return launch_row<true>(a, rq, st, k_sample_window<true>, k_sample_parts<true, false>,
                                 k_sample_parts<true, true>, k_sample_merge<true, kMergeThreadsFast, kKeyCapFast, false>,
                                 k_sample_merge<true, kMergeThreadsExact, kKeyCapExact, false>,
-                                k_sample_merge<true, kMergeThreadsExact, kKeyCapExact, true>);
+                                k_sample_merge<true, kMergeThreadsWin, kKeyCapWin, true>);
     return launch_row<false>(a, rq, st, k_sample_window<false>, k_sample_parts<false, false>,
                              k_sample_parts<false, true>, k_sample_merge<false, kMergeThreadsFast, kKeyCapFast, false>,
                              k_sample_merge<false, kMergeThreadsExact, kKeyCapExact, false>,
-                             k_sample_merge<false, kMergeThreadsExact, kKeyCapExact, true>);
+                             k_sample_merge<false, kMergeThreadsWin, kKeyCapWin, true>);
 }
 
 hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d, hipStream_t st) {
@@ -1647,12 +1653,12 @@ hipError_t launch_sample_row_dev(bool bf16, const SampleArgs& a, const DevReq& d
                                 k_sample_parts_dev<true, true>,
                                 k_sample_merge_dev<true, kMergeThreadsFast, kKeyCapFast, false>,
                                 k_sample_merge_dev<true, kMergeThreadsExact, kKeyCapExact, false>,
-                                k_sample_merge_dev<true, kMergeThreadsExact, kKeyCapExact, true>);
+                                k_sample_merge_dev<true, kMergeThreadsWin, kKeyCapWin, true>);
     return launch_row<false>(a, d, st, k_sample_window_dev<false>, k_sample_parts_dev<false, false>,
                              k_sample_parts_dev<false, true>,
                              k_sample_merge_dev<false, kMergeThreadsFast, kKeyCapFast, false>,
                              k_sample_merge_dev<false, kMergeThreadsExact, kKeyCapExact, false>,
-                             k_sample_merge_dev<false, kMergeThreadsExact, kKeyCapExact, true>);
+                             k_sample_merge_dev<false, kMergeThreadsWin, kKeyCapWin, true>);
 }
 
 bool greedy_rows_fits(bool bf16, int V, int chunks, const void* x) {
