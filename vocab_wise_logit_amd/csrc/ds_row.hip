@@ -130,11 +130,15 @@ constexpr int kKeyCapWin = kKeyCapFast;
 // window's width goes as 1 / sqrt(sampled share), and the parts' and the merge's
 // work with it, against the sample's reads here.  On the large-vocabulary step
 // (thresholds included) 7168 ids: window 25 us, parts 500, merge 37; 15360: 42,
-// 467, 30 (28 us less in all); 31744: 126, 443, 27.  512 threads keep each wave's
-// part of the sample (four runs) in 60 VGPRs; with 256 threads the registers of
-// eight runs cost more than the workgroups gained.
-constexpr int kWindowThreads = 512;
+// 467, 30 (28 us less in all); 31744: 126, 443, 27.  Each wave of a 256-thread
+// workgroup takes its eight runs four at a time (kWindowBatch): 36 us for the
+// 15360-id sample, against 41 us with every run of a 512-thread workgroup's
+// waves in registers at once (two rounds of 1024 rows).  The sample's 123 MB of
+// 1 KB pieces scattered over the rows read at about 3.4 TB/s, which is most of
+// that time.
+constexpr int kWindowThreads = 256;
 constexpr int kWindowSample = 16128;
+constexpr int kWindowBatch = 4;
 
 // The merge's staged part records (or the threshold select's keys) and histogram.
 template <int MT_, int KCAP>
@@ -392,20 +396,23 @@ __device__ __forceinline__ uint32_t lds_kth(const RowGeom& G, SH& sh, int n, int
 
 // A window of order keys that holds the row's top_k-th largest key with high
 // probability, from a sample of the row: the ids of every `every`-th run of 64
-// pieces (at most SCAP ids), one histogram of their h over kHistBins equal bins
-// between the sample's finite minimum and maximum, and the bins holding the
-// sample's order statistics at ranks k * n / V -+ (sigmas standard deviations +
-// 4).  The window [key_lo, key_hi] runs from the lower edge of the one bin to the
-// upper edge of the other (open at an end bin), and is expected to hold about
-// 2 (sigmas sqrt(k f) + 4) / f row ids (f the sampled share) plus a bin's width
-// at either end; whether it holds the answer is checked by whoever uses it.  The
-// bins are a monotone function of h, so ranks counted over them bracket the
-// sample's order statistics.  Every wave loads all of its runs before it decodes
-// any, and the ids stay in registers: one pass, no keys in LDS.  Returns false
-// (no window) when the row is too short for a sample to pay, the expected window
-// would not leave room in `cap` keys, or the sample's finite values are all
+// pieces (at most SCAP ids), one histogram of their h over kHistBins equal bins,
+// and the bins holding the sample's order statistics at ranks k * n / V -+
+// (sigmas standard deviations + 4).  The window [key_lo, key_hi] runs from the
+// lower edge of the one bin to the upper edge of the other (open at an end bin),
+// and is expected to hold about 2 (sigmas sqrt(k f) + 4) / f row ids (f the
+// sampled share) plus a bin's width at either end; whether it holds the answer
+// is checked by whoever uses it.  The bins are a non-decreasing function of h,
+// so ranks counted over them bracket the sample's order statistics.
+//
+// Each wave takes its runs RB at a time (all of them at once by default),
+// loading a batch's runs before it decodes any.  The bins span the finite range
+// of the first batch; with later batches that range is widened by a quarter on
+// either side and what lies beyond it goes to the end bins.  Returns false (no
+// window) when the row is too short for a sample to pay, the expected window
+// would not leave room in `cap` keys, or the first batch's finite values are all
 // equal.
-template <bool BF16, int SCAP, typename SH>
+template <bool BF16, int SCAP, int RB_ = 0, typename SH>
 __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool use_u, int k, SH& sh, float sigmas,
                                               int cap, uint32_t& key_lo, uint32_t& key_hi) {
     constexpr int BT = SH::kThreads;
@@ -414,6 +421,8 @@ __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool us
     constexpr int kRunIds = kWave * EPP;
     constexpr int kSampleRuns = SCAP / kRunIds - 1;
     constexpr int RPW = (kSampleRuns + NW - 1) / NW;  // runs per wave
+    constexpr int RB = RB_ > 0 && RB_ < RPW ? RB_ : RPW;  // runs per batch
+    constexpr int NB = (RPW + RB - 1) / RB;
     static_assert(kSampleRuns >= 1, "a sample of at least one run");
     const int64_t q0 = G.gbase / EPP;
     const int64_t q1 = (G.gbase + G.V - 1) / EPP;
@@ -428,95 +437,105 @@ __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool us
     const int wv = threadIdx.x / kWave;
     const int lane = lane_id();
     for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
-    // run wv + j * NW of the sample is run (wv + j * NW) * every of the row
-    u32x4 cw[RPW], uw[RPW];
+    float lo_f = 0.0f, scale = 0.0f;  // bin of h: floor((h - lo_f) * scale), clamped to the bins
+    int nv = 0;                       // sampled ids of this lane (every one is binned once)
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        const int i = wv + j * NW;
-        const int64_t q = q0 + (int64_t)i * every * kWave + lane;
-        cw[j] = u32x4{0u, 0u, 0u, 0u};
-        uw[j] = cw[j];
-        if (i < nsr && q <= q1) {
-            cw[j] = stream_load(G.c16 + q);
-            if (use_u) uw[j] = stream_load(G.u16 + q);
-        }
-    }
-    // h of the sampled ids (NaN where a slot holds none), their count and finite
-    // range; every id counted is binned once below
-    float h[RPW][EPP];
-    float mn = __builtin_inff(), mx = -__builtin_inff();
-    int nv = 0;
+    for (int bt = 0; bt < NB; ++bt) {
+        // run wv + j * NW of the sample is run (wv + j * NW) * every of the row
+        u32x4 cw[RB], uw[RB];
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        const int i = wv + j * NW;
-        const int64_t q = q0 + (int64_t)i * every * kWave + lane;
-        const int64_t v0 = q * EPP - G.gbase;
-        Piece<BF16> P;
-        decode_piece<BF16>(cw[j], uw[j], s, use_u, P);
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) {
-            const float x = P.h[e];
-            const bool ok = i < nsr && q <= q1 && v0 + e >= 0 && v0 + e < G.V && x == x;
-            h[j][e] = ok ? x : __builtin_nanf("");
-            nv += ok ? 1 : 0;
-            if (ok && __builtin_fabsf(x) < __builtin_inff()) {
-                mn = __builtin_fminf(mn, x);
-                mx = __builtin_fmaxf(mx, x);
+        for (int jj = 0; jj < RB; ++jj) {
+            const int i = wv + (bt * RB + jj) * NW;
+            const int64_t q = q0 + (int64_t)i * every * kWave + lane;
+            cw[jj] = u32x4{0u, 0u, 0u, 0u};
+            uw[jj] = cw[jj];
+            if (bt * RB + jj < RPW && i < nsr && q <= q1) {
+                cw[jj] = stream_load(G.c16 + q);
+                if (use_u) uw[jj] = stream_load(G.u16 + q);
             }
         }
+        // h of the batch's ids (NaN where a slot holds none), and of the first
+        // batch the finite range
+        float h[RB][EPP];
+        float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+        for (int jj = 0; jj < RB; ++jj) {
+            const int i = wv + (bt * RB + jj) * NW;
+            const int64_t q = q0 + (int64_t)i * every * kWave + lane;
+            const int64_t v0 = q * EPP - G.gbase;
+            Piece<BF16> P;
+            decode_piece<BF16>(cw[jj], uw[jj], s, use_u, P);
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) {
+                const float x = P.h[e];
+                const bool ok = bt * RB + jj < RPW && i < nsr && q <= q1 && v0 + e >= 0 && v0 + e < G.V && x == x;
+                h[jj][e] = ok ? x : __builtin_nanf("");
+                nv += ok ? 1 : 0;
+                if (bt == 0 && ok && __builtin_fabsf(x) < __builtin_inff()) {
+                    mn = __builtin_fminf(mn, x);
+                    mx = __builtin_fmaxf(mx, x);
+                }
+            }
+        }
+        if (bt == 0) {
+            const float wmn = wave_min(mn), wmx = wave_max(mx);
+            if (lane == 0) {
+                sh.r.f[wv] = wmn;
+                sh.r.f2[wv] = wmx;
+            }
+            __syncthreads();
+            float bmn = __builtin_inff(), bmx = -__builtin_inff();
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                bmn = __builtin_fminf(bmn, sh.r.f[w2]);
+                bmx = __builtin_fmaxf(bmx, sh.r.f2[w2]);
+            }
+            const float pad = NB > 1 ? 0.25f * (bmx - bmn) : 0.0f;
+            lo_f = bmn - pad;
+            scale = (float)kHistBins / ((bmx + pad) - lo_f);
+            if (!(bmx > bmn && scale < __builtin_inff())) return false;
+        }
+        // a non-decreasing function of h (-inf to the lowest bin, +inf to the highest)
+#pragma unroll
+        for (int jj = 0; jj < RB; ++jj)
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) {
+                const float x = h[jj][e];
+                if (x == x) {
+                    const float t = (x - lo_f) * scale;
+                    const int bin = t >= (float)(kHistBins - 1) ? kHistBins - 1 : (t > 0.0f ? (int)t : 0);
+                    atomicAdd(&sh.hist[bin], 1u);
+                }
+            }
     }
     {
-        const float wmn = wave_min(mn), wmx = wave_max(mx);
         const int wn = wave_sum_i(nv);
-        if (lane == 0) {
-            sh.r.f[wv] = wmn;
-            sh.r.f2[wv] = wmx;
-            sh.r.i[wv] = wn;
-        }
+        if (lane == 0) sh.r.i[wv] = wn;
     }
     __syncthreads();
-    float bmn = __builtin_inff(), bmx = -__builtin_inff();
     int ns = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) {
-        bmn = __builtin_fminf(bmn, sh.r.f[w2]);
-        bmx = __builtin_fmaxf(bmx, sh.r.f2[w2]);
-        ns += sh.r.i[w2];
-    }
+    for (int w2 = 0; w2 < NW; ++w2) ns += sh.r.i[w2];
+    __syncthreads();  // every read of the counts before find_digit reuses their slots
     // expected sample rank of the answer and a margin of `sigmas` standard deviations
     const float f = (float)ns / (float)G.V;
     const float r = (float)k * f;
     const float m = sigmas * __builtin_sqrtf(r) + 4.0f;
-    const float scale = (float)kHistBins / (bmx - bmn);
-    if (!(ns > 0 && 2.0f * m < 0.7f * (float)cap * f && bmx > bmn && scale < __builtin_inff())) return false;
-    // bin of h: floor((h - min) * scale) clamped to the bins (-inf to the lowest,
-    // +inf to the highest), a non-decreasing function of h
-#pragma unroll
-    for (int j = 0; j < RPW; ++j)
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) {
-            const float x = h[j][e];
-            if (x == x) {
-                const float t = (x - bmn) * scale;
-                const int bin = t >= (float)(kHistBins - 1) ? kHistBins - 1 : (t > 0.0f ? (int)t : 0);
-                atomicAdd(&sh.hist[bin], 1u);
-            }
-        }
-    __syncthreads();
+    if (!(ns > 0 && 2.0f * m < 0.7f * (float)cap * f)) return false;
     const int r_hi = (int)__builtin_floorf(r - m);
     const int r_lo = (int)__builtin_ceilf(r + m);
-    const float width = (bmx - bmn) / (float)kHistBins;
+    const float width = __builtin_amdgcn_rcpf(scale);  // of a bin, the edges lo_f + b * width
     key_hi = 0xFFFFFFFFu;  // open above
     key_lo = 0u;           // open below
     if (r_hi >= 1) {
         int kh = r_hi;
         const int b = (int)find_digit(sh, kHistBins, kh);
-        if (b + 1 < kHistBins) key_hi = order_key(__builtin_fmaf((float)(b + 1), width, bmn) + 0.0f);
+        if (b + 1 < kHistBins) key_hi = order_key(__builtin_fmaf((float)(b + 1), width, lo_f) + 0.0f);
     }
     if (r_lo <= ns) {
         int kl = r_lo;
         const int b = (int)find_digit(sh, kHistBins, kl);
-        if (b > 0) key_lo = order_key(__builtin_fmaf((float)b, width, bmn) + 0.0f);
+        if (b > 0) key_lo = order_key(__builtin_fmaf((float)b, width, lo_f) + 0.0f);
     }
     return true;
 }
@@ -1102,7 +1121,7 @@ __device__ void window_body(const void* cptr, const void* uptr, int V, int k, co
         // five standard deviations: with thousands of rows per launch, one row
         // whose window misses costs its merge a pass over the row, and the launch
         // waits for its slowest row
-        if (sample_window<BF16, kWindowSample>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
+        if (sample_window<BF16, kWindowSample, kWindowBatch>(G, cp.s, use_u, k, sh, 5.0f, kWinKeysPerRow, a, b)) {
             lo = a;
             hi = b;
         }
