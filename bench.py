@@ -103,9 +103,11 @@ def kernel_name(w, kind: str) -> str:
     if kind == "reveal":
         return "k_reveal_topk"
     if kind == "ar":
-        dev = [k.replace("_wide", "") + "_dev" + ("_wide" if k.endswith("_wide") else "")
-               for k in sampler_kernels(w.vocab, w.dtype).split("+")]
-        return "+".join(["k_repetition_penalty"] + dev)
+        # the streaming parts penalise their own ids; the wave-per-cell kernel
+        # takes its rows from the penalty kernel
+        ks = sampler_kernels(w.vocab, w.dtype)
+        dev = [k.replace("_wide", "") + "_dev" + ("_wide" if k.endswith("_wide") else "") for k in ks.split("+")]
+        return "+".join(dev if ks.startswith("k_sample_parts") else ["k_repetition_penalty"] + dev)
     if kind == "draft":
         return draft_kernel(w)
     return sampler_kernels(w.vocab, w.dtype)
@@ -324,10 +326,10 @@ def launches_per_step(w, kind: str) -> int:
     """Kernel launches of one call: one for the wave-per-cell kernel and the
     one-workgroup-per-row draft kernel, a parts and a merge kernel for the
     streaming path (every sampling workload here fits one batch).  The
-    autoregressive step is the penalty kernel and then the sampler over all its
-    requests at once."""
+    autoregressive step samples all its requests at once: parts (which apply
+    the penalty) and merge, or the penalty kernel and the wave-per-cell kernel."""
     if kind == "ar":
-        return 1 + (1 if sampler_kernels(w.vocab, w.dtype).startswith("k_sample_small") else 2)
+        return 2
     return 1 if kernel_name(w, kind).startswith(("k_sample_small", "k_reveal", "k_greedy_rows")) else 2
 
 

@@ -274,10 +274,14 @@ int ds_repetition_penalty(ds_sampler *s, void *logits, int64_t n_rows, const uin
  * ds_sample_ar -- one autoregressive step: one token per request ([ISSUE]: the
  * existing sampler draws one token per request and applies a repetition penalty
  * over seen-token masks).  The repetition penalty (as ds_repetition_penalty, in
- * place) and then, in one launch, every row sampled as the only position of its
- * request: guidance 0, the request's temperature (0 = greedy), the handle's
- * top_k, Gumbel noise keyed by (seed, request id, iteration, row 0, position 0,
- * id) exactly as ds_sample keys a request with one position, and the
+ * place) and then every row sampled as the only position of its request.  On
+ * the streaming path (V above the wave-per-cell kernel's limit, or the forced
+ * fallback) each part of a row penalises its own ids just before it reads them,
+ * so the row is read once; otherwise the penalty kernel runs first.  Either
+ * way the penalised logits and the results are the same.  Each row is sampled
+ * with guidance 0, the request's temperature (0 = greedy), the handle's top_k,
+ * Gumbel noise keyed by (seed, request id, iteration, row 0, position 0, id)
+ * exactly as ds_sample keys a request with one position, and the
  * full-vocabulary log-probability of the penalised row.
  *
  *   request_ids   device int64 [R], 8-byte aligned.

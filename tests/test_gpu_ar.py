@@ -4,6 +4,8 @@ from the penalised rows (to the bar of the other sampler tests)."""
 
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -51,19 +53,17 @@ def _run(w, smp):
     return xo, tok.cpu().numpy(), lp.cpu().numpy()
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_ar_step_matches_oracle(case):
+def _check_against_oracle(w, name, oracle_penalty=None, **sampler_kw):
+    """One step through ds_sample_ar, checked against the oracle: penalised logits
+    bit for bit, greedy tokens exactly, sampled tokens except bounded near ties
+    (which must still draw a kept id inside the band), logprobs to LP_TOL.  The
+    oracle takes `oracle_penalty` as the thetas when given."""
     import vocab_wise_logit_amd as ds
 
-    name, R, V, dt, (lo, hi), temps, top_k = case
-    w = synth.ar(n_requests=R, vocab=V, seed=31 + R, dtype=dt, seen_lo=lo, seen_hi=hi, penalty=1.0,
-                 temperatures=temps, top_k=top_k, name=name)
-    # varied penalties, one row left unpenalised through an invalid theta
-    w.penalty[:] = np.linspace(0.6, 2.5, R).astype(np.float32)
-    log(f"[gpu] ar {name}: R={R} V={V} {dt} seen={w.n_seen()} top_k={w.top_k}")
-    with ds.Sampler(V, dt, max_rows=1, max_positions=R, max_requests=R, top_k=w.top_k) as smp:
+    R, V = w.rows, w.vocab
+    with ds.Sampler(V, w.dtype, max_rows=1, max_positions=R, max_requests=R, top_k=w.top_k, **sampler_kw) as smp:
         xo, tok, lp = _run(w, smp)
-    pen, ref = oracle.ar_step(w)
+    pen, ref = oracle.ar_step(w if oracle_penalty is None else dataclasses.replace(w, penalty=oracle_penalty))
     assert np.array_equal(xo, pen), "penalised logits differ from the oracle"
     greedy = w.temperature == 0
     near = ref.near_tie.astype(bool) & ~greedy
@@ -79,7 +79,58 @@ def test_ar_step_matches_oracle(case):
     NEAR_TIE_TALLY.append((f"ar_{name}", sampled, int(near.sum()), int((near & (tok != ref.tokens)).sum())))
     same = tok == ref.tokens
     assert np.max(np.abs(lp[same].astype(np.float64) - ref.logprobs[same])) <= LP_TOL
-    log(f"[check] ar {name}: greedy={int(greedy.sum())} sampled={int((~greedy).sum())} near_ties={int(near.sum())}")
+    log(f"[check] ar {name}: greedy={int(greedy.sum())} sampled={sampled} near_ties={int(near.sum())}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_ar_step_matches_oracle(case):
+    name, R, V, dt, (lo, hi), temps, top_k = case
+    w = synth.ar(n_requests=R, vocab=V, seed=31 + R, dtype=dt, seen_lo=lo, seen_hi=hi, penalty=1.0,
+                 temperatures=temps, top_k=top_k, name=name)
+    # varied penalties
+    w.penalty[:] = np.linspace(0.6, 2.5, R).astype(np.float32)
+    log(f"[gpu] ar {name}: R={R} V={V} {dt} seen={w.n_seen()} top_k={w.top_k}")
+    _check_against_oracle(w, name)
+
+
+PROLOGUE_CASES = [
+    # (name, R, V, dtype, vocab chunks, force the streaming path)
+    ("bf16_3_chunks", 5, 40961, "bf16", 3, False),
+    ("f32_4_chunks", 4, 30011, "f32", 4, False),
+    ("bf16_7_chunks_top_ratio", 6, 65536, "bf16", 7, False),
+    ("bf16_small_row_streamed", 7, 1025, "bf16", 2, True),
+]
+
+
+@pytest.mark.parametrize("case", PROLOGUE_CASES, ids=[c[0] for c in PROLOGUE_CASES])
+def test_ar_every_id_seen_is_penalised_once(case):
+    """Every id of every row seen, the mask bits past V set too.  On the streaming
+    path each part penalises its own ids in place before reading them, so an id
+    penalised by two parts, or by none, at a part or chunk edge (ragged V, chunk
+    lengths that are not whole 16-byte pieces or mask words) changes the
+    penalised logits, which must equal the oracle's bit for bit.  One row's theta
+    is not finite and leaves it unchanged."""
+    name, R, V, dt, chunks, forced = case
+    top_k = (V + 9) // 10 if "top_ratio" in name else None
+    w = synth.ar(n_requests=R, vocab=V, seed=90 + R, dtype=dt, seen_lo=1, seen_hi=2, penalty=1.0,
+                 temperatures=(0.0, 0.8, 1.1), top_k=top_k, name=name)
+    w.seen[:] = np.uint32(0xFFFFFFFF)
+    w.penalty[:] = np.linspace(0.55, 2.4, R).astype(np.float32)
+    w.penalty[1] = np.inf
+    # the oracle takes only valid thetas; theta 1 leaves every value as it is
+    ora = w.penalty.copy()
+    ora[1] = 1.0
+    log(f"[gpu] ar all seen {name}: R={R} V={V} {dt} chunks={chunks} forced={forced}")
+    _check_against_oracle(w, f"all_seen_{name}", oracle_penalty=ora, vocab_chunks=chunks, force_fallback=forced)
+
+
+def test_ar_step_full_size():
+    """The autoregressive step at full size, as timed: 256 requests x 248320 bf16,
+    256 to 1280 seen ids each, theta 1.1, temperatures 0 / 0.7 / 1.0, no top-ratio
+    filter; every row's penalised logits, token and logprob."""
+    w = synth.ar()
+    log(f"[gpu] ar full size: R={w.rows} V={w.vocab} seen={w.n_seen()}")
+    _check_against_oracle(w, "full_size")
 
 
 def test_penalty_edge_rows():

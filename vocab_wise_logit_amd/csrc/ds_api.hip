@@ -630,6 +630,17 @@ int ds_greedy_lse(ds_sampler* s, const void* logits, int64_t n_rows, int32_t* to
 }
 
 
+// The pointer checks of the repetition penalty's arguments.
+static int check_penalty_args(const ds_sampler* s, const void* logits, const uint32_t* seen_mask, const float* penalty) {
+    if (!logits || !seen_mask || !penalty)
+        return fail(DS_ERR_INVALID_ARG, "logits, seen_mask and penalty must be non-NULL");
+    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(logits, es)) return fail(DS_ERR_INVALID_ARG, "logits is not %d-byte aligned", (int)es);
+    if (!aligned(seen_mask, 4) || !aligned(penalty, 4))
+        return fail(DS_ERR_INVALID_ARG, "seen_mask and penalty must be 4-byte aligned");
+    return DS_OK;
+}
+
 int ds_repetition_penalty(ds_sampler* s, void* logits, int64_t n_rows, const uint32_t* seen_mask,
                           const float* penalty, void* stream) {
     g_err.clear();
@@ -638,12 +649,10 @@ int ds_repetition_penalty(ds_sampler* s, void* logits, int64_t n_rows, const uin
     if (n_rows > (int64_t)s->max_rows * s->max_positions)
         return fail(DS_ERR_CAPACITY, "n_rows %lld exceeds max_rows * max_positions", (long long)n_rows);
     if (n_rows == 0) return DS_OK;
-    if (!logits || !seen_mask || !penalty)
-        return fail(DS_ERR_INVALID_ARG, "logits, seen_mask and penalty must be non-NULL");
-    const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
-    if (!aligned(logits, es)) return fail(DS_ERR_INVALID_ARG, "logits is not %d-byte aligned", (int)es);
-    if (!aligned(seen_mask, 4) || !aligned(penalty, 4))
-        return fail(DS_ERR_INVALID_ARG, "seen_mask and penalty must be 4-byte aligned");
+    {
+        const int rc = check_penalty_args(s, logits, seen_mask, penalty);
+        if (rc != DS_OK) return rc;
+    }
 
     DeviceGuard dg(s->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
@@ -675,13 +684,20 @@ int ds_sample_ar(ds_sampler* s, const int64_t* request_ids, void* logits, const 
         return fail(DS_ERR_INVALID_ARG, "per-request device arrays must be aligned to their element size");
     if (!aligned(tokens_out, 4) || !aligned(logprobs_out, 4))
         return fail(DS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
-    // the penalty validates logits, seen_mask and penalty, and runs first on the stream
-    if (seen_mask || penalty) {
-        const int rc = ds_repetition_penalty(s, logits, num_requests, seen_mask, penalty, stream);
+    const bool pen = seen_mask || penalty;
+    if (pen) {
+        const int rc = check_penalty_args(s, logits, seen_mask, penalty);
         if (rc != DS_OK) return rc;
     } else {
         const uintptr_t es = s->dtype == DS_DTYPE_BF16 ? 2 : 4;
         if (!aligned(logits, es)) return fail(DS_ERR_INVALID_ARG, "logits is not %d-byte aligned", (int)es);
+    }
+    // The wave-per-cell kernel takes the penalised rows from the penalty kernel,
+    // run first on the stream; the streaming parts penalise their own ids.
+    const bool small = use_small_kernel(s);
+    if (pen && small) {
+        const int rc = ds_repetition_penalty(s, logits, num_requests, seen_mask, penalty, stream);
+        if (rc != DS_OK) return rc;
     }
 
     DeviceGuard dg(s->device);
@@ -710,6 +726,11 @@ int ds_sample_ar(ds_sampler* s, const int64_t* request_ids, void* logits, const 
     d.n = num_requests;
     d.P = num_requests;
     d.one_per_request = 1;
+    if (pen && !small) {
+        a.seen = seen_mask;
+        a.penalty = penalty;
+        a.W = (s->vocab + 31) / 32;
+    }
     return launch_dev_params(s, a, d, 1, (hipStream_t)stream);
 }
 

@@ -68,6 +68,13 @@ struct SampleArgs {
     float* logprobs;        // [C, P]
     float* thresholds;      // [C, P] or nullptr
     RowWork w;              // streaming kernel workspace (unused by the small kernel)
+    // Repetition penalty applied by the streaming parts of the device-parameter
+    // kernel before they read their ids (one position per request, so the cell
+    // is the row of the logits, of seen and of penalty); nullptr: none.  The
+    // logits (c) are then written in place.
+    const uint32_t* seen = nullptr;  // [cells, W] seen-id bits
+    const float* penalty = nullptr;  // [cells] theta
+    int32_t W = 0;                   // ceil(V / 32)
 };
 
 // Largest row the wave-per-cell kernel keeps in registers, in dwords per lane.

@@ -1061,13 +1061,83 @@ __device__ __forceinline__ const void* cell_u(const void* uptr, const CellParams
     return uptr ? (const void*)((const char*)uptr + (cp.ucell - cp.cell) * (int64_t)V * (bf16 ? 2 : 4)) : uptr;
 }
 
+// The repetition penalty of one part's ids [v0, v1), in place, ahead of the
+// part's stream (the autoregressive step; the same arithmetic as
+// k_repetition_penalty: x / theta for x > 0, else x * theta, in binary32, stored
+// in the logits' type).  Each thread loads up to four of the part's seen-mask
+// words at once, then reads the logits of kPenaltyBatch set ids before writing
+// any back; a barrier ends it, after which the workgroup's stream, and the merge
+// launched later, read the penalised values.  The parts of a row own disjoint
+// id ranges that cover it, so each seen id is penalised once, and the lines a
+// part writes are those its own stream reads next: the step reads the row once
+// instead of a separate pass reading a whole line for each seen id.
+template <bool BF16, int NT>
+__device__ void penalize_part(void* xrow, const uint32_t* seen, float theta, int v0, int v1) {
+    if (v1 > v0 && theta > 0.0f && theta < __builtin_huge_valf()) {
+        const int w0 = v0 >> 5, w1 = (v1 - 1) >> 5;  // the part's words, inclusive
+        // word w of the mask, only the part's bits [v0 - 32 w, v1 - 32 w) kept
+        auto word = [&](int w) {
+            uint32_t x = w <= w1 ? __builtin_nontemporal_load(seen + w) : 0u;
+            const int b0 = v0 - w * 32, b1 = v1 - w * 32;
+            if (b0 > 0) x &= ~0u << b0;
+            if (b1 < 32) x &= b1 > 0 ? (1u << b1) - 1u : 0u;
+            return x;
+        };
+        for (int wb = w0 + (int)threadIdx.x; wb <= w1; wb += NT * 4) {
+            // four words per thread (scalars, not an array, so that they stay in
+            // registers)
+            uint32_t m0 = word(wb), m1 = word(wb + NT), m2 = word(wb + 2 * NT), m3 = word(wb + 3 * NT);
+            // the next set id of the thread's words, lowest word first
+            auto next = [&](int& v) {
+                const bool s0 = m0 != 0u, s1 = !s0 && m1 != 0u, s2 = !s0 && !s1 && m2 != 0u;
+                const uint32_t cur = s0 ? m0 : s1 ? m1 : s2 ? m2 : m3;
+                const int k = s0 ? 0 : s1 ? 1 : s2 ? 2 : 3;
+                v = (wb + k * NT) * 32 + __builtin_ctz(cur | (cur == 0u ? 1u : 0u));
+                const uint32_t rest = cur & (cur - 1u);
+                m0 = s0 ? rest : m0;
+                m1 = s1 ? rest : m1;
+                m2 = s2 ? rest : m2;
+                m3 = (s0 || s1 || s2) ? m3 : rest;
+                return cur != 0u;
+            };
+            while ((m0 | m1 | m2 | m3) != 0u) {
+                int at[kPenaltyBatch];
+                bool ok[kPenaltyBatch];
+#pragma unroll
+                for (int b = 0; b < kPenaltyBatch; ++b) ok[b] = next(at[b]);
+                if constexpr (BF16) {
+                    uint16_t* x = static_cast<uint16_t*>(xrow);
+                    uint16_t hv[kPenaltyBatch];
+#pragma unroll
+                    for (int b = 0; b < kPenaltyBatch; ++b) hv[b] = ok[b] ? x[at[b]] : (uint16_t)0;
+#pragma unroll
+                    for (int b = 0; b < kPenaltyBatch; ++b)
+                        if (ok[b]) x[at[b]] = bf16_rne(penalized(__uint_as_float((uint32_t)hv[b] << 16), theta));
+                } else {
+                    float* x = static_cast<float*>(xrow);
+                    float fv[kPenaltyBatch];
+#pragma unroll
+                    for (int b = 0; b < kPenaltyBatch; ++b) fv[b] = ok[b] ? x[at[b]] : 0.0f;
+#pragma unroll
+                    for (int b = 0; b < kPenaltyBatch; ++b)
+                        if (ok[b]) x[at[b]] = penalized(fv[b], theta);
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // Kernel 1 body: stream part `part` of the row and write its partial record.
 // With WIN the part also takes its share of the row's threshold window; it then
 // streams with masked ids already mapped to -inf (FIX), since appended keys
 // cannot be taken back by a second pass.
+// With `seen` (the autoregressive step) the part first applies the repetition
+// penalty to its own ids (penalize_part).
 template <bool BF16, bool SAMPLE, bool WIN = false>
 __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bool force_fallback,
-                          const RowWork& w, const CellParams& cp, int64_t slot, int part) {
+                          const RowWork& w, const CellParams& cp, int64_t slot, int part,
+                          const uint32_t* seen = nullptr, const float* penalty = nullptr, int W = 0) {
     __shared__ PartLDS<BF16, SAMPLE, WIN> sh;
     const int j = part / w.ppc;
     const int q = part - j * w.ppc;
@@ -1075,6 +1145,17 @@ __device__ void part_body(const void* cptr, const void* uptr, int V, int nch, bo
     const bool race = SAMPLE && cp.tau != 0.0f && !force_fallback;
     const RowGeom G = row_geom<BF16>(cptr, cell_u(uptr, cp, V, BF16), use_u, cp.cell, V, nch, w.ppc);
     const PartRange<BF16> pr(G, j, q);
+    if (seen) {
+        // the part's ids: its pieces, clipped to its chunk
+        constexpr int EPP = Piece<BF16>::EPP;
+        int v0 = 0, v1 = 0;
+        if (pr.q1 >= pr.q0) {
+            v0 = (int)max((int64_t)pr.lo, pr.q0 * EPP - G.gbase);
+            v1 = (int)min((int64_t)pr.hi, (pr.q1 + 1) * EPP - G.gbase);
+        }
+        void* xrow = const_cast<char*>(static_cast<const char*>(cptr)) + cp.cell * (int64_t)V * (BF16 ? 2 : 4);
+        penalize_part<BF16, kPartThreads<WIN>>(xrow, seen + cp.cell * (int64_t)W, penalty[cp.cell], v0, v1);
+    }
     WinCtx wc{false, 0.0f, 0.0f, nullptr, nullptr};
     PartOut po;
     if constexpr (WIN) {
@@ -1340,7 +1421,8 @@ __global__ __launch_bounds__(kPartThreads<WIN>) __attribute__((amdgpu_waves_per_
     const int part = (int)(blockIdx.x - slot * a.w.nparts);
     CellParams cp;
     if (!sample_cell_dev(a, d, slot, cp)) return;
-    part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part);
+    part_body<BF16, true, WIN>(a.c, a.u, a.V, a.vocab_chunks, a.force_fallback != 0, a.w, cp, slot, part, a.seen,
+                               a.penalty, a.W);
 }
 template <bool BF16, int MT_, int KCAP, bool WIN>
 __global__ __launch_bounds__(MT_) __attribute__((amdgpu_waves_per_eu(WIN && BF16 ? 8 : 1, 8))) void k_sample_merge_dev(SampleArgs a, DevReq d) {
