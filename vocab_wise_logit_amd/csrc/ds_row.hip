@@ -309,7 +309,7 @@ template <typename SH>
 __device__ uint32_t find_digit(SH& sh, int nbins, int& kk) {
     const int bpt = nbins / SH::kThreads;
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform, in a scalar register
     int own = 0;
     for (int i = 0; i < bpt; ++i) own += (int)sh.hist[nbins - 1 - ((int)threadIdx.x * bpt + i)];
     int x = own;
@@ -699,7 +699,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
 
     // Gumbel race state: wave-uniform bound, queue lengths and queued count; the
     // lane's best (score, id, h)
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform, in a scalar register
     float Bw = kNegInf;
     int pn = 0, qn = 0, qtot = 0;
     float bz = kNegInf, bh = kNegInf;
@@ -761,10 +761,13 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
         wn -= n;
         if (lane < n && base + lane < kWinKeysPerRow) wc.keys[base + lane] = sh.wk[wv][wn + lane];
     };
-    auto win_push = [&](float h) {
-        const uint64_t mk = __builtin_amdgcn_ballot_w64(h >= wc.lo) & __builtin_amdgcn_ballot_w64(h <= wc.hi);
+    // (keys in [lo, wc.hi]; masks straight from the compares, and the lane
+    // predicate from the same compares, so no mask is rebuilt from a bool)
+    auto win_push = [&](float h, float lo) {
+        const bool ge = h >= lo, le = h <= wc.hi;
+        const uint64_t mk = __builtin_amdgcn_ballot_w64(ge) & __builtin_amdgcn_ballot_w64(le);
         if (mk) {
-            if ((mk >> lane) & 1ull) sh.wk[wv][wn + lanes_below(mk)] = __float_as_uint(h);
+            if (ge & le) sh.wk[wv][wn + lanes_below(mk)] = __float_as_uint(h);
             wn += popc(mk);
             if (wn >= kWave) {
                 __builtin_amdgcn_wave_barrier();
@@ -778,11 +781,11 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
     auto win_expand = [&]() {
         const int n = wqn;
         wqn = 0;
+        // slots past the queue hold stale values: a NaN bound keeps them out (no
+        // comparison with it holds)
+        const float lo = lane < n ? wc.lo : __builtin_nanf("");
 #pragma unroll 1
-        for (int i = 0; i < EPP; ++i) {
-            const float h = lane < n ? sh.wq[wv][i][lane] : __builtin_nanf("");
-            win_push(h);
-        }
+        for (int i = 0; i < EPP; ++i) win_push(sh.wq[wv][i][lane], lo);
     };
 
     // ids [lo, hi) cover every element of pieces 1 .. nq-2; only the first and the
@@ -864,7 +867,7 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
                             win_expand();
                             __builtin_amdgcn_wave_barrier();
                         }
-                        if ((any >> lane) & 1ull) {
+                        if (__builtin_amdgcn_inverse_ballot_w64(any)) {
                             const int at = wqn + lanes_below(any);
 #pragma unroll
                             for (int i = 0; i < EPP; ++i) {
