@@ -567,8 +567,8 @@ def main() -> int:
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs on a single GPU and has no "
-              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the sampler library runs on a single GPU and "
+              "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
