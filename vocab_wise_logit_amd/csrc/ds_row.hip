@@ -437,7 +437,7 @@ __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool us
     const int wv = threadIdx.x / kWave;
     const int lane = lane_id();
     for (int i = threadIdx.x; i < kHistBins; i += BT) sh.hist[i] = 0;
-    float lo_f = 0.0f, scale = 0.0f;  // bin of h: floor((h - lo_f) * scale), clamped to the bins
+    float lo_f = 0.0f, scale = 0.0f;  // bin of h: trunc(fma(h, scale, -lo_f * scale)), clamped to the bins
     int nv = 0;                       // sampled ids of this lane (every one is binned once)
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
@@ -454,8 +454,10 @@ __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool us
                 if (use_u) uw[jj] = stream_load(G.u16 + q);
             }
         }
-        // h of the batch's ids (NaN where a slot holds none), and of the first
-        // batch the finite range
+        // h of the batch's ids (NaN where a slot holds none, and for a masked id
+        // under guidance: such ids are counted as sampled but binned nowhere,
+        // which ranks them below every bin, where a masked id belongs), and of
+        // the first batch the range
         float h[RB][EPP];
         float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
@@ -463,48 +465,83 @@ __device__ __forceinline__ bool sample_window(const RowGeom& G, float s, bool us
             const int i = wv + (bt * RB + jj) * NW;
             const int64_t q = q0 + (int64_t)i * every * kWave + lane;
             const int64_t v0 = q * EPP - G.gbase;
+            const bool pv = bt * RB + jj < RPW && i < nsr && q <= q1;  // a piece was loaded
             Piece<BF16> P;
-            decode_piece<BF16>(cw[jj], uw[jj], s, use_u, P);
+            decode_piece<BF16, false>(cw[jj], uw[jj], s, use_u, P);
+            // a missing piece, or one reaching past the row (a row's first and
+            // last pieces only): its ids outside the row as NaN
+            int nvp = EPP;
+            if (!(pv && v0 >= 0 && v0 + EPP <= G.V)) {
+                nvp = 0;
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) {
+                    const bool in = pv && v0 + e >= 0 && v0 + e < G.V;
+                    if (!in) P.h[e] = __builtin_nanf("");
+                    nvp += in ? 1 : 0;
+                }
+            }
+            nv += nvp;
 #pragma unroll
             for (int e = 0; e < EPP; ++e) {
-                const float x = P.h[e];
-                const bool ok = bt * RB + jj < RPW && i < nsr && q <= q1 && v0 + e >= 0 && v0 + e < G.V && x == x;
-                h[jj][e] = ok ? x : __builtin_nanf("");
-                nv += ok ? 1 : 0;
-                if (bt == 0 && ok && __builtin_fabsf(x) < __builtin_inff()) {
-                    mn = __builtin_fminf(mn, x);
-                    mx = __builtin_fmaxf(mx, x);
+                h[jj][e] = P.h[e];
+                if (bt == 0) {  // (a NaN changes neither)
+                    mn = __builtin_fminf(mn, P.h[e]);
+                    mx = __builtin_fmaxf(mx, P.h[e]);
                 }
             }
         }
         if (bt == 0) {
-            const float wmn = wave_min(mn), wmx = wave_max(mx);
-            if (lane == 0) {
-                sh.r.f[wv] = wmn;
-                sh.r.f2[wv] = wmx;
-            }
-            __syncthreads();
-            float bmn = __builtin_inff(), bmx = -__builtin_inff();
+            // the block's min and max of the lanes' values (every read done
+            // before the slots are written again)
+            auto block_range = [&](float a, float b, float& lo, float& hi) {
+                const float wa = wave_min(a), wb = wave_max(b);
+                if (lane == 0) {
+                    sh.r.f[wv] = wa;
+                    sh.r.f2[wv] = wb;
+                }
+                __syncthreads();
+                lo = __builtin_inff();
+                hi = -__builtin_inff();
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) {
-                bmn = __builtin_fminf(bmn, sh.r.f[w2]);
-                bmx = __builtin_fmaxf(bmx, sh.r.f2[w2]);
+                for (int w2 = 0; w2 < NW; ++w2) {
+                    lo = __builtin_fminf(lo, sh.r.f[w2]);
+                    hi = __builtin_fmaxf(hi, sh.r.f2[w2]);
+                }
+                __syncthreads();
+            };
+            float bmn, bmx;
+            block_range(mn, mx, bmn, bmx);
+            if (!(bmn > -__builtin_inff() && bmx < __builtin_inff())) {
+                // an infinite h in the first batch (a masked id, or an overflow):
+                // the finite range instead
+                mn = __builtin_inff();
+                mx = -__builtin_inff();
+#pragma unroll
+                for (int jj = 0; jj < RB; ++jj)
+#pragma unroll
+                    for (int e = 0; e < EPP; ++e)
+                        if (__builtin_fabsf(h[jj][e]) < __builtin_inff()) {
+                            mn = __builtin_fminf(mn, h[jj][e]);
+                            mx = __builtin_fmaxf(mx, h[jj][e]);
+                        }
+                block_range(mn, mx, bmn, bmx);
             }
             const float pad = NB > 1 ? 0.25f * (bmx - bmn) : 0.0f;
             lo_f = bmn - pad;
             scale = (float)kHistBins / ((bmx + pad) - lo_f);
             if (!(bmx > bmn && scale < __builtin_inff())) return false;
         }
-        // a non-decreasing function of h (-inf to the lowest bin, +inf to the highest)
+        // a non-decreasing function of h (-inf to the lowest bin, +inf to the
+        // highest, NaN to none)
+        const float off = -lo_f * scale;
 #pragma unroll
         for (int jj = 0; jj < RB; ++jj)
 #pragma unroll
             for (int e = 0; e < EPP; ++e) {
                 const float x = h[jj][e];
                 if (x == x) {
-                    const float t = (x - lo_f) * scale;
-                    const int bin = t >= (float)(kHistBins - 1) ? kHistBins - 1 : (t > 0.0f ? (int)t : 0);
-                    atomicAdd(&sh.hist[bin], 1u);
+                    const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, scale, off), 0.0f, (float)(kHistBins - 1));
+                    atomicAdd(&sh.hist[(int)t], 1u);
                 }
             }
     }
@@ -860,6 +897,11 @@ __device__ PartOut stream_part(const RowGeom& G, const PartRange<BF16>& pr, cons
                         if (EDGE) in &= __builtin_amdgcn_ballot_w64(j < nqi && v0 + i >= pr.lo && v0 + i < pr.hi);
                         any |= in;
                     }
+                    // the count taken now (an empty statement that reads it): left
+                    // to the compiler, the popcounts of a whole group sink to its end
+                    // and keep 32 masks live, and the scalar registers they take are
+                    // spilled and reloaded on every group
+                    asm volatile("" : "+s"(wabove));
                     if (any) {
                         const int add = popc(any);
                         if (wqn + add > kWave) {
