@@ -278,12 +278,16 @@ def test_threshold_windows_over_several_launches():
     check_sample(w, run_sample(w, threshold=False), ref, check_threshold=False)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunks", [1, 3])
-def test_threshold_window_f32(chunks):
-    # f32 rows long enough for the threshold window (V = 65536: every fifth run
-    # of 256 ids is sampled), guided and not, with a masked id
-    w = synth.diffusion("window_f32", seed=93, vocab=65536, rows=2, seq_lens=[5, 4], dtype="f32", sigma=3.0,
-                        guidance=[1.5, 0.0], temperature=[1.0, 0.7], vocab_chunks=chunks, masked_ids=[11])
+def test_threshold_window_masked_ids(dtype, chunks):
+    # rows long enough for the threshold window (V = 65536, a sample of runs
+    # spread over the row), guided and not, with masked ids (c and u -inf, so the
+    # guided h is NaN before it is taken as -inf) at the row's start, inside it
+    # and at its end, inside sampled runs and outside them
+    w = synth.diffusion(f"window_{dtype}", seed=93, vocab=65536, rows=2, seq_lens=[5, 4], dtype=dtype, sigma=3.0,
+                        guidance=[1.5, 0.0], temperature=[1.0, 0.7], vocab_chunks=chunks,
+                        masked_ids=[0, 11, 30000, 40961, 65535])
     ref = oracle.sample_workload(w)
     for thr in (True, False):
         check_sample(w, run_sample(w, threshold=thr), ref)
