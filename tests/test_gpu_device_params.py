@@ -200,14 +200,17 @@ def test_device_params_take_invalid_values_as_documented():
 
 
 @pytest.mark.parametrize("dtype,V,chunks,fallback", [("bf16", 5000, 1, False), ("bf16", 3000, 3, False),
-                                                     ("f32", 4100, 2, False), ("bf16", 1025, 1, True)])
+                                                     ("f32", 4100, 2, False), ("bf16", 1025, 1, True),
+                                                     ("bf16", 65536, 2, False), ("f32", 65536, 1, False)])
 def test_device_params_streaming_path(dtype, V, chunks, fallback):
     import torch
 
     import vocab_wise_logit_amd as ds
 
     # vocabularies past the wave-per-cell kernel (and, with the forced fallback,
-    # one inside it) go through the streaming kernels over the fixed layout
+    # one inside it) go through the streaming kernels over the fixed layout; at
+    # V = 65536 the threshold output takes the window path (its own window,
+    # parts and merge kernels for device parameters)
     w = synth.diffusion(f"devp_row_{dtype}_{V}", seed=64 + V, vocab=V, rows=2, seq_lens=[3, 0, 4], dtype=dtype,
                         sigma=4.0, guidance=[1.5, 2.0, 0.0], temperature=[1.0, 0.5, 0.7], iterations=[2, 0, 5],
                         vocab_chunks=chunks)
