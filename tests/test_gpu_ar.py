@@ -26,6 +26,9 @@ CASES = [
     # more requests than one wave's table: every request is its own position
     ("many_small_bf16", 150, 1025, "bf16", (5, 100), (0.0, 0.9), None),
     ("many_row_bf16", 90, 8192, "bf16", (50, 500), (0.0, 1.0), None),
+    # the large vocabulary with the top-ratio filter: the merge's top-set
+    # decision runs on rows the parts penalised
+    ("full_vocab_topratio", 24, 248320, "bf16", (256, 1280), (0.0, 0.7, 1.0), 24832),
 ]
 
 
