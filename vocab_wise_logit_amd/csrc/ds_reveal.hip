@@ -13,9 +13,10 @@
 //      of cells tied at that key that must be taken;
 //   2. one pass in flattened order collects every cell above that key, and the
 //      first tied cells in index order (a block prefix count per 1024 cells);
-//   3. a bitonic sort in LDS of the selected cells on the 64-bit key
-//      (order key << 32 | ~index), descending, and the write-out; -0 and +0
-//      rank as equal scores.
+//   3. a bitonic sort of the selected cells on the 64-bit key (order key << 32 |
+//      ~index), descending: in one wave's registers when at most 128 are
+//      selected (no block barrier), otherwise in LDS; then the write-out; -0 and
+//      +0 rank as equal scores.
 #include <stdint.h>
 
 #include "ds_device.h"
@@ -181,8 +182,45 @@ __device__ void reveal_body(const RevealArgs& a, const RevealTable& rt, RevealLD
     __syncthreads();
 
     // ---- 3. bitonic sort of the k selected keys, descending (pad with 0)
+    if (k <= 2 * kWave) {
+        // one wave sorts 128 keys in registers, two per lane (key e = lane + 64 h):
+        // the partner of e at a stride below 64 is in lane ^ stride, read with a
+        // shuffle, at stride 64 it is the lane's other key; no block barrier
+        if (wv == 0) {
+            unsigned long long x[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) x[h] = lane + kWave * h < k ? sh.sel[lane + kWave * h] : 0ull;
+            for (int size = 2; size <= 2 * kWave; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    if (stride == kWave) {
+                        // e = lane is the lower of the pair; (lane & size) == 0 here
+                        const bool desc = (lane & size) == 0;
+                        const unsigned long long hi = x[0] > x[1] ? x[0] : x[1];
+                        const unsigned long long lo = x[0] > x[1] ? x[1] : x[0];
+                        x[0] = desc ? hi : lo;
+                        x[1] = desc ? lo : hi;
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int e = lane + kWave * h;
+                            const unsigned long long y = __shfl_xor(x[h], stride);
+                            const bool lower = (e & stride) == 0;
+                            const bool desc = (e & size) == 0;  // the same for both keys of the pair
+                            const bool take_max = lower == desc;
+                            x[h] = take_max ? (x[h] > y ? x[h] : y) : (x[h] > y ? y : x[h]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if (lane + kWave * h < k) sh.sel[lane + kWave * h] = x[h];
+        }
+        __syncthreads();
+    }
     int N = 1;
     while (N < k) N <<= 1;
+    if (k <= 2 * kWave) N = 1;  // sorted above
     for (int i = k + (int)threadIdx.x; i < N; i += NTR) sh.sel[i] = 0ull;
     __syncthreads();
     for (int size = 2; size <= N; size <<= 1) {
