@@ -78,10 +78,12 @@ def test_compact_u_wave_per_cell(dtype, V):
 
 
 @pytest.mark.parametrize("dtype,V,chunks,fallback", [("bf16", 3000, 1, False), ("bf16", 4104, 3, False),
-                                                     ("f32", 4100, 2, False), ("f32", 1024, 1, True)])
+                                                     ("f32", 4100, 2, False), ("f32", 1024, 1, True),
+                                                     ("bf16", 65536, 2, False)])
 def test_compact_u_streaming_path(dtype, V, chunks, fallback):
     # V * b is a multiple of 16 bytes, so every u row keeps its c row's 16-byte
-    # alignment under the compaction
+    # alignment under the compaction; at V = 65536 the threshold output takes the
+    # window path, whose sample reads the compacted u rows too
     w = synth.diffusion(f"cu_row_{dtype}_{V}", seed=81 + V, vocab=V, rows=2, seq_lens=[3, 2, 4, 1], dtype=dtype,
                         sigma=4.0, guidance=[1.5, 0.0, 2.0, 1.0], temperature=[1.0, 0.5, 0.0, 0.7],
                         vocab_chunks=chunks)
